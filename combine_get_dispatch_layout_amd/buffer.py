@@ -1,0 +1,314 @@
+"""Python front end with the call shapes of the pages, over libmoedx.so.
+
+``Buffer`` mirrors the normal and low-latency usage examples of the
+EnflameTechnology/DeepEP README (get_dispatch_layout, dispatch, combine,
+low_latency_dispatch, low_latency_combine, capture); ``EventOverlap`` mirrors
+the event wrapper of "How DeepEP Achieves Communication-Computation
+Overlapping with EventOverlap" (current_stream_wait and the context manager).
+PyTorch only provides device memory and the current stream; every step runs in
+the library's HIP kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _capi as C
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr() or None)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class EventOverlap:
+    """Owns one library event.  ``event is None`` means "already complete"
+    (what a call with async_finish=False hands back, for tuple arity)."""
+
+    def __init__(self, event: Optional[int] = None):
+        self.event = event
+
+    def current_stream_wait(self) -> None:
+        if self.event is not None:
+            C.check(C.moedx_event_wait(self.event, _stream()))
+
+    def synchronize(self) -> None:
+        if self.event is not None:
+            C.check(C.moedx_event_synchronize(self.event))
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.current_stream_wait()
+
+    def __del__(self):
+        if getattr(self, "event", None) is not None:
+            C.moedx_event_destroy(self.event)
+            self.event = None
+
+
+_MATRICES = {C.MOEDX_T_CHANNEL_PREFIX_MATRIX, C.MOEDX_T_RECV_CHANNEL_PREFIX_MATRIX,
+             C.MOEDX_T_IS_TOKEN_IN_RANK, C.MOEDX_T_SEND_HEAD, C.MOEDX_T_LL_SRC_IDX,
+             C.MOEDX_T_LL_SLOT_OF}
+
+
+class Handle:
+    """A prepared layout: the library handle plus the device workspace that
+    holds its arrays (kept alive as long as the handle)."""
+
+    def __init__(self, ptr: int, workspace: torch.Tensor, T: int, K: int, low_latency: bool,
+                 capacity: int = 0):
+        self.ptr = ptr
+        self.workspace = workspace
+        self.T, self.K = T, K
+        self.low_latency = low_latency
+        self.capacity = capacity
+
+    def tensor(self, which: int, dtype: torch.dtype) -> torch.Tensor:
+        """View of one handle array (MOEDX_T_*) inside the workspace."""
+        dev = ctypes.c_void_p()
+        shape = (ctypes.c_int64 * 2)()
+        C.check(C.moedx_handle_tensor(self.ptr, which, ctypes.byref(dev), shape))
+        n0, n1 = int(shape[0]), int(shape[1])
+        off = (dev.value or 0) - self.workspace.data_ptr()
+        nbytes = n0 * n1 * torch.empty((), dtype=dtype).element_size()
+        assert 0 <= off and off + nbytes <= self.workspace.numel()
+        v = self.workspace[off: off + nbytes].view(dtype)
+        return v.view(n0, n1) if which in _MATRICES else v
+
+    @property
+    def num_recv(self) -> int:
+        n = ctypes.c_int64()
+        C.check(C.moedx_handle_num_recv(self.ptr, ctypes.byref(n)))
+        return int(n.value)
+
+    def recv_tokens_per_expert(self, num_experts: int) -> list:
+        a = (ctypes.c_int32 * num_experts)()
+        C.check(C.moedx_handle_recv_tokens_per_expert(self.ptr, a))
+        return list(a)
+
+    # handle fields named on the handle-reuse page
+    def fields(self) -> dict:
+        if self.low_latency:
+            return {"src_idx": self.tensor(C.MOEDX_T_LL_SRC_IDX, torch.int32),
+                    "slot_of": self.tensor(C.MOEDX_T_LL_SLOT_OF, torch.int32)}
+        return {
+            "rank_prefix_matrix": self.tensor(C.MOEDX_T_RANK_PREFIX_MATRIX, torch.int32),
+            "channel_prefix_matrix": self.tensor(C.MOEDX_T_CHANNEL_PREFIX_MATRIX, torch.int32),
+            "recv_channel_prefix_matrix": self.tensor(C.MOEDX_T_RECV_CHANNEL_PREFIX_MATRIX, torch.int32),
+            "recv_src_idx": self.tensor(C.MOEDX_T_RECV_SRC_IDX, torch.int32),
+            "is_token_in_rank": self.tensor(C.MOEDX_T_IS_TOKEN_IN_RANK, torch.uint8),
+            "send_head": self.tensor(C.MOEDX_T_SEND_HEAD, torch.int32),
+            "num_tokens_per_rank": self.tensor(C.MOEDX_T_NUM_TOKENS_PER_RANK, torch.int32),
+            "num_tokens_per_expert": self.tensor(C.MOEDX_T_NUM_TOKENS_PER_EXPERT, torch.int32),
+            "num_recv": self.tensor(C.MOEDX_T_NUM_RECV, torch.int32),
+        }
+
+    def __del__(self):
+        if getattr(self, "ptr", None):
+            C.moedx_handle_destroy(self.ptr)
+            self.ptr = None
+
+
+class Buffer:
+    """One GPU's share of the expert-parallel exchange: ``num_ranks`` logical
+    ranks are buckets of ``num_experts / num_ranks`` experts in this GPU's HBM."""
+
+    def __init__(self, num_experts: int, num_ranks: int, num_channels: int = 24,
+                 max_tokens: int = 16384, device: Optional[int] = None):
+        self.device = torch.cuda.current_device() if device is None else device
+        self.num_experts, self.num_ranks, self.num_channels = num_experts, num_ranks, num_channels
+        self.max_tokens = max_tokens
+        ctx = ctypes.c_void_p()
+        C.check(C.moedx_create(ctypes.byref(ctx), self.device, num_experts, num_ranks,
+                               num_channels, max_tokens, 0))
+        self.ctx = ctx.value
+
+    def __del__(self):
+        if getattr(self, "ctx", None):
+            C.moedx_destroy(self.ctx)
+            self.ctx = None
+
+    # -- plumbing ---------------------------------------------------------------
+    def _exec(self, previous_event, async_finish, allocate_on_comm_stream, no_sync=False):
+        done = ctypes.c_void_p() if async_finish else None
+        flags = (C.MOEDX_ON_CTX_STREAM if allocate_on_comm_stream else 0) | (
+            C.MOEDX_ASYNC if no_sync else 0)
+        prev = previous_event.event if previous_event is not None else None
+        return C.make_exec(_stream(), prev, done, flags), done
+
+    @staticmethod
+    def _event(done) -> EventOverlap:
+        return EventOverlap(done.value if done is not None else None)
+
+    def stats(self) -> dict:
+        s = C.moedx_stats()
+        C.check(C.moedx_ctx_stats(self.ctx, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in C.moedx_stats._fields_}
+
+    @staticmethod
+    def capture() -> EventOverlap:
+        ev = ctypes.c_void_p()
+        C.check(C.moedx_event_record(ctypes.byref(ev), _stream()))
+        return EventOverlap(ev.value)
+
+    # -- layout -----------------------------------------------------------------
+    def get_dispatch_layout(self, topk_idx: torch.Tensor, num_experts: int,
+                            previous_event: Optional[EventOverlap] = None,
+                            async_finish: bool = False, allocate_on_comm_stream: bool = False):
+        """Returns (num_tokens_per_rank, None, num_tokens_per_expert,
+        is_token_in_rank, event); the None stands for the per-RDMA-rank counts,
+        which do not exist on one GPU."""
+        assert num_experts == self.num_experts
+        topk_idx = topk_idx.contiguous()
+        T, K = topk_idx.shape
+        dev = topk_idx.device
+        ntr = torch.empty(self.num_ranks, dtype=torch.int32, device=dev)
+        nte = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        itr = torch.empty(T, self.num_ranks, dtype=torch.bool, device=dev)
+        ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream)
+        C.check(C.moedx_get_dispatch_layout(self.ctx, _ptr(topk_idx), T, K, _ptr(ntr), _ptr(nte),
+                                            _ptr(itr), ctypes.byref(ex)))
+        return ntr, None, nte, itr, self._event(done)
+
+    # -- normal dispatch / combine --------------------------------------------------
+    def prepare(self, topk_idx: torch.Tensor, num_worst_tokens: int = 0,
+                previous_event=None, async_finish=False, allocate_on_comm_stream=False,
+                no_sync=False):
+        """Layout + scan into a new handle (exact mode, or capacity mode with
+        ``num_worst_tokens`` receive rows)."""
+        topk_idx = topk_idx.contiguous()
+        T, K = topk_idx.shape
+        nbytes = ctypes.c_size_t()
+        C.check(C.moedx_handle_workspace_bytes(self.ctx, T, K, num_worst_tokens, ctypes.byref(nbytes)))
+        ws = torch.empty(nbytes.value, dtype=torch.uint8, device=topk_idx.device)
+        h = ctypes.c_void_p()
+        ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream, no_sync)
+        C.check(C.moedx_dispatch_prepare(self.ctx, _ptr(topk_idx), T, K, _ptr(ws), nbytes.value,
+                                         num_worst_tokens, ctypes.byref(h), ctypes.byref(ex)))
+        return Handle(h.value, ws, T, K, False, num_worst_tokens), self._event(done)
+
+    def dispatch(self, x, handle: Optional[Handle] = None, num_tokens_per_rank=None,
+                 num_tokens_per_rdma_rank=None, is_token_in_rank=None, num_tokens_per_expert=None,
+                 topk_idx: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
+                 previous_event: Optional[EventOverlap] = None, async_finish: bool = False,
+                 allocate_on_comm_stream: bool = False, num_worst_tokens: int = 0,
+                 fp8: bool = False, out: Optional[torch.Tensor] = None,
+                 out_scales: Optional[torch.Tensor] = None, no_sync: bool = False):
+        """Returns (recv_x, recv_topk_idx, recv_topk_weights,
+        num_recv_tokens_per_expert_list, handle, event); recv_x is
+        (codes, scales) when fp8.  With ``handle`` (cached dispatch) topk_idx and
+        topk_weights must be None and only recv_x is produced.  The layout
+        arguments are accepted for call-shape compatibility; the handle is
+        computed from topk_idx on the device."""
+        x = x.contiguous()
+        T, H = x.shape
+        first = handle is None
+        if first:
+            assert topk_idx is not None, "a first dispatch needs topk_idx"
+            handle, _ = self.prepare(topk_idx, num_worst_tokens, previous_event,
+                                     False, allocate_on_comm_stream, no_sync=True)
+            previous_event = None
+        else:
+            assert topk_idx is None and topk_weights is None, \
+                "a cached dispatch takes no topk_idx / topk_weights"
+        rows = handle.capacity if handle.capacity > 0 else handle.num_recv
+        K = handle.K
+        dev = x.device
+        # (at least one row is allocated so that an empty receive side still
+        # passes a valid device pointer; the returned views have `rows` rows)
+        alloc = max(rows, 1)
+        if fp8:
+            recv_x = out if out is not None else torch.empty(alloc, H, dtype=torch.uint8, device=dev)[:rows]
+            recv_s = out_scales if out_scales is not None else torch.empty(
+                alloc, H // 128, dtype=torch.float32, device=dev)[:rows]
+        else:
+            recv_x = out if out is not None else torch.empty(alloc, H, dtype=torch.bfloat16, device=dev)[:rows]
+            recv_s = None
+        rti = rtw = None
+        if first and not fp8:
+            rti = torch.empty(alloc, K, dtype=torch.int64, device=dev)[:rows]
+            if topk_weights is not None:
+                rtw = torch.empty(alloc, K, dtype=torch.float32, device=dev)[:rows]
+        ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream, no_sync)
+        tw = topk_weights.contiguous() if topk_weights is not None else None
+        ti = topk_idx.contiguous() if (first and not fp8) else None
+        C.check(C.moedx_dispatch(self.ctx, handle.ptr, _ptr(x), T, H,
+                                 C.MOEDX_QUANT_FP8_E4M3_1X128 if fp8 else C.MOEDX_QUANT_NONE,
+                                 _ptr(ti), _ptr(tw if (first and not fp8) else None), _ptr(recv_x),
+                                 _ptr(recv_s), _ptr(rti), _ptr(rtw), ctypes.byref(ex)))
+        per_expert = handle.recv_tokens_per_expert(self.num_experts) if (
+            first and handle.capacity == 0) else None
+        rx = (recv_x, recv_s) if fp8 else recv_x
+        return rx, rti, rtw, per_expert, handle, self._event(done)
+
+    def combine(self, x: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None,
+                gate_weights: Optional[torch.Tensor] = None,
+                previous_event: Optional[EventOverlap] = None, async_finish: bool = False,
+                allocate_on_comm_stream: bool = False, out: Optional[torch.Tensor] = None,
+                no_sync: bool = False):
+        """Returns (combined_x, combined_topk_weights, event).  ``topk_weights``
+        is the per-row weight payload ([rows, K]) reduced like the rows;
+        ``gate_weights`` ([T, K]) scales each bucket's row by its summed gate
+        weight."""
+        x = x.contiguous()
+        H = x.shape[1]
+        T, K = handle.T, handle.K
+        combined = out if out is not None else torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+        cw = torch.empty(T, K, dtype=torch.float32, device=x.device) if topk_weights is not None else None
+        ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream, no_sync)
+        gw = gate_weights.contiguous() if gate_weights is not None else None
+        tw = topk_weights.contiguous() if topk_weights is not None else None
+        C.check(C.moedx_combine(self.ctx, handle.ptr, _ptr(x), H, _ptr(gw), _ptr(tw),
+                                _ptr(combined), _ptr(cw), ctypes.byref(ex)))
+        return combined, cw, self._event(done)
+
+    # -- low-latency ------------------------------------------------------------
+    def low_latency_dispatch(self, x: torch.Tensor, topk_idx: torch.Tensor,
+                             num_max_dispatch_tokens_per_rank: int, num_experts: int,
+                             previous_event=None, async_finish: bool = False,
+                             return_recv_hook: bool = False, no_sync: bool = False):
+        """Returns (recv_x [E, cap, H], recv_count [E] int32, handle, event, None).
+        There is no deferred receive: the hook slot is None."""
+        assert num_experts == self.num_experts
+        assert not return_recv_hook, "no deferred receive phase exists on one GPU"
+        x = x.contiguous()
+        topk_idx = topk_idx.contiguous()
+        T, H = x.shape
+        K = topk_idx.shape[1]
+        cap = num_max_dispatch_tokens_per_rank
+        dev = x.device
+        nbytes = ctypes.c_size_t()
+        C.check(C.moedx_ll_workspace_bytes(self.ctx, T, K, cap, ctypes.byref(nbytes)))
+        ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+        recv_x = torch.empty(num_experts, cap, H, dtype=torch.bfloat16, device=dev)
+        cnt = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        h = ctypes.c_void_p()
+        ex, done = self._exec(previous_event, async_finish, False, no_sync)
+        C.check(C.moedx_ll_dispatch(self.ctx, _ptr(x), _ptr(topk_idx), T, K, H, cap, _ptr(recv_x),
+                                    _ptr(cnt), _ptr(ws), nbytes.value, ctypes.byref(h),
+                                    ctypes.byref(ex)))
+        return recv_x, cnt, Handle(h.value, ws, T, K, True), self._event(done), None
+
+    def low_latency_combine(self, x: torch.Tensor, topk_idx: torch.Tensor,
+                            topk_weights: torch.Tensor, handle: Handle, previous_event=None,
+                            async_finish: bool = False, return_recv_hook: bool = False,
+                            out: Optional[torch.Tensor] = None, no_sync: bool = False):
+        """Returns (combined [T, H] bf16, event, None)."""
+        assert not return_recv_hook, "no deferred receive phase exists on one GPU"
+        x = x.contiguous()
+        H = x.shape[-1]
+        T = handle.T
+        combined = out if out is not None else torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+        ex, done = self._exec(previous_event, async_finish, False, no_sync)
+        C.check(C.moedx_ll_combine(self.ctx, _ptr(x), _ptr(topk_idx.contiguous()),
+                                   _ptr(topk_weights.contiguous()), handle.ptr, H, _ptr(combined),
+                                   ctypes.byref(ex)))
+        return combined, self._event(done), None

@@ -1,0 +1,637 @@
+// C ABI of libmoedx.so: validation, contexts, handles, events and launches.
+//
+// The calls follow the problem statement of the pages: get_dispatch_layout,
+// dispatch with or without a cached handle, combine, and the low-latency pair
+// (EnflameTechnology/DeepEP README usage examples), ordered by events in the
+// way "How DeepEP Achieves Communication-Computation Overlapping with
+// EventOverlap" describes (previous_event, async_finish, the comm stream).
+//
+// Every argument is checked on the host before anything is enqueued, and no
+// C++ exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "launch.h"
+#include "moedx.h"
+
+using namespace moedx;
+
+struct moedx_event {
+    hipEvent_t ev;
+};
+
+struct moedx_ctx {
+    int device;
+    int E, R, P, C, max_tokens;
+    hipStream_t stream;      // the ctx's own stream (default priority)
+    hipEvent_t order_event;  // orders the ctx stream after the caller's
+    void* scratch;           // per-tile counts of the standalone layout
+    size_t scratch_bytes;
+    int32_t* pinned;         // host readback: [0] = N, [1..E] = per-expert counts
+    moedx_stats stats;
+};
+
+enum HandleKind { kNormal = 1, kLowLatency = 2 };
+
+struct moedx_handle {
+    HandleKind kind;
+    int T, K, E, R, P, C;
+    int64_t capacity;  // 0 = exact mode
+    int64_t n_host;    // exact mode only
+    std::vector<int32_t> per_expert_host;
+    // device arrays inside the caller's workspace
+    uint8_t* is_token_in_rank;
+    int8_t* slot_bucket;
+    int32_t* num_tokens_per_rank;
+    int32_t* num_tokens_per_expert;
+    int32_t* rank_prefix_matrix;
+    int32_t* channel_prefix_matrix;
+    int32_t* recv_channel_prefix_matrix;
+    int32_t* send_head;
+    int32_t* recv_src_idx;
+    int32_t* num_recv;
+    int32_t* tile_rank;
+    int32_t* tile_expert;
+    // low-latency
+    int cap;
+    int32_t* ll_src_idx;
+    int32_t* ll_slot_of;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(MOEDX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_OR_FAIL(call)                                  \
+    do {                                                   \
+        hipError_t e_ = (call);                            \
+        if (e_ != hipSuccess) return hip_fail(e_, #call);  \
+    } while (0)
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Carves consecutive 256-byte-aligned regions out of one workspace.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    template <typename T>
+    T* take(size_t count) {
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += align256(count * sizeof(T));
+        return p;
+    }
+};
+
+// Lays out a normal handle's device arrays; with base == nullptr it only sizes.
+size_t carve_normal(moedx_handle* h, char* base, int T, int K, int E, int R, int C,
+                    int64_t rows) {
+    Carver cv{base};
+    const int nt = num_tiles(T);
+    moedx_handle tmp;
+    moedx_handle* d = h ? h : &tmp;
+    d->is_token_in_rank = cv.take<uint8_t>((size_t)T * R);
+    d->slot_bucket = cv.take<int8_t>((size_t)T * K);
+    d->num_tokens_per_rank = cv.take<int32_t>(R);
+    d->num_tokens_per_expert = cv.take<int32_t>(E);
+    d->rank_prefix_matrix = cv.take<int32_t>(R);
+    d->channel_prefix_matrix = cv.take<int32_t>((size_t)R * C);
+    d->recv_channel_prefix_matrix = cv.take<int32_t>((size_t)R * C);
+    d->send_head = cv.take<int32_t>((size_t)T * R);
+    d->recv_src_idx = cv.take<int32_t>((size_t)std::max<int64_t>(rows, 1));
+    d->num_recv = cv.take<int32_t>(1);
+    d->tile_rank = cv.take<int32_t>((size_t)std::max(nt, 1) * R);
+    d->tile_expert = cv.take<int32_t>((size_t)std::max(nt, 1) * E);
+    return cv.off;
+}
+
+size_t carve_ll(moedx_handle* h, char* base, int T, int K, int E, int cap) {
+    Carver cv{base};
+    moedx_handle tmp;
+    moedx_handle* d = h ? h : &tmp;
+    d->ll_src_idx = cv.take<int32_t>((size_t)E * cap);
+    d->ll_slot_of = cv.take<int32_t>((size_t)std::max(T, 1) * K);
+    return cv.off;
+}
+
+// Worst-case receive rows: each token lands in at most min(K, R) buckets.
+int64_t worst_rows(int T, int K, int R) { return (int64_t)T * std::min(K, R); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Stream choice and the previous_event wait; see moedx_exec.
+struct Exec {
+    hipStream_t caller = nullptr;
+    hipStream_t run = nullptr;
+    moedx_event** done = nullptr;
+    bool async = false;
+};
+
+int exec_begin(moedx_ctx* ctx, const moedx_exec* ex, Exec* out) {
+    if (ex && (ex->flags & ~uint32_t(MOEDX_ON_CTX_STREAM | MOEDX_ASYNC)))
+        return fail(MOEDX_EINVAL, "unknown moedx_exec flags 0x%x", ex->flags);
+    out->caller = ex ? ex->stream : nullptr;
+    out->done = ex ? ex->done : nullptr;
+    out->async = ex && (ex->flags & MOEDX_ASYNC);
+    const bool on_ctx = ex && (ex->flags & MOEDX_ON_CTX_STREAM);
+    out->run = on_ctx ? ctx->stream : out->caller;
+    HIP_OR_FAIL(hipSetDevice(ctx->device));
+    if (ex && ex->prev) HIP_OR_FAIL(hipStreamWaitEvent(out->run, ex->prev->ev, 0));
+    if (on_ctx) {
+        HIP_OR_FAIL(hipEventRecord(ctx->order_event, out->caller));
+        HIP_OR_FAIL(hipStreamWaitEvent(out->run, ctx->order_event, 0));
+    }
+    return MOEDX_OK;
+}
+
+int exec_end(const Exec& ex) {
+    if (ex.done) {
+        moedx_event* ev = new (std::nothrow) moedx_event;
+        if (!ev) return fail(MOEDX_ENOMEM, "event allocation failed");
+        hipError_t e = hipEventCreateWithFlags(&ev->ev, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            delete ev;
+            return hip_fail(e, "hipEventCreateWithFlags");
+        }
+        e = hipEventRecord(ev->ev, ex.run);
+        if (e != hipSuccess) {
+            (void)hipEventDestroy(ev->ev);
+            delete ev;
+            return hip_fail(e, "hipEventRecord");
+        }
+        *ex.done = ev;
+        return MOEDX_OK;
+    }
+    if (!ex.async) HIP_OR_FAIL(hipStreamSynchronize(ex.run));
+    return MOEDX_OK;
+}
+
+int check_ctx(const moedx_ctx* ctx) {
+    if (!ctx) return fail(MOEDX_EINVAL, "ctx is NULL");
+    return MOEDX_OK;
+}
+
+int check_tokens(const moedx_ctx* ctx, int T, int K) {
+    if (T < 0 || T > ctx->max_tokens)
+        return fail(MOEDX_EINVAL, "T=%d outside [0, max_tokens=%d]", T, ctx->max_tokens);
+    if (K < 1 || K > kMaxTopk) return fail(MOEDX_EINVAL, "K=%d outside [1, %d]", K, kMaxTopk);
+    return MOEDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moedx_last_error(void) { return g_err; }
+
+int moedx_create(moedx_ctx** out, int device, int num_experts, int num_ranks, int num_channels,
+                 int max_tokens, uint32_t flags) {
+    if (!out) return fail(MOEDX_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (flags != 0) return fail(MOEDX_EINVAL, "flags must be 0");
+    if (num_ranks < 1 || num_ranks > kMaxRanks)
+        return fail(MOEDX_EINVAL, "num_ranks=%d outside [1, %d]", num_ranks, kMaxRanks);
+    if (num_experts < 1 || num_experts > kMaxExperts)
+        return fail(MOEDX_EINVAL, "num_experts=%d outside [1, %d]", num_experts, kMaxExperts);
+    if (num_experts % num_ranks != 0)
+        return fail(MOEDX_EINVAL, "num_experts=%d is not a multiple of num_ranks=%d", num_experts,
+                    num_ranks);
+    if (num_channels < 1) return fail(MOEDX_EINVAL, "num_channels=%d < 1", num_channels);
+    if (max_tokens < 0 || max_tokens > (1 << 24))
+        return fail(MOEDX_EINVAL, "max_tokens=%d outside [0, 2^24]", max_tokens);
+    if (device < 0) return fail(MOEDX_EINVAL, "device=%d < 0", device);
+
+    moedx_ctx* c = new (std::nothrow) moedx_ctx();
+    if (!c) return fail(MOEDX_ENOMEM, "ctx allocation failed");
+    c->device = device;
+    c->E = num_experts;
+    c->R = num_ranks;
+    c->P = num_experts / num_ranks;
+    c->C = num_channels;
+    c->max_tokens = max_tokens;
+    const int nt = std::max(num_tiles(max_tokens), 1);
+    c->scratch_bytes = align256((size_t)nt * num_ranks * 4) + align256((size_t)nt * num_experts * 4);
+    hipError_t e = hipSetDevice(device);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->order_event, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipMalloc(&c->scratch, c->scratch_bytes);
+    if (e == hipSuccess)
+        e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned), (size_t)(num_experts + 1) * 4,
+                          hipHostMallocDefault);
+    if (e != hipSuccess) {
+        int rc = hip_fail(e, "moedx_create");
+        moedx_destroy(c);
+        return rc;
+    }
+    *out = c;
+    return MOEDX_OK;
+}
+
+int moedx_destroy(moedx_ctx* ctx) {
+    if (!ctx) return MOEDX_OK;
+    (void)hipSetDevice(ctx->device);
+    if (ctx->stream) (void)hipStreamSynchronize(ctx->stream);
+    if (ctx->scratch) (void)hipFree(ctx->scratch);
+    if (ctx->pinned) (void)hipHostFree(ctx->pinned);
+    if (ctx->order_event) (void)hipEventDestroy(ctx->order_event);
+    if (ctx->stream) (void)hipStreamDestroy(ctx->stream);
+    delete ctx;
+    return MOEDX_OK;
+}
+
+int moedx_ctx_stats(const moedx_ctx* ctx, moedx_stats* out) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!out) return fail(MOEDX_EINVAL, "out is NULL");
+    *out = ctx->stats;
+    return MOEDX_OK;
+}
+
+int moedx_ctx_stream(const moedx_ctx* ctx, hipStream_t* out) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!out) return fail(MOEDX_EINVAL, "out is NULL");
+    *out = ctx->stream;
+    return MOEDX_OK;
+}
+
+// ---- events -----------------------------------------------------------------
+
+int moedx_event_record(moedx_event** out, hipStream_t stream) {
+    if (!out) return fail(MOEDX_EINVAL, "out is NULL");
+    *out = nullptr;
+    moedx_event* ev = new (std::nothrow) moedx_event;
+    if (!ev) return fail(MOEDX_ENOMEM, "event allocation failed");
+    hipError_t e = hipEventCreate(&ev->ev);
+    if (e == hipSuccess) e = hipEventRecord(ev->ev, stream);
+    if (e != hipSuccess) {
+        (void)hipEventDestroy(ev->ev);
+        delete ev;
+        return hip_fail(e, "moedx_event_record");
+    }
+    *out = ev;
+    return MOEDX_OK;
+}
+
+int moedx_event_wait(const moedx_event* ev, hipStream_t stream) {
+    if (!ev) return fail(MOEDX_EINVAL, "event is NULL");
+    HIP_OR_FAIL(hipStreamWaitEvent(stream, ev->ev, 0));
+    return MOEDX_OK;
+}
+
+int moedx_event_synchronize(const moedx_event* ev) {
+    if (!ev) return fail(MOEDX_EINVAL, "event is NULL");
+    HIP_OR_FAIL(hipEventSynchronize(ev->ev));
+    return MOEDX_OK;
+}
+
+int moedx_event_elapsed_ms(const moedx_event* start, const moedx_event* end, float* ms) {
+    if (!start || !end || !ms) return fail(MOEDX_EINVAL, "NULL argument");
+    HIP_OR_FAIL(hipEventElapsedTime(ms, start->ev, end->ev));
+    return MOEDX_OK;
+}
+
+int moedx_event_destroy(moedx_event* ev) {
+    if (!ev) return MOEDX_OK;
+    (void)hipEventDestroy(ev->ev);
+    delete ev;
+    return MOEDX_OK;
+}
+
+// ---- layout -----------------------------------------------------------------
+
+int moedx_get_dispatch_layout(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K,
+                              int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                              uint8_t* is_token_in_rank, const moedx_exec* exec) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (int rc = check_tokens(ctx, T, K)) return rc;
+    if ((T > 0 && (!topk_idx || !is_token_in_rank)) || !num_tokens_per_rank ||
+        !num_tokens_per_expert)
+        return fail(MOEDX_EINVAL, "NULL device pointer");
+    Exec ex;
+    if (int rc = exec_begin(ctx, exec, &ex)) return rc;
+    const int nt = num_tiles(T);
+    int32_t* tile_rank = static_cast<int32_t*>(ctx->scratch);
+    int32_t* tile_expert = reinterpret_cast<int32_t*>(
+        static_cast<char*>(ctx->scratch) +
+        align256((size_t)std::max(num_tiles(ctx->max_tokens), 1) * ctx->R * 4));
+    HIP_OR_FAIL(launch_layout_tiles(topk_idx, T, K, ctx->E, ctx->R, is_token_in_rank, nullptr,
+                                    tile_rank, tile_expert, ex.run));
+    HIP_OR_FAIL(launch_layout_reduce(tile_rank, tile_expert, nt, ctx->R, ctx->E,
+                                     num_tokens_per_rank, num_tokens_per_expert, ex.run));
+    ctx->stats.layout_launches += 1;
+    return exec_end(ex);
+}
+
+// ---- handle -----------------------------------------------------------------
+
+int moedx_handle_workspace_bytes(const moedx_ctx* ctx, int T, int K, int64_t capacity_rows,
+                                 size_t* bytes) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (int rc = check_tokens(ctx, T, K)) return rc;
+    if (!bytes) return fail(MOEDX_EINVAL, "bytes is NULL");
+    if (capacity_rows < 0) return fail(MOEDX_EINVAL, "capacity_rows < 0");
+    const int64_t rows = capacity_rows > 0 ? capacity_rows : worst_rows(T, K, ctx->R);
+    *bytes = carve_normal(nullptr, nullptr, T, K, ctx->E, ctx->R, ctx->C, rows);
+    return MOEDX_OK;
+}
+
+int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K,
+                           void* workspace, size_t workspace_bytes, int64_t capacity_rows,
+                           moedx_handle** out, const moedx_exec* exec) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!out) return fail(MOEDX_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (int rc = check_tokens(ctx, T, K)) return rc;
+    if ((T > 0 && !topk_idx) || !workspace) return fail(MOEDX_EINVAL, "NULL device pointer");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(MOEDX_EINVAL, "workspace is not 256-byte aligned");
+    if (capacity_rows < 0) return fail(MOEDX_EINVAL, "capacity_rows < 0");
+    const int64_t worst = worst_rows(T, K, ctx->R);
+    if (capacity_rows > 0 && capacity_rows < worst)
+        return fail(MOEDX_ECAPACITY, "capacity_rows=%lld < T*min(K,R)=%lld",
+                    (long long)capacity_rows, (long long)worst);
+    const int64_t rows = capacity_rows > 0 ? capacity_rows : worst;
+    const size_t need = carve_normal(nullptr, nullptr, T, K, ctx->E, ctx->R, ctx->C, rows);
+    if (workspace_bytes < need)
+        return fail(MOEDX_ECAPACITY, "workspace_bytes=%zu < %zu", workspace_bytes, need);
+
+    moedx_handle* h = new (std::nothrow) moedx_handle();
+    if (!h) return fail(MOEDX_ENOMEM, "handle allocation failed");
+    h->kind = kNormal;
+    h->T = T;
+    h->K = K;
+    h->E = ctx->E;
+    h->R = ctx->R;
+    h->P = ctx->P;
+    h->C = ctx->C;
+    h->capacity = capacity_rows;
+    h->n_host = -1;
+    carve_normal(h, static_cast<char*>(workspace), T, K, ctx->E, ctx->R, ctx->C, rows);
+
+    Exec ex;
+    int rc = exec_begin(ctx, exec, &ex);
+    hipError_t e = hipSuccess;
+    if (rc == MOEDX_OK) {
+        e = launch_layout_tiles(topk_idx, T, K, h->E, h->R, h->is_token_in_rank, h->slot_bucket,
+                                h->tile_rank, h->tile_expert, ex.run);
+        if (e == hipSuccess) {
+            ScanOut so{h->num_tokens_per_rank, h->num_tokens_per_expert, h->rank_prefix_matrix,
+                       h->num_recv, h->channel_prefix_matrix, h->recv_channel_prefix_matrix,
+                       h->send_head, h->recv_src_idx};
+            e = launch_scan(h->is_token_in_rank, T, h->R, h->C, h->E, h->tile_rank,
+                            h->tile_expert, so, ex.run);
+        }
+        if (e != hipSuccess) rc = hip_fail(e, "layout/scan launch");
+    }
+    if (rc == MOEDX_OK) {
+        ctx->stats.layout_launches += 1;
+        ctx->stats.scan_launches += 1;
+    }
+    if (rc == MOEDX_OK && capacity_rows == 0) {
+        // Exact mode: the host waits for N and the per-expert counts.
+        e = hipMemcpyAsync(ctx->pinned, h->num_recv, 4, hipMemcpyDeviceToHost, ex.run);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(ctx->pinned + 1, h->num_tokens_per_expert, (size_t)h->E * 4,
+                               hipMemcpyDeviceToHost, ex.run);
+        if (e == hipSuccess) e = hipStreamSynchronize(ex.run);
+        if (e != hipSuccess) {
+            rc = hip_fail(e, "exact-mode count readback");
+        } else {
+            ctx->stats.host_syncs += 1;
+            h->n_host = ctx->pinned[0];
+            h->per_expert_host.assign(ctx->pinned + 1, ctx->pinned + 1 + h->E);
+        }
+    }
+    if (rc == MOEDX_OK) rc = exec_end(ex);
+    if (rc != MOEDX_OK) {
+        delete h;
+        return rc;
+    }
+    *out = h;
+    return MOEDX_OK;
+}
+
+int moedx_handle_num_recv(const moedx_handle* h, int64_t* n) {
+    if (!h || !n) return fail(MOEDX_EINVAL, "NULL argument");
+    if (h->kind != kNormal || h->capacity != 0)
+        return fail(MOEDX_ESTATE, "N is on the host only for exact-mode normal handles");
+    *n = h->n_host;
+    return MOEDX_OK;
+}
+
+int moedx_handle_recv_tokens_per_expert(const moedx_handle* h, int32_t* host_counts) {
+    if (!h || !host_counts) return fail(MOEDX_EINVAL, "NULL argument");
+    if (h->kind != kNormal || h->capacity != 0)
+        return fail(MOEDX_ESTATE, "counts are on the host only for exact-mode normal handles");
+    std::memcpy(host_counts, h->per_expert_host.data(), (size_t)h->E * 4);
+    return MOEDX_OK;
+}
+
+int moedx_handle_tensor(const moedx_handle* h, int which, const void** dev, int64_t shape[2]) {
+    if (!h || !dev || !shape) return fail(MOEDX_EINVAL, "NULL argument");
+    const void* p = nullptr;
+    int64_t s0 = 0, s1 = 1;
+    if (h->kind == kNormal) {
+        switch (which) {
+            case MOEDX_T_RANK_PREFIX_MATRIX: p = h->rank_prefix_matrix; s0 = h->R; break;
+            case MOEDX_T_CHANNEL_PREFIX_MATRIX: p = h->channel_prefix_matrix; s0 = h->R; s1 = h->C; break;
+            case MOEDX_T_RECV_CHANNEL_PREFIX_MATRIX:
+                p = h->recv_channel_prefix_matrix; s0 = h->R; s1 = h->C; break;
+            case MOEDX_T_RECV_SRC_IDX:
+                p = h->recv_src_idx; s0 = h->capacity > 0 ? h->capacity : h->n_host; break;
+            case MOEDX_T_IS_TOKEN_IN_RANK: p = h->is_token_in_rank; s0 = h->T; s1 = h->R; break;
+            case MOEDX_T_SEND_HEAD: p = h->send_head; s0 = h->T; s1 = h->R; break;
+            case MOEDX_T_NUM_TOKENS_PER_RANK: p = h->num_tokens_per_rank; s0 = h->R; break;
+            case MOEDX_T_NUM_TOKENS_PER_EXPERT: p = h->num_tokens_per_expert; s0 = h->E; break;
+            case MOEDX_T_NUM_RECV: p = h->num_recv; s0 = 1; break;
+            default: return fail(MOEDX_EINVAL, "tensor %d is not part of a normal handle", which);
+        }
+    } else {
+        switch (which) {
+            case MOEDX_T_LL_SRC_IDX: p = h->ll_src_idx; s0 = h->E; s1 = h->cap; break;
+            case MOEDX_T_LL_SLOT_OF: p = h->ll_slot_of; s0 = h->T; s1 = h->K; break;
+            default: return fail(MOEDX_EINVAL, "tensor %d is not part of a low-latency handle", which);
+        }
+    }
+    *dev = p;
+    shape[0] = s0;
+    shape[1] = s1;
+    return MOEDX_OK;
+}
+
+int moedx_handle_destroy(moedx_handle* h) {
+    delete h;
+    return MOEDX_OK;
+}
+
+// ---- dispatch / combine -------------------------------------------------------
+
+int moedx_dispatch(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, int H, int quant,
+                   const int64_t* topk_idx, const float* topk_weights, void* recv_x,
+                   float* recv_scales, int64_t* recv_topk_idx, float* recv_topk_weights,
+                   const moedx_exec* exec) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!h || h->kind != kNormal) return fail(MOEDX_EINVAL, "a normal handle is required");
+    if (T != h->T) return fail(MOEDX_ESTATE, "T=%d differs from the handle's T=%d", T, h->T);
+    if (h->E != ctx->E || h->R != ctx->R || h->C != ctx->C)
+        return fail(MOEDX_ESTATE, "handle was prepared on a ctx with a different E/R/C");
+    if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
+    if (quant != MOEDX_QUANT_NONE && quant != MOEDX_QUANT_FP8_E4M3_1X128)
+        return fail(MOEDX_EINVAL, "unknown quant mode %d", quant);
+    if (quant == MOEDX_QUANT_FP8_E4M3_1X128 && H % 128 != 0)
+        return fail(MOEDX_EINVAL, "FP8 dispatch needs H %% 128 == 0 (H=%d)", H);
+    if (T > 0 && (!x || !recv_x)) return fail(MOEDX_EINVAL, "NULL device pointer");
+    if ((T > 0) && (!aligned16(x) || !aligned16(recv_x)))
+        return fail(MOEDX_EINVAL, "x and recv_x must be 16-byte aligned");
+    if (quant == MOEDX_QUANT_FP8_E4M3_1X128 && T > 0 && !recv_scales)
+        return fail(MOEDX_EINVAL, "FP8 dispatch needs recv_scales");
+    if (quant == MOEDX_QUANT_NONE && recv_scales)
+        return fail(MOEDX_EINVAL, "recv_scales is only produced by FP8 dispatch");
+    const bool reuse = (topk_idx == nullptr);
+    if (reuse && (topk_weights || recv_topk_idx || recv_topk_weights))
+        return fail(MOEDX_EINVAL,
+                    "cached dispatch takes no topk_weights and produces no recv_topk_*");
+    if (!reuse && (recv_topk_weights && !topk_weights))
+        return fail(MOEDX_EINVAL, "recv_topk_weights needs topk_weights");
+    if (!reuse && !recv_topk_idx && recv_topk_weights)
+        return fail(MOEDX_EINVAL, "recv_topk_weights needs recv_topk_idx");
+    if (quant == MOEDX_QUANT_FP8_E4M3_1X128 && (recv_topk_idx || recv_topk_weights))
+        return fail(MOEDX_EINVAL, "FP8 dispatch does not produce recv_topk_*");
+    Exec ex;
+    if (int rc = exec_begin(ctx, exec, &ex)) return rc;
+    RowMap rm{h->send_head, h->rank_prefix_matrix, h->num_tokens_per_rank, h->R};
+    if (quant == MOEDX_QUANT_NONE) {
+        HIP_OR_FAIL(launch_pack_bf16(x, T, H, rm, recv_x, topk_idx, topk_weights, h->K, h->E,
+                                     h->P, recv_topk_idx, recv_topk_weights, ex.run));
+        ctx->stats.pack_launches += 1;
+    } else {
+        HIP_OR_FAIL(launch_pack_fp8(x, T, H, rm, recv_x, recv_scales, ex.run));
+        ctx->stats.pack_fp8_launches += 1;
+    }
+    return exec_end(ex);
+}
+
+int moedx_combine(moedx_ctx* ctx, const moedx_handle* h, const uint16_t* y, int H,
+                  const float* gate_weights, const float* recv_topk_weights, uint16_t* out,
+                  float* combined_topk_weights, const moedx_exec* exec) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!h || h->kind != kNormal) return fail(MOEDX_EINVAL, "a normal handle is required");
+    if (h->E != ctx->E || h->R != ctx->R || h->C != ctx->C)
+        return fail(MOEDX_ESTATE, "handle was prepared on a ctx with a different E/R/C");
+    if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
+    if (h->T > 0 && (!y || !out)) return fail(MOEDX_EINVAL, "NULL device pointer");
+    if (h->T > 0 && (!aligned16(y) || !aligned16(out)))
+        return fail(MOEDX_EINVAL, "y and out must be 16-byte aligned");
+    if ((combined_topk_weights != nullptr) != (recv_topk_weights != nullptr))
+        return fail(MOEDX_EINVAL,
+                    "recv_topk_weights and combined_topk_weights go together");
+    Exec ex;
+    if (int rc = exec_begin(ctx, exec, &ex)) return rc;
+    RowMap rm{h->send_head, h->rank_prefix_matrix, h->num_tokens_per_rank, h->R};
+    HIP_OR_FAIL(launch_combine(y, h->T, H, h->K, rm, h->slot_bucket, gate_weights,
+                               recv_topk_weights, out, combined_topk_weights, ex.run));
+    ctx->stats.combine_launches += 1;
+    return exec_end(ex);
+}
+
+// ---- low-latency ----------------------------------------------------------------
+
+int moedx_ll_workspace_bytes(const moedx_ctx* ctx, int T, int K,
+                             int num_max_dispatch_tokens_per_rank, size_t* bytes) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (int rc = check_tokens(ctx, T, K)) return rc;
+    if (!bytes) return fail(MOEDX_EINVAL, "bytes is NULL");
+    if (num_max_dispatch_tokens_per_rank < 1)
+        return fail(MOEDX_EINVAL, "num_max_dispatch_tokens_per_rank < 1");
+    *bytes = carve_ll(nullptr, nullptr, T, K, ctx->E, num_max_dispatch_tokens_per_rank);
+    return MOEDX_OK;
+}
+
+int moedx_ll_dispatch(moedx_ctx* ctx, const uint16_t* x, const int64_t* topk_idx, int T, int K,
+                      int H, int num_max_dispatch_tokens_per_rank, uint16_t* recv_x,
+                      int32_t* recv_count, void* workspace, size_t workspace_bytes,
+                      moedx_handle** out, const moedx_exec* exec) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!out) return fail(MOEDX_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (int rc = check_tokens(ctx, T, K)) return rc;
+    const int cap = num_max_dispatch_tokens_per_rank;
+    if (cap < 1) return fail(MOEDX_EINVAL, "num_max_dispatch_tokens_per_rank < 1");
+    if (T > cap)
+        return fail(MOEDX_ECAPACITY, "T=%d exceeds num_max_dispatch_tokens_per_rank=%d", T, cap);
+    if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
+    if (!recv_count || !workspace || (T > 0 && (!x || !topk_idx || !recv_x)))
+        return fail(MOEDX_EINVAL, "NULL device pointer");
+    if (T > 0 && (!aligned16(x) || !aligned16(recv_x)))
+        return fail(MOEDX_EINVAL, "x and recv_x must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(MOEDX_EINVAL, "workspace is not 256-byte aligned");
+    const size_t need = carve_ll(nullptr, nullptr, T, K, ctx->E, cap);
+    if (workspace_bytes < need)
+        return fail(MOEDX_ECAPACITY, "workspace_bytes=%zu < %zu", workspace_bytes, need);
+    moedx_handle* h = new (std::nothrow) moedx_handle();
+    if (!h) return fail(MOEDX_ENOMEM, "handle allocation failed");
+    h->kind = kLowLatency;
+    h->T = T;
+    h->K = K;
+    h->E = ctx->E;
+    h->R = ctx->R;
+    h->P = ctx->P;
+    h->C = ctx->C;
+    h->cap = cap;
+    carve_ll(h, static_cast<char*>(workspace), T, K, ctx->E, cap);
+    Exec ex;
+    int rc = exec_begin(ctx, exec, &ex);
+    if (rc == MOEDX_OK) {
+        hipError_t e = launch_ll_dispatch(x, topk_idx, T, K, H, h->E, cap, recv_x, recv_count,
+                                          h->ll_src_idx, h->ll_slot_of, ex.run);
+        if (e != hipSuccess) rc = hip_fail(e, "ll dispatch launch");
+    }
+    if (rc == MOEDX_OK) {
+        ctx->stats.ll_dispatch_launches += 1;
+        rc = exec_end(ex);
+    }
+    if (rc != MOEDX_OK) {
+        delete h;
+        return rc;
+    }
+    *out = h;
+    return MOEDX_OK;
+}
+
+int moedx_ll_combine(moedx_ctx* ctx, const uint16_t* y, const int64_t* topk_idx,
+                     const float* topk_weights, const moedx_handle* h, int H, uint16_t* out,
+                     const moedx_exec* exec) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!h || h->kind != kLowLatency) return fail(MOEDX_EINVAL, "a low-latency handle is required");
+    if (h->E != ctx->E) return fail(MOEDX_ESTATE, "handle was made on a ctx with a different E");
+    if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
+    if (h->T > 0 && (!y || !topk_idx || !topk_weights || !out))
+        return fail(MOEDX_EINVAL, "NULL device pointer");
+    if (h->T > 0 && (!aligned16(y) || !aligned16(out)))
+        return fail(MOEDX_EINVAL, "y and out must be 16-byte aligned");
+    Exec ex;
+    if (int rc = exec_begin(ctx, exec, &ex)) return rc;
+    HIP_OR_FAIL(launch_ll_combine(y, topk_idx, topk_weights, h->ll_slot_of, h->T, h->K, H, h->E,
+                                  h->cap, out, ex.run));
+    ctx->stats.ll_combine_launches += 1;
+    return exec_end(ex);
+}
+
+}  // extern "C"

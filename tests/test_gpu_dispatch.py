@@ -1,0 +1,179 @@
+"""GPU parity: layout, handle, bf16 / FP8 pack and combine against the oracle.
+
+Every configuration runs at its full size, in the launch configuration the
+benchmark uses, and every output element is compared: bit-exact for counts,
+prefixes, indices, packed bf16 rows and FP8 codes and scales; within one bf16
+ulp for the combine.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from combine_get_dispatch_layout_amd import workloads as wl
+from tests.gpu_common import (assert_bf16_within_1ulp, assert_equal, check_handle, device,
+                              make_buffer, np_, oracle_first_dispatch)
+from tests.helpers import bf16_bits, bits_to_f32, f32_to_bf16_torch
+
+pytestmark = pytest.mark.gpu
+
+NORMAL = [wl.TINY, wl.PREFILL, wl.FP8_SKEWED, wl.HANDLE_REUSE]
+
+
+def _channels(w):
+    return max(w.channels, 1)
+
+
+@pytest.mark.parametrize("w", NORMAL + [wl.LL_DECODE], ids=lambda w: w.name)
+def test_get_dispatch_layout(oracle, w):
+    dev = device()
+    print(f"[layout] {w.name}", flush=True)
+    inp = wl.make_inputs(w)
+    buf = make_buffer(w.experts, w.ranks, _channels(w), w.tokens)
+    ntr, none, nte, itr, ev = buf.get_dispatch_layout(inp.topk_idx.to(dev), w.experts)
+    assert none is None
+    ref = oracle.layout(inp.topk_idx.numpy(), w.experts, w.ranks)
+    assert_equal("num_tokens_per_rank", np_(ntr), ref.num_tokens_per_rank)
+    assert_equal("num_tokens_per_expert", np_(nte), ref.num_tokens_per_expert)
+    assert_equal("is_token_in_rank", np_(itr), ref.is_token_in_rank)
+
+
+@pytest.mark.parametrize("w", NORMAL, ids=lambda w: w.name)
+@pytest.mark.parametrize("mode", ["exact", "capacity"])
+def test_first_dispatch_and_combine(oracle, w, mode):
+    dev = device()
+    print(f"[dispatch] {w.name} {mode}", flush=True)
+    inp = wl.make_inputs(w)
+    E, R, C, T, H, K = w.experts, w.ranks, _channels(w), w.tokens, w.hidden, w.topk
+    ref = oracle_first_dispatch(oracle, inp, E, R, C)
+    N = ref.prefix.num_recv
+    buf = make_buffer(E, R, C, T)
+    x, idx, gw = inp.x.to(dev), inp.topk_idx.to(dev), inp.topk_weights.to(dev)
+    cap = T * min(K, R) if mode == "capacity" else 0
+    out = None
+    if cap:
+        out = torch.full((cap, H), -7.0, dtype=torch.bfloat16, device=dev)  # sentinel rows
+    recv_x, rti, rtw, per_expert, h, _ = buf.dispatch(x, topk_idx=idx, topk_weights=gw,
+                                                      num_worst_tokens=cap, out=out)
+    torch.cuda.synchronize()
+    check_handle(h, ref, N)
+    rx = np_(recv_x)
+    assert_equal("recv_x", rx[:N], ref.recv_x)
+    assert_equal("recv_topk_idx", np_(rti)[:N], ref.recv_topk_idx)
+    assert_equal("recv_topk_weights", np_(rtw)[:N].view(np.uint32), ref.recv_topk_weights.view(np.uint32))
+    if cap:
+        assert (rx[N:] == bf16_bits(torch.tensor([-7.0], dtype=torch.bfloat16))[0]).all()
+        assert per_expert is None
+    else:
+        assert rx.shape[0] == N
+        assert per_expert == ref.layout.num_tokens_per_expert.tolist()
+
+    # Combine 1: identity expert, no gate weights -> |R(t)| * x, plus the weight payload.
+    comb, cw, _ = buf.combine(recv_x, h, topk_weights=rtw)
+    want, want_cw = oracle.combine(ref.recv_x, inp.topk_idx.numpy(), E, ref.prefix,
+                                   recv_topk_weights=ref.recv_topk_weights)
+    assert_bf16_within_1ulp("combine(unweighted)", np_(comb), want)
+    assert_equal("combined_topk_weights", np_(cw).view(np.uint32), want_cw.view(np.uint32))
+    # Combine 2: distinct expert outputs and gate weights.
+    g = torch.Generator().manual_seed(w.seed + 100)
+    scale = (torch.rand(N, H, generator=g) + 0.5).to(torch.bfloat16)
+    y_cpu = (inp.x[torch.from_numpy(ref.prefix.recv_src_idx).long()] * scale).to(torch.bfloat16)
+    y = torch.zeros(recv_x.shape[0], H, dtype=torch.bfloat16, device=dev)
+    y[:N] = y_cpu.to(dev)
+    comb_w, _, _ = buf.combine(y, h, gate_weights=gw)
+    want_w, _ = oracle.combine(bf16_bits(y_cpu), inp.topk_idx.numpy(), E, ref.prefix, gate_weights=inp.topk_weights.numpy())
+    assert_bf16_within_1ulp("combine(weighted)", np_(comb_w), want_w)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("w", [wl.FP8_SKEWED, wl.TINY, wl.PREFILL], ids=lambda w: w.name)
+def test_fp8_dispatch(oracle, w):
+    dev = device()
+    print(f"[fp8] {w.name}", flush=True)
+    inp = wl.make_inputs(w)
+    E, R, C, T, H, K = w.experts, w.ranks, _channels(w), w.tokens, w.hidden, w.topk
+    ref = oracle_first_dispatch(oracle, inp, E, R, C, with_rows=False)
+    N = ref.prefix.num_recv
+    codes_ref, scales_ref = oracle.pack_fp8(bf16_bits(inp.x), ref.prefix)
+    buf = make_buffer(E, R, C, T)
+    x, idx = inp.x.to(dev), inp.topk_idx.to(dev)
+    (codes, scales), rti, rtw, _, h, _ = buf.dispatch(x, topk_idx=idx, fp8=True)
+    torch.cuda.synchronize()
+    assert rti is None and rtw is None
+    check_handle(h, ref, N)
+    assert_equal("fp8 scales", np_(scales).view(np.uint32), scales_ref.view(np.uint32))
+    assert_equal("fp8 codes", np_(codes), codes_ref)
+    # Combine of the dequantised rows (the expert sees bf16(decode(code) * s)).
+    deq = (torch.from_numpy(codes_ref).view(torch.float8_e4m3fn).to(torch.float32).view(N, H // 128, 128)
+           * torch.from_numpy(scales_ref)[:, :, None]).view(N, H).to(torch.bfloat16)
+    comb, _, _ = buf.combine(deq.to(dev), h, gate_weights=inp.topk_weights.to(dev))
+    want, _ = oracle.combine(bf16_bits(deq), inp.topk_idx.numpy(), E, ref.prefix,
+                             gate_weights=inp.topk_weights.numpy())
+    assert_bf16_within_1ulp("combine(fp8 rows)", np_(comb), want)
+
+
+def test_handle_reuse(oracle):
+    """First dispatch builds the handle; ten fresh batches reuse it with no
+    layout or scan launch, each followed by a weighted combine."""
+    w = wl.HANDLE_REUSE
+    dev = device()
+    inp = wl.make_inputs(w)
+    E, R, C, T, H = w.experts, w.ranks, w.channels, w.tokens, w.hidden
+    ref = oracle_first_dispatch(oracle, inp, E, R, C, with_rows=False)
+    buf = make_buffer(E, R, C, T)
+    gw = inp.topk_weights.to(dev)
+    recv0, _, _, _, h, _ = buf.dispatch(inp.x.to(dev), topk_idx=inp.topk_idx.to(dev),
+                                         topk_weights=gw)
+    before = buf.stats()
+    for i, seed in enumerate(w.reuse_seeds):
+        print(f"[reuse] seed {seed}", flush=True)
+        x2 = wl.fresh_x(w, seed)
+        recv, rti, rtw, per_expert, h2, _ = buf.dispatch(x2.to(dev), handle=h)
+        assert h2 is h and rti is None and rtw is None and per_expert is None
+        want, _, _ = oracle.pack_bf16(bf16_bits(x2), inp.topk_idx.numpy(), None, E, ref.prefix,
+                                      with_topk=False)
+        assert_equal(f"reuse recv_x seed {seed}", np_(recv), want)
+        comb, _, _ = buf.combine(recv, h, gate_weights=gw)
+        if i < 2:  # the full fp32 combine oracle is the slow part; two reps suffice
+            wc, _ = oracle.combine(want, inp.topk_idx.numpy(), E, ref.prefix,
+                                   gate_weights=inp.topk_weights.numpy())
+            assert_bf16_within_1ulp("reuse combine", np_(comb), wc)
+        else:  # softmax gates on identity rows give x back bit for bit
+            assert_equal("reuse combine == x", bits_to_f32(np_(comb)), bits_to_f32(bf16_bits(x2)))
+    after = buf.stats()
+    assert after["layout_launches"] == before["layout_launches"]
+    assert after["scan_launches"] == before["scan_launches"]
+    assert after["host_syncs"] == before["host_syncs"]
+    assert after["pack_launches"] == before["pack_launches"] + len(w.reuse_seeds)
+
+
+def test_reuse_equals_first_dispatch(oracle):
+    w = wl.PREFILL
+    dev = device()
+    inp = wl.make_inputs(w, tokens=1000)
+    buf = make_buffer(w.experts, w.ranks, w.channels, 1000)
+    x = inp.x.to(dev)
+    first, _, _, _, h, _ = buf.dispatch(x, topk_idx=inp.topk_idx.to(dev))
+    again, _, _, _, _, _ = buf.dispatch(x, handle=h)
+    assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+def test_cached_dispatch_rejects_topk(oracle):
+    from combine_get_dispatch_layout_amd import _capi
+    dev = device()
+    w = wl.TINY
+    inp = wl.make_inputs(w)
+    buf = make_buffer(w.experts, w.ranks, w.channels, w.tokens)
+    _, _, _, _, h, _ = buf.dispatch(inp.x.to(dev), topk_idx=inp.topk_idx.to(dev))
+    import ctypes
+    recv = torch.empty(h.num_recv, w.hidden, dtype=torch.bfloat16, device=dev)
+    rti = torch.empty(h.num_recv, w.topk, dtype=torch.int64, device=dev)
+    rc = _capi.moedx_dispatch(buf.ctx, h.ptr, ctypes.c_void_p(inp.x.to(dev).data_ptr()), w.tokens,
+                              w.hidden, 0, None, None, ctypes.c_void_p(recv.data_ptr()), None,
+                              ctypes.c_void_p(rti.data_ptr()), None, None)
+    assert rc == _capi.MOEDX_EINVAL
+    # a handle for another T is refused
+    rc = _capi.moedx_dispatch(buf.ctx, h.ptr, ctypes.c_void_p(recv.data_ptr()), w.tokens - 1,
+                              w.hidden, 0, None, None, ctypes.c_void_p(recv.data_ptr()), None,
+                              None, None, None)
+    assert rc == _capi.MOEDX_ESTATE

@@ -1,0 +1,119 @@
+"""GPU parity on edge cases: empty and ragged batches, more channels than
+tokens, empty buckets, every expert of a token in one bucket, empty (-1) slots,
+the size limits (R = 64, E = 1024, K = 16, H = 8) and FP8 blocks of zeros."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as om
+from combine_get_dispatch_layout_amd import workloads as wl
+from tests.gpu_common import (assert_bf16_within_1ulp, assert_equal, check_handle, device,
+                              make_buffer, np_)
+from tests.helpers import bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(o, idx: np.ndarray, H: int, E: int, R: int, C: int, seed: int = 0,
+             x_u16: np.ndarray = None, capacity: bool = False, fp8: bool = False):
+    dev = device()
+    T, K = idx.shape
+    print(f"[edge] T={T} K={K} H={H} E={E} R={R} C={C} cap={capacity} fp8={fp8}", flush=True)
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    if x_u16 is not None:
+        x = torch.from_numpy(x_u16.astype(np.int16)).view(torch.bfloat16).reshape(T, H)
+    w = torch.softmax(torch.randn(T, K, generator=g, dtype=torch.float64), -1).to(torch.float32)
+    ref = om.dispatch(o, bf16_bits(x), idx, w.numpy(), E, R, C)
+    N = ref.prefix.num_recv
+    buf = make_buffer(E, R, C, max(T, 1))
+    ti = torch.from_numpy(idx).to(dev)
+    ntr, _, nte, itr, _ = buf.get_dispatch_layout(ti, E)
+    assert_equal("num_tokens_per_rank", np_(ntr), ref.layout.num_tokens_per_rank)
+    assert_equal("num_tokens_per_expert", np_(nte), ref.layout.num_tokens_per_expert)
+    assert_equal("is_token_in_rank", np_(itr).reshape(T, R), ref.layout.is_token_in_rank)
+    cap = T * min(K, R) if capacity else 0
+    if fp8:
+        (codes, scales), _, _, _, h, _ = buf.dispatch(x.to(dev), topk_idx=ti, fp8=True,
+                                                      num_worst_tokens=cap)
+        cref, sref = o.pack_fp8(bf16_bits(x), ref.prefix)
+        assert_equal("codes", np_(codes)[:N], cref)
+        assert_equal("scales", np_(scales)[:N].view(np.uint32), sref.view(np.uint32))
+        check_handle(h, ref, N)
+        return
+    recv, rti, rtw, _, h, _ = buf.dispatch(x.to(dev), topk_idx=ti, topk_weights=w.to(dev),
+                                           num_worst_tokens=cap)
+    torch.cuda.synchronize()
+    check_handle(h, ref, N)
+    assert_equal("recv_x", np_(recv)[:N], ref.recv_x)
+    assert_equal("recv_topk_idx", np_(rti)[:N], ref.recv_topk_idx)
+    assert_equal("recv_topk_weights", np_(rtw)[:N].view(np.uint32), ref.recv_topk_weights.view(np.uint32))
+    comb, cw, _ = buf.combine(recv, h, topk_weights=rtw, gate_weights=w.to(dev))
+    want, want_cw = o.combine(ref.recv_x, idx, E, ref.prefix, gate_weights=w.numpy(),
+                              recv_topk_weights=ref.recv_topk_weights)
+    assert_bf16_within_1ulp("combine", np_(comb).reshape(T, H), want)
+    assert_equal("combined_topk_weights", np_(cw).reshape(T, K).view(np.uint32), want_cw.view(np.uint32))
+
+
+def _rand(T, E, K, p_empty=0.0, seed=0):
+    return wl.random_routing(np.random.default_rng(seed), T, E, K, p_empty)
+
+
+def test_empty_batch(oracle):
+    run_case(oracle, np.zeros((0, 4), np.int64), 64, 16, 4, 3)
+
+
+def test_single_token(oracle):
+    run_case(oracle, _rand(1, 16, 4), 256, 16, 4, 8)
+
+
+@pytest.mark.parametrize("T", [255, 256, 257, 1000, 3001])
+def test_ragged_tiles(oracle, T):
+    run_case(oracle, _rand(T, 64, 6, seed=T), 128, 64, 16, 7)
+
+
+def test_more_channels_than_tokens(oracle):
+    run_case(oracle, _rand(5, 16, 2, seed=3), 64, 16, 4, 24)
+
+
+def test_all_slots_empty(oracle):
+    run_case(oracle, np.full((40, 4), -1, np.int64), 64, 16, 4, 3)
+
+
+def test_empty_slots_and_empty_bucket(oracle):
+    idx = _rand(300, 12, 3, p_empty=0.4, seed=5)
+    idx[(idx >= 4) & (idx < 8)] = -1  # bucket 1 of 3 gets nothing
+    run_case(oracle, idx, 128, 12, 3, 5)
+
+
+def test_token_with_all_experts_in_one_bucket(oracle):
+    idx = _rand(200, 32, 4, seed=9)
+    idx[::3] = np.array([8, 9, 10, 11])  # bucket 2 of 8 (P = 4) takes all four
+    run_case(oracle, idx, 64, 32, 8, 4)
+
+
+def test_single_bucket(oracle):
+    run_case(oracle, _rand(300, 8, 8, seed=1), 64, 8, 1, 3)
+
+
+def test_limits(oracle):
+    run_case(oracle, _rand(700, 1024, 16, seed=2), 8, 1024, 64, 33)
+
+
+def test_capacity_mode_small(oracle):
+    run_case(oracle, _rand(333, 16, 3, p_empty=0.2, seed=4), 64, 16, 4, 3, capacity=True)
+
+
+def test_fp8_zero_blocks_and_negative_zero(oracle):
+    T, H = 64, 256
+    x = np.asarray(np.random.default_rng(1).integers(0, 1 << 16, (T, H)), np.uint16)
+    x[(x & 0x7F80) == 0x7F80] = 0x3F80  # no inf / nan inputs
+    x[0, :128] = 0
+    x[1, :128] = 0x8000
+    x[2, 128:] = 0x0001  # denormal bf16 values
+    run_case(oracle, _rand(T, 16, 2, seed=6), H, 16, 4, 2, x_u16=x, fp8=True)
+
+
+def test_fp8_capacity(oracle):
+    run_case(oracle, _rand(500, 64, 6, seed=8), 384, 64, 16, 5, fp8=True, capacity=True)

@@ -1,0 +1,83 @@
+"""GPU parity of the low-latency pair: per-expert slot layout, counts, source
+indices, slot-of map, packed slots and the weighted combine."""
+
+import numpy as np
+import pytest
+import torch
+
+from combine_get_dispatch_layout_amd import workloads as wl
+from tests.gpu_common import assert_bf16_within_1ulp, assert_equal, device, make_buffer, np_
+from tests.helpers import bf16_bits, bits_to_f32, f32_to_bf16_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def run_ll(o, x: torch.Tensor, idx: np.ndarray, w: torch.Tensor, E: int, R: int, cap: int):
+    dev = device()
+    T, H = x.shape
+    K = idx.shape[1]
+    print(f"[ll] T={T} K={K} H={H} E={E} cap={cap}", flush=True)
+    buf = make_buffer(E, R, 1, max(T, 1))
+    rx_ref, cnt_ref, src_ref, slot_ref = o.ll_dispatch(bf16_bits(x), idx, E, cap)
+    ti = torch.from_numpy(idx).to(dev)
+    recv_x, cnt, h, ev, hook = buf.low_latency_dispatch(x.to(dev), ti, cap, E)
+    assert hook is None
+    torch.cuda.synchronize()
+    assert_equal("recv_count", np_(cnt), cnt_ref)
+    f = h.fields()
+    src = np_(f["src_idx"])
+    for e in range(E):
+        n = cnt_ref[e]
+        assert_equal(f"src_idx[{e}]", src[e, :n], src_ref[e, :n])
+    assert_equal("slot_of", np_(f["slot_of"]), slot_ref)
+    rx = np_(recv_x)
+    for e in range(E):
+        n = cnt_ref[e]
+        if n:
+            assert_equal(f"recv_x[{e}]", rx[e, :n], rx_ref[e, :n])
+    # weighted combine of the slots as they came back
+    comb, ev2, hook2 = buf.low_latency_combine(recv_x, ti, w.to(dev), h)
+    assert hook2 is None
+    want = o.ll_combine(rx, idx, w.numpy(), slot_ref)
+    assert_bf16_within_1ulp("ll_combine", np_(comb), want)
+    ones = torch.ones_like(w)
+    comb1, _, _ = buf.low_latency_combine(recv_x, ti, ones.to(dev), h)
+    kv = (idx >= 0).sum(1).astype(np.float32)[:, None]
+    assert_equal("ll_combine(unit)", np_(comb1), f32_to_bf16_torch(bits_to_f32(bf16_bits(x)) * kv))
+    return buf
+
+
+def test_ll_decode_config(oracle):
+    w = wl.LL_DECODE
+    inp = wl.make_inputs(w)
+    run_ll(oracle, inp.x, inp.topk_idx.numpy(), inp.topk_weights, w.experts, w.ranks, w.ll_capacity)
+
+
+@pytest.mark.parametrize("T,cap,p_empty", [(1, 4, 0.0), (64, 64, 0.0), (100, 256, 0.3), (37, 40, 0.0)])
+def test_ll_shapes(oracle, T, cap, p_empty):
+    E, K, H = 32, 6, 512
+    idx = wl.random_routing(np.random.default_rng(T), T, E, K, p_empty)
+    g = torch.Generator().manual_seed(T)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    w = torch.softmax(torch.randn(T, K, generator=g, dtype=torch.float64), -1).to(torch.float32)
+    run_ll(oracle, x, idx, w, E, 8, cap)
+
+
+def test_ll_empty_batch(oracle):
+    dev = device()
+    buf = make_buffer(16, 4, 1, 8)
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=dev)
+    idx = torch.empty(0, 2, dtype=torch.int64, device=dev)
+    recv_x, cnt, h, _, _ = buf.low_latency_dispatch(x, idx, 8, 16)
+    assert np_(cnt).tolist() == [0] * 16
+
+
+def test_ll_capacity_check():
+    from combine_get_dispatch_layout_amd import _capi
+    dev = device()
+    buf = make_buffer(16, 4, 1, 64)
+    x = torch.zeros(10, 64, dtype=torch.bfloat16, device=dev)
+    idx = torch.zeros(10, 2, dtype=torch.int64, device=dev)
+    with pytest.raises(_capi.MoedxError) as ei:
+        buf.low_latency_dispatch(x, idx, 8, 16)  # T = 10 > cap = 8
+    assert ei.value.code == _capi.MOEDX_ECAPACITY
