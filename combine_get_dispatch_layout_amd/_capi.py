@@ -45,12 +45,13 @@ MOEDX_T_LL_SLOT_OF = 10
 
 class moedx_exec(ctypes.Structure):
     _fields_ = [("stream", ctypes.c_void_p), ("prev", ctypes.c_void_p),
-                ("done", ctypes.c_void_p), ("flags", ctypes.c_uint32)]
+                ("done", ctypes.c_void_p), ("flags", ctypes.c_uint32),
+                ("kernel_start", ctypes.c_void_p), ("kernel_stop", ctypes.c_void_p)]
 
 
 class moedx_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
-        "layout_launches", "scan_launches", "pack_launches", "pack_fp8_launches",
+        "layout_launches", "pack_launches", "pack_fp8_launches",
         "combine_launches", "ll_dispatch_launches", "ll_combine_launches", "host_syncs")]
 
 
@@ -74,6 +75,7 @@ SIGNATURES = {
     "moedx_ctx_stats": (_I, [_P, ctypes.POINTER(moedx_stats)]),
     "moedx_ctx_stream": (_I, [_P, _PP]),
     "moedx_event_record": (_I, [_PP, _P]),
+    "moedx_event_create": (_I, [_PP]),
     "moedx_event_wait": (_I, [_P, _P]),
     "moedx_event_synchronize": (_I, [_P]),
     "moedx_event_elapsed_ms": (_I, [_P, _P, ctypes.POINTER(ctypes.c_float)]),
@@ -124,12 +126,14 @@ def check(rc: int) -> None:
         raise MoedxError(rc, last_error())
 
 
-def make_exec(stream: int = 0, prev=None, done=None, flags: int = 0) -> moedx_exec:
-    """prev: an event pointer (int) or None; done: a ctypes.c_void_p to receive
-    the completion event, or None."""
+def make_exec(stream: int = 0, prev=None, done=None, flags: int = 0, kernel_start=None,
+              kernel_stop=None) -> moedx_exec:
+    """prev / kernel_start / kernel_stop: event pointers (int) or None; done: a
+    ctypes.c_void_p to receive the completion event, or None."""
     return moedx_exec(ctypes.c_void_p(stream or None), ctypes.c_void_p(prev or None),
                       ctypes.cast(ctypes.byref(done), ctypes.c_void_p) if done is not None else None,
-                      flags)
+                      flags, ctypes.c_void_p(kernel_start or None),
+                      ctypes.c_void_p(kernel_stop or None))
 
 
 # The entry points under their C names.

@@ -20,7 +20,12 @@ from . import _capi as C
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr() or None)
+    if t is None:
+        return None
+    p = t.data_ptr()
+    if p == 0 and t.numel() == 0:  # an empty view still names its allocation
+        p = t.untyped_storage().data_ptr()
+    return ctypes.c_void_p(p or None)
 
 
 def _stream() -> int:
@@ -222,21 +227,21 @@ class Buffer:
         rows = handle.capacity if handle.capacity > 0 else handle.num_recv
         K = handle.K
         dev = x.device
-        # (at least one row is allocated so that an empty receive side still
-        # passes a valid device pointer; the returned views have `rows` rows)
+        # At least one row is allocated so that an empty receive side still
+        # passes a valid device pointer; the returned views have `rows` rows.
         alloc = max(rows, 1)
         if fp8:
-            recv_x = out if out is not None else torch.empty(alloc, H, dtype=torch.uint8, device=dev)[:rows]
+            recv_x = out if out is not None else torch.empty(alloc, H, dtype=torch.uint8, device=dev)
             recv_s = out_scales if out_scales is not None else torch.empty(
-                alloc, H // 128, dtype=torch.float32, device=dev)[:rows]
+                alloc, H // 128, dtype=torch.float32, device=dev)
         else:
-            recv_x = out if out is not None else torch.empty(alloc, H, dtype=torch.bfloat16, device=dev)[:rows]
+            recv_x = out if out is not None else torch.empty(alloc, H, dtype=torch.bfloat16, device=dev)
             recv_s = None
         rti = rtw = None
         if first and not fp8:
-            rti = torch.empty(alloc, K, dtype=torch.int64, device=dev)[:rows]
+            rti = torch.empty(alloc, K, dtype=torch.int64, device=dev)
             if topk_weights is not None:
-                rtw = torch.empty(alloc, K, dtype=torch.float32, device=dev)[:rows]
+                rtw = torch.empty(alloc, K, dtype=torch.float32, device=dev)
         ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream, no_sync)
         tw = topk_weights.contiguous() if topk_weights is not None else None
         ti = topk_idx.contiguous() if (first and not fp8) else None
@@ -246,6 +251,12 @@ class Buffer:
                                  _ptr(recv_s), _ptr(rti), _ptr(rtw), ctypes.byref(ex)))
         per_expert = handle.recv_tokens_per_expert(self.num_experts) if (
             first and handle.capacity == 0) else None
+        if out is None:
+            recv_x = recv_x[:rows]
+        if recv_s is not None and out_scales is None:
+            recv_s = recv_s[:rows]
+        rti = rti[:rows] if rti is not None else None
+        rtw = rtw[:rows] if rtw is not None else None
         rx = (recv_x, recv_s) if fp8 else recv_x
         return rx, rti, rtw, per_expert, handle, self._event(done)
 

@@ -31,8 +31,11 @@ struct moedx_ctx {
     int E, R, P, C, max_tokens;
     hipStream_t stream;      // the ctx's own stream (default priority)
     hipEvent_t order_event;  // orders the ctx stream after the caller's
-    void* scratch;           // per-tile counts of the standalone layout
+    void* scratch;           // layout ticket + partial counts of the standalone layout
     size_t scratch_bytes;
+    unsigned int* ticket;    // zero between layout launches
+    int32_t* group_cnt;      // [ceil(max_tokens/64), R]
+    int32_t* tile_expert;    // [ceil(max_tokens/256), E]
     int32_t* pinned;         // host readback: [0] = N, [1..E] = per-expert counts
     moedx_stats stats;
 };
@@ -45,18 +48,22 @@ struct moedx_handle {
     int64_t capacity;  // 0 = exact mode
     int64_t n_host;    // exact mode only
     std::vector<int32_t> per_expert_host;
+    mutable bool rows_written;  // send_head / recv_src_idx filled by a dispatch
     // device arrays inside the caller's workspace
     uint8_t* is_token_in_rank;
+    uint64_t* token_mask;
     int8_t* slot_bucket;
     int32_t* num_tokens_per_rank;
     int32_t* num_tokens_per_expert;
     int32_t* rank_prefix_matrix;
     int32_t* channel_prefix_matrix;
     int32_t* recv_channel_prefix_matrix;
+    int32_t* group_prefix;
     int32_t* send_head;
     int32_t* recv_src_idx;
     int32_t* num_recv;
-    int32_t* tile_rank;
+    int32_t* group_cnt;
+    int32_t* chan_part;
     int32_t* tile_expert;
     // low-latency
     int cap;
@@ -107,17 +114,21 @@ size_t carve_normal(moedx_handle* h, char* base, int T, int K, int E, int R, int
     const int nt = num_tiles(T);
     moedx_handle tmp;
     moedx_handle* d = h ? h : &tmp;
+    const int ng = num_groups(T);
     d->is_token_in_rank = cv.take<uint8_t>((size_t)T * R);
+    d->token_mask = cv.take<uint64_t>((size_t)T);
     d->slot_bucket = cv.take<int8_t>((size_t)T * K);
     d->num_tokens_per_rank = cv.take<int32_t>(R);
     d->num_tokens_per_expert = cv.take<int32_t>(E);
     d->rank_prefix_matrix = cv.take<int32_t>(R);
     d->channel_prefix_matrix = cv.take<int32_t>((size_t)R * C);
     d->recv_channel_prefix_matrix = cv.take<int32_t>((size_t)R * C);
+    d->group_prefix = cv.take<int32_t>((size_t)std::max(ng, 1) * R);
     d->send_head = cv.take<int32_t>((size_t)T * R);
     d->recv_src_idx = cv.take<int32_t>((size_t)std::max<int64_t>(rows, 1));
     d->num_recv = cv.take<int32_t>(1);
-    d->tile_rank = cv.take<int32_t>((size_t)std::max(nt, 1) * R);
+    d->group_cnt = cv.take<int32_t>((size_t)std::max(ng, 1) * R);
+    d->chan_part = cv.take<int32_t>((size_t)(C + 1) * R);
     d->tile_expert = cv.take<int32_t>((size_t)std::max(nt, 1) * E);
     return cv.off;
 }
@@ -142,6 +153,16 @@ struct Exec {
     hipStream_t run = nullptr;
     moedx_event** done = nullptr;
     bool async = false;
+    hipEvent_t start = nullptr;  // stamped at the op's kernel start
+    hipEvent_t stop = nullptr;   // stamped at the op's kernel end
+    Launch launch() const { return Launch{run, start, stop}; }
+    // An op that launches no kernel still completes its timing events.
+    hipError_t no_kernel() const {
+        hipError_t e = hipSuccess;
+        if (start) e = hipEventRecord(start, run);
+        if (e == hipSuccess && stop) e = hipEventRecord(stop, run);
+        return e;
+    }
 };
 
 int exec_begin(moedx_ctx* ctx, const moedx_exec* ex, Exec* out) {
@@ -150,6 +171,8 @@ int exec_begin(moedx_ctx* ctx, const moedx_exec* ex, Exec* out) {
     out->caller = ex ? ex->stream : nullptr;
     out->done = ex ? ex->done : nullptr;
     out->async = ex && (ex->flags & MOEDX_ASYNC);
+    out->start = (ex && ex->kernel_start) ? ex->kernel_start->ev : nullptr;
+    out->stop = (ex && ex->kernel_stop) ? ex->kernel_stop->ev : nullptr;
     const bool on_ctx = ex && (ex->flags & MOEDX_ON_CTX_STREAM);
     out->run = on_ctx ? ctx->stream : out->caller;
     HIP_OR_FAIL(hipSetDevice(ctx->device));
@@ -227,11 +250,20 @@ int moedx_create(moedx_ctx** out, int device, int num_experts, int num_ranks, in
     c->C = num_channels;
     c->max_tokens = max_tokens;
     const int nt = std::max(num_tiles(max_tokens), 1);
-    c->scratch_bytes = align256((size_t)nt * num_ranks * 4) + align256((size_t)nt * num_experts * 4);
+    const int ng = std::max(num_groups(max_tokens), 1);
+    c->scratch_bytes = 256 + align256((size_t)ng * num_ranks * 4) +
+                       align256((size_t)nt * num_experts * 4);
     hipError_t e = hipSetDevice(device);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->order_event, hipEventDisableTiming);
     if (e == hipSuccess) e = hipMalloc(&c->scratch, c->scratch_bytes);
+    if (e == hipSuccess) e = hipMemset(c->scratch, 0, c->scratch_bytes);  // the ticket starts at 0
+    if (e == hipSuccess) {
+        char* p = static_cast<char*>(c->scratch);
+        c->ticket = reinterpret_cast<unsigned int*>(p);
+        c->group_cnt = reinterpret_cast<int32_t*>(p + 256);
+        c->tile_expert = reinterpret_cast<int32_t*>(p + 256 + align256((size_t)ng * num_ranks * 4));
+    }
     if (e == hipSuccess)
         e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned), (size_t)(num_experts + 1) * 4,
                           hipHostMallocDefault);
@@ -288,6 +320,20 @@ int moedx_event_record(moedx_event** out, hipStream_t stream) {
     return MOEDX_OK;
 }
 
+int moedx_event_create(moedx_event** out) {
+    if (!out) return fail(MOEDX_EINVAL, "out is NULL");
+    *out = nullptr;
+    moedx_event* ev = new (std::nothrow) moedx_event;
+    if (!ev) return fail(MOEDX_ENOMEM, "event allocation failed");
+    hipError_t e = hipEventCreate(&ev->ev);
+    if (e != hipSuccess) {
+        delete ev;
+        return hip_fail(e, "moedx_event_create");
+    }
+    *out = ev;
+    return MOEDX_OK;
+}
+
 int moedx_event_wait(const moedx_event* ev, hipStream_t stream) {
     if (!ev) return fail(MOEDX_EINVAL, "event is NULL");
     HIP_OR_FAIL(hipStreamWaitEvent(stream, ev->ev, 0));
@@ -325,15 +371,22 @@ int moedx_get_dispatch_layout(moedx_ctx* ctx, const int64_t* topk_idx, int T, in
         return fail(MOEDX_EINVAL, "NULL device pointer");
     Exec ex;
     if (int rc = exec_begin(ctx, exec, &ex)) return rc;
-    const int nt = num_tiles(T);
-    int32_t* tile_rank = static_cast<int32_t*>(ctx->scratch);
-    int32_t* tile_expert = reinterpret_cast<int32_t*>(
-        static_cast<char*>(ctx->scratch) +
-        align256((size_t)std::max(num_tiles(ctx->max_tokens), 1) * ctx->R * 4));
-    HIP_OR_FAIL(launch_layout_tiles(topk_idx, T, K, ctx->E, ctx->R, is_token_in_rank, nullptr,
-                                    tile_rank, tile_expert, ex.run));
-    HIP_OR_FAIL(launch_layout_reduce(tile_rank, tile_expert, nt, ctx->R, ctx->E,
-                                     num_tokens_per_rank, num_tokens_per_expert, ex.run));
+    LayoutArgs a{};
+    a.topk_idx = topk_idx;
+    a.T = T;
+    a.K = K;
+    a.E = ctx->E;
+    a.R = ctx->R;
+    a.P = ctx->P;
+    a.C = ctx->C;
+    a.per = T > 0 ? (T + ctx->C - 1) / ctx->C : 1;
+    a.is_token_in_rank = is_token_in_rank;
+    a.num_tokens_per_rank = num_tokens_per_rank;
+    a.num_tokens_per_expert = num_tokens_per_expert;
+    a.group_cnt = ctx->group_cnt;
+    a.tile_expert = ctx->tile_expert;
+    a.ticket = ctx->ticket;
+    HIP_OR_FAIL(launch_layout(a, ex.launch()));
     ctx->stats.layout_launches += 1;
     return exec_end(ex);
 }
@@ -388,21 +441,33 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
     int rc = exec_begin(ctx, exec, &ex);
     hipError_t e = hipSuccess;
     if (rc == MOEDX_OK) {
-        e = launch_layout_tiles(topk_idx, T, K, h->E, h->R, h->is_token_in_rank, h->slot_bucket,
-                                h->tile_rank, h->tile_expert, ex.run);
-        if (e == hipSuccess) {
-            ScanOut so{h->num_tokens_per_rank, h->num_tokens_per_expert, h->rank_prefix_matrix,
-                       h->num_recv, h->channel_prefix_matrix, h->recv_channel_prefix_matrix,
-                       h->send_head, h->recv_src_idx};
-            e = launch_scan(h->is_token_in_rank, T, h->R, h->C, h->E, h->tile_rank,
-                            h->tile_expert, so, ex.run);
-        }
-        if (e != hipSuccess) rc = hip_fail(e, "layout/scan launch");
+        LayoutArgs a{};
+        a.topk_idx = topk_idx;
+        a.T = T;
+        a.K = K;
+        a.E = h->E;
+        a.R = h->R;
+        a.P = h->P;
+        a.C = h->C;
+        a.per = T > 0 ? (T + h->C - 1) / h->C : 1;
+        a.is_token_in_rank = h->is_token_in_rank;
+        a.token_mask = h->token_mask;
+        a.slot_bucket = h->slot_bucket;
+        a.num_tokens_per_rank = h->num_tokens_per_rank;
+        a.num_tokens_per_expert = h->num_tokens_per_expert;
+        a.rank_prefix_matrix = h->rank_prefix_matrix;
+        a.num_recv = h->num_recv;
+        a.group_prefix = h->group_prefix;
+        a.channel_prefix_matrix = h->channel_prefix_matrix;
+        a.recv_channel_prefix_matrix = h->recv_channel_prefix_matrix;
+        a.group_cnt = h->group_cnt;
+        a.chan_part = h->chan_part;
+        a.tile_expert = h->tile_expert;
+        a.ticket = ctx->ticket;
+        e = launch_layout(a, ex.launch());
+        if (e != hipSuccess) rc = hip_fail(e, "layout launch");
     }
-    if (rc == MOEDX_OK) {
-        ctx->stats.layout_launches += 1;
-        ctx->stats.scan_launches += 1;
-    }
+    if (rc == MOEDX_OK) ctx->stats.layout_launches += 1;
     if (rc == MOEDX_OK && capacity_rows == 0) {
         // Exact mode: the host waits for N and the per-expert counts.
         e = hipMemcpyAsync(ctx->pinned, h->num_recv, 4, hipMemcpyDeviceToHost, ex.run);
@@ -504,7 +569,7 @@ int moedx_dispatch(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, 
     if (quant == MOEDX_QUANT_NONE && recv_scales)
         return fail(MOEDX_EINVAL, "recv_scales is only produced by FP8 dispatch");
     const bool reuse = (topk_idx == nullptr);
-    if (reuse && (topk_weights || recv_topk_idx || recv_topk_weights))
+    if (T > 0 && reuse && (topk_weights || recv_topk_idx || recv_topk_weights))
         return fail(MOEDX_EINVAL,
                     "cached dispatch takes no topk_weights and produces no recv_topk_*");
     if (!reuse && (recv_topk_weights && !topk_weights))
@@ -515,15 +580,22 @@ int moedx_dispatch(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, 
         return fail(MOEDX_EINVAL, "FP8 dispatch does not produce recv_topk_*");
     Exec ex;
     if (int rc = exec_begin(ctx, exec, &ex)) return rc;
-    RowMap rm{h->send_head, h->rank_prefix_matrix, h->num_tokens_per_rank, h->R};
-    if (quant == MOEDX_QUANT_NONE) {
-        HIP_OR_FAIL(launch_pack_bf16(x, T, H, rm, recv_x, topk_idx, topk_weights, h->K, h->E,
-                                     h->P, recv_topk_idx, recv_topk_weights, ex.run));
+    const RowMap rm{h->token_mask, h->group_prefix, h->rank_prefix_matrix, h->num_tokens_per_rank,
+                    h->R, h->T, h->capacity > 0 ? h->capacity : h->n_host};
+    // The first dispatch on a handle also writes send_head and recv_src_idx.
+    const HandleRows hr = h->rows_written ? HandleRows{nullptr, nullptr}
+                                          : HandleRows{h->send_head, h->recv_src_idx};
+    if (T == 0) {
+        HIP_OR_FAIL(ex.no_kernel());
+    } else if (quant == MOEDX_QUANT_NONE) {
+        HIP_OR_FAIL(launch_pack_bf16(x, T, H, rm, hr, recv_x, topk_idx, topk_weights, h->K, h->E,
+                                     h->P, recv_topk_idx, recv_topk_weights, ex.launch()));
         ctx->stats.pack_launches += 1;
     } else {
-        HIP_OR_FAIL(launch_pack_fp8(x, T, H, rm, recv_x, recv_scales, ex.run));
+        HIP_OR_FAIL(launch_pack_fp8(x, T, H, rm, hr, recv_x, recv_scales, ex.launch()));
         ctx->stats.pack_fp8_launches += 1;
     }
+    h->rows_written = true;
     return exec_end(ex);
 }
 
@@ -535,18 +607,26 @@ int moedx_combine(moedx_ctx* ctx, const moedx_handle* h, const uint16_t* y, int 
     if (h->E != ctx->E || h->R != ctx->R || h->C != ctx->C)
         return fail(MOEDX_ESTATE, "handle was prepared on a ctx with a different E/R/C");
     if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
-    if (h->T > 0 && (!y || !out)) return fail(MOEDX_EINVAL, "NULL device pointer");
+    // y may be NULL only when there is provably no receive row (exact mode, N = 0)
+    const bool no_rows = h->capacity == 0 && h->n_host == 0;
+    if (h->T > 0 && (!out || (!y && !no_rows))) return fail(MOEDX_EINVAL, "NULL device pointer");
     if (h->T > 0 && (!aligned16(y) || !aligned16(out)))
         return fail(MOEDX_EINVAL, "y and out must be 16-byte aligned");
-    if ((combined_topk_weights != nullptr) != (recv_topk_weights != nullptr))
+    if (h->T > 0 && (combined_topk_weights != nullptr) != (recv_topk_weights != nullptr))
         return fail(MOEDX_EINVAL,
                     "recv_topk_weights and combined_topk_weights go together");
     Exec ex;
     if (int rc = exec_begin(ctx, exec, &ex)) return rc;
-    RowMap rm{h->send_head, h->rank_prefix_matrix, h->num_tokens_per_rank, h->R};
-    HIP_OR_FAIL(launch_combine(y, h->T, H, h->K, rm, h->slot_bucket, gate_weights,
-                               recv_topk_weights, out, combined_topk_weights, ex.run));
-    ctx->stats.combine_launches += 1;
+    const RowMap rm{h->token_mask, h->group_prefix, h->rank_prefix_matrix, h->num_tokens_per_rank,
+                    h->R, h->T, h->capacity > 0 ? h->capacity : h->n_host};
+    if (h->T == 0) {
+        HIP_OR_FAIL(ex.no_kernel());
+    } else {
+        HIP_OR_FAIL(launch_combine(y, h->T, H, h->K, rm, h->slot_bucket, gate_weights,
+                                   recv_topk_weights, out, combined_topk_weights, h->send_head,
+                                   ex.launch()));
+        ctx->stats.combine_launches += 1;
+    }
     return exec_end(ex);
 }
 
@@ -600,7 +680,7 @@ int moedx_ll_dispatch(moedx_ctx* ctx, const uint16_t* x, const int64_t* topk_idx
     int rc = exec_begin(ctx, exec, &ex);
     if (rc == MOEDX_OK) {
         hipError_t e = launch_ll_dispatch(x, topk_idx, T, K, H, h->E, cap, recv_x, recv_count,
-                                          h->ll_src_idx, h->ll_slot_of, ex.run);
+                                          h->ll_src_idx, h->ll_slot_of, ex.launch());
         if (e != hipSuccess) rc = hip_fail(e, "ll dispatch launch");
     }
     if (rc == MOEDX_OK) {
@@ -628,9 +708,13 @@ int moedx_ll_combine(moedx_ctx* ctx, const uint16_t* y, const int64_t* topk_idx,
         return fail(MOEDX_EINVAL, "y and out must be 16-byte aligned");
     Exec ex;
     if (int rc = exec_begin(ctx, exec, &ex)) return rc;
-    HIP_OR_FAIL(launch_ll_combine(y, topk_idx, topk_weights, h->ll_slot_of, h->T, h->K, H, h->E,
-                                  h->cap, out, ex.run));
-    ctx->stats.ll_combine_launches += 1;
+    if (h->T == 0) {
+        HIP_OR_FAIL(ex.no_kernel());
+    } else {
+        HIP_OR_FAIL(launch_ll_combine(y, topk_idx, topk_weights, h->ll_slot_of, h->T, h->K, H,
+                                      h->E, h->cap, out, ex.launch()));
+        ctx->stats.ll_combine_launches += 1;
+    }
     return exec_end(ex);
 }
 

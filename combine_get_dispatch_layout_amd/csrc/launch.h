@@ -1,73 +1,115 @@
 // Internal launchers of the gfx950 kernels (host functions; not exported).
-// Each launcher enqueues one kernel on `stream` and returns the HIP status of
-// the launch.  Shapes have been validated by the C-ABI layer before any call.
+// Each launcher enqueues exactly one kernel on L.stream and returns the HIP
+// status of the launch.  Shapes have been validated by the C-ABI layer.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace moedx {
 
-constexpr int kTile = 256;        // tokens per workgroup of the layout and scan kernels
-constexpr int kMaxRanks = 64;     // buckets fit one 64-bit wavefront mask
-constexpr int kMaxExperts = 1024; // LDS histogram bound
+constexpr int kTile = 256;         // tokens per workgroup of the layout kernel
+constexpr int kGroup = 64;         // tokens per receive-position group (one wavefront)
+constexpr int kMaxRanks = 64;      // buckets fit one 64-bit mask
+constexpr int kMaxExperts = 1024;  // LDS histogram bound
 constexpr int kMaxTopk = 16;
 
-inline int num_tiles(int T) { return (T + kTile - 1) / kTile; }
+__host__ __device__ inline int num_tiles(int T) { return (T + kTile - 1) / kTile; }
+__host__ __device__ inline int num_groups(int T) { return (T + kGroup - 1) / kGroup; }
 
-// Layout: per-token bucket mask, is_token_in_rank, bucket of each slot and
-// per-tile counts (tile_rank [ntiles, R], tile_expert [ntiles, E]).
-hipError_t launch_layout_tiles(const int64_t* topk_idx, int T, int K, int E, int R,
-                               uint8_t* is_token_in_rank, int8_t* slot_bucket,
-                               int32_t* tile_rank, int32_t* tile_expert, hipStream_t stream);
-
-// Column sums of the per-tile counts: num_tokens_per_rank [R], num_tokens_per_expert [E].
-hipError_t launch_layout_reduce(const int32_t* tile_rank, const int32_t* tile_expert, int ntiles,
-                                int R, int E, int32_t* num_tokens_per_rank,
-                                int32_t* num_tokens_per_expert, hipStream_t stream);
-
-// Scan: counts, prefix matrices, send_head, recv_src_idx and N.
-struct ScanOut {
-    int32_t* num_tokens_per_rank;
-    int32_t* num_tokens_per_expert;
-    int32_t* rank_prefix_matrix;
-    int32_t* num_recv;
-    int32_t* channel_prefix_matrix;
-    int32_t* recv_channel_prefix_matrix;
-    int32_t* send_head;
-    int32_t* recv_src_idx;
+// Where a launch goes and, optionally, events stamped with the kernel's own
+// start and end (hipExtLaunchKernel), for kernel-accurate timing.
+struct Launch {
+    hipStream_t stream;
+    hipEvent_t start;
+    hipEvent_t stop;
 };
-hipError_t launch_scan(const uint8_t* is_token_in_rank, int T, int R, int C, int E,
-                       const int32_t* tile_rank, const int32_t* tile_expert, const ScanOut& out,
-                       hipStream_t stream);
 
-// Receive-row lookup shared by pack and combine: row(t,r) = base[r] + send_head[t,r],
-// base[r] = rank_prefix_matrix[r] - num_tokens_per_rank[r].
+template <typename Tup, size_t... I>
+inline void fill_args(void** argv, Tup& tup, std::index_sequence<I...>) {
+    ((argv[I] = static_cast<void*>(&std::get<I>(tup))), ...);
+}
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, const Launch& L,
+                                Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    std::tuple<KArgs...> tup(static_cast<KArgs>(args)...);
+    void* argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    fill_args(argv, tup, std::index_sequence_for<KArgs...>{});
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0,
+                              L.stream, L.start, L.stop, 0);
+}
+
+// ---- layout ------------------------------------------------------------------
+
+// Everything the layout kernel reads and writes.  Pointers marked "handle" are
+// null for the standalone get_dispatch_layout.
+struct LayoutArgs {
+    const int64_t* topk_idx;  // [T, K]
+    int T, K, E, R, P, C, per;
+    uint8_t* is_token_in_rank;             // [T, R]
+    uint64_t* token_mask;                  // [T] bucket bit mask (handle)
+    int8_t* slot_bucket;                   // [T, K] bucket of each slot or -1 (handle)
+    int32_t* num_tokens_per_rank;          // [R]
+    int32_t* num_tokens_per_expert;        // [E]
+    int32_t* rank_prefix_matrix;           // [R] inclusive (handle)
+    int32_t* num_recv;                     // [1] (handle)
+    int32_t* group_prefix;                 // [ceil(T/64), R] exclusive, per bucket (handle)
+    int32_t* channel_prefix_matrix;        // [R, C] inclusive (handle)
+    int32_t* recv_channel_prefix_matrix;   // [R, C] exclusive (handle)
+    int32_t* group_cnt;                    // scratch [ceil(T/64), R]
+    int32_t* chan_part;                    // scratch [C + 1, R] (handle)
+    int32_t* tile_expert;                  // scratch [ceil(T/256), E]
+    unsigned int* ticket;                  // zero between launches
+};
+
+hipError_t launch_layout(const LayoutArgs& a, const Launch& L);
+
+// ---- receive rows ------------------------------------------------------------
+
+// row(t, r) = base[r] + group_prefix[t / 64][r] + (tokens of t's 64-token group
+// before t that go to bucket r), base[r] = rank_prefix_matrix[r] - count[r].
 struct RowMap {
-    const int32_t* send_head;           // [T, R]
-    const int32_t* rank_prefix_matrix;  // [R]
-    const int32_t* num_tokens_per_rank; // [R]
+    const uint64_t* token_mask;           // [T]
+    const int32_t* group_prefix;          // [ceil(T/64), R]
+    const int32_t* rank_prefix_matrix;    // [R]
+    const int32_t* num_tokens_per_rank;   // [R]
     int R;
+    int T;
+    int64_t rows;  // rows of the receive buffer; a row at or past it is never touched
 };
 
-hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, void* recv_x,
-                            const int64_t* topk_idx, const float* topk_weights, int K, int E, int P,
-                            int64_t* recv_topk_idx, float* recv_topk_weights, hipStream_t stream);
+// First-dispatch outputs that complete the handle (null on a cached dispatch).
+struct HandleRows {
+    int32_t* send_head;     // [T, R]
+    int32_t* recv_src_idx;  // [rows]
+};
 
-hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, void* recv_x8,
-                           float* recv_scales, hipStream_t stream);
+hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
+                            void* recv_x, const int64_t* topk_idx, const float* topk_weights,
+                            int K, int E, int P, int64_t* recv_topk_idx,
+                            float* recv_topk_weights, const Launch& L);
+
+hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
+                           void* recv_x8, float* recv_scales, const Launch& L);
 
 hipError_t launch_combine(const void* y, int T, int H, int K, const RowMap& rm,
                           const int8_t* slot_bucket, const float* gate_weights,
                           const float* recv_topk_weights, void* out,
-                          float* combined_topk_weights, hipStream_t stream);
+                          float* combined_topk_weights, const int32_t* send_head,
+                          const Launch& L);
 
 hipError_t launch_ll_dispatch(const void* x, const int64_t* topk_idx, int T, int K, int H, int E,
                               int cap, void* recv_x, int32_t* recv_count, int32_t* src_idx,
-                              int32_t* slot_of, hipStream_t stream);
+                              int32_t* slot_of, const Launch& L);
 
 hipError_t launch_ll_combine(const void* y, const int64_t* topk_idx, const float* topk_weights,
                              const int32_t* slot_of, int T, int K, int H, int E, int cap, void* out,
-                             hipStream_t stream);
+                             const Launch& L);
 
 }  // namespace moedx

@@ -1,17 +1,24 @@
-// Dispatch layout and scan kernels for gfx950 (wave64).
+// Dispatch layout kernel for gfx950 (wave64): one launch computes the layout
+// and every prefix the receive side needs.
 //
 // The layout is what get_dispatch_layout returns in the normal-kernel example
 // of the EnflameTechnology/DeepEP README: tokens per bucket, tokens per expert
-// and the token-by-bucket mask.  The scan produces the handle fields listed
-// under "What the Handle Contains" on the handle-reuse page (rank and channel
-// prefix matrices, recv_src_idx, send_head), on the device, so that no host
-// prefix sum is needed.
+// and the token-by-bucket mask.  For a handle it also yields the fields listed
+// under "What the Handle Contains" on the handle-reuse page that do not depend
+// on the row data: rank_prefix_matrix, channel_prefix_matrix and
+// recv_channel_prefix_matrix, all on the device (no host prefix sum).
 //
-// Both kernels give one token to each lane and 256 tokens to a workgroup (a
-// "tile").  Bucket membership of a wave's 64 tokens is a 64-bit ballot per
-// bucket; popcounts give per-wave counts and mbcnt gives each lane's position,
-// so every position is a pure function of the routing: no atomics decide an
-// order, and the result is deterministic.
+// Each workgroup takes a tile of 256 tokens, one per lane.  Bucket membership
+// of a wave's 64 tokens (a "group") is one 64-bit ballot per bucket, so group
+// counts, and the counts from a group's start to any channel boundary inside
+// it, are popcounts of registers the wave already holds; expert counts go
+// through an LDS histogram.  The last workgroup to finish (an atomic ticket;
+// no workgroup ever waits on another) turns the group counts into exclusive
+// per-bucket prefixes with wave shuffles, and derives the bucket totals and
+// offsets, the expert totals and the channel prefixes.  A receive position is
+// then base[r] + group_prefix[g][r] + a popcount inside the group, which the
+// pack and combine kernels evaluate for themselves.  Every value is a pure
+// function of the routing; no atomic decides an order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,108 +29,199 @@ namespace moedx {
 namespace {
 
 constexpr int kWaves = kTile / 64;
+constexpr int kPerThread = 16;  // groups per finishing thread per pass
+constexpr int kBatch = 8;       // loads issued together for the expert totals
+constexpr int kLdsGroups = 8192;  // LDS slots for group prefixes (32 KB)
+constexpr int kLdsChan = 2048;    // LDS slots for channel-boundary partials (8 KB)
 
-__device__ __forceinline__ uint32_t lane_id() {
-    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+// Channel c starts at token b_c = min(c * per, T), c = 0..C (b_C = T).
+__device__ __forceinline__ int64_t boundary(int c, int per, int T) {
+    const int64_t b = (int64_t)c * per;
+    return b < T ? b : T;
 }
 
-// Number of set bits of `mask` below this lane.
-__device__ __forceinline__ uint32_t count_below(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-__global__ __launch_bounds__(kTile) void layout_tiles_kernel(
-    const int64_t* __restrict__ topk_idx, int T, int K, int E, int R, int P,
-    uint8_t* __restrict__ is_token_in_rank, int8_t* __restrict__ slot_bucket,
-    int32_t* __restrict__ tile_rank, int32_t* __restrict__ tile_expert) {
+__global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
     __shared__ int32_t hist[kMaxExperts];
-    __shared__ int32_t wave_cnt[kWaves][kMaxRanks];
+    __shared__ int32_t s_gp[kLdsGroups];   // group prefixes, when ng * R fits
+    __shared__ int32_t s_chan[kLdsChan];   // channel-boundary partials, when (C+1) * R fits
+    __shared__ int32_t s_total[kMaxRanks];
+    __shared__ int32_t s_base[kMaxRanks];
+    __shared__ unsigned int s_ticket;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int t = blockIdx.x * kTile + tid;
+    const int T = a.T, K = a.K, E = a.E, R = a.R;
+    const bool with_channels = a.channel_prefix_matrix != nullptr;
 
+    // ---- phase 1: this tile's tokens ----------------------------------------
+    // The small partials the finishing workgroup reads are stored first and
+    // published (fence + ticket) before the large per-token outputs, so the
+    // fence only waits for them.
+    const int t = blockIdx.x * kTile + tid;
+    uint64_t mask = 0;
+    int64_t ids[kMaxTopk];
+    if (T > 0) {
+        for (int e = tid; e < E; e += kTile) hist[e] = 0;
+        __syncthreads();
+        if (t < T) {
+            const int64_t* row = a.topk_idx + (int64_t)t * K;
+#pragma unroll
+            for (int k = 0; k < kMaxTopk; ++k) ids[k] = (k < K) ? row[k] : -1;
+#pragma unroll
+            for (int k = 0; k < kMaxTopk; ++k) {
+                if (k >= K) break;
+                const int64_t e = ids[k];
+                if (e >= 0 && e < E) {  // ids outside [0, E) are treated as empty slots
+                    mask |= 1ull << ((int)e / a.P);
+                    atomicAdd(&hist[(int)e], 1);
+                }
+            }
+        }
+        // Group (one wave = 64 tokens) counts of every bucket; lane r keeps bucket r.
+        const int g = blockIdx.x * kWaves + wave;
+        const int g_begin = g * kGroup;
+        if (g_begin < T) {
+            int32_t my_cnt = 0;
+            for (int r = 0; r < R; ++r) {
+                const int c = __popcll(__ballot((mask >> r) & 1u));
+                if (lane == r) my_cnt = c;
+            }
+            if (lane < R) a.group_cnt[(int64_t)g * R + lane] = my_cnt;
+            // Channel boundaries inside this group: count from the group start.
+            if (with_channels) {
+                int c = (int)((g_begin + a.per - 1) / a.per);
+                for (; c <= a.C; ++c) {
+                    const int64_t b = boundary(c, a.per, T);
+                    if (b >= T || b >= g_begin + kGroup) break;
+                    const int off = (int)(b - g_begin);
+                    const uint64_t below = off == 0 ? 0ull : (~0ull >> (64 - off));
+                    int32_t part = 0;
+                    for (int r = 0; r < R; ++r) {
+                        const int n = __popcll(__ballot((mask >> r) & 1u) & below);
+                        if (lane == r) part = n;
+                    }
+                    if (lane < R) a.chan_part[(int64_t)c * R + lane] = part;
+                }
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += kTile) a.tile_expert[(int64_t)blockIdx.x * E + e] = hist[e];
+    }
+
+    // ---- phase 2: publish the partials; the last workgroup finishes the job ----
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_ticket = atomicAdd(a.ticket, 1u);
+
+    // The per-token outputs (not read by the finishing step).
+    if (t < T) {
+        uint8_t* out = a.is_token_in_rank + (int64_t)t * R;
+        if ((R & 3) == 0) {
+            for (int r = 0; r < R; r += 4)
+                *reinterpret_cast<uint32_t*>(out + r) =
+                    (uint32_t)((mask >> r) & 1u) | ((uint32_t)((mask >> (r + 1)) & 1u) << 8) |
+                    ((uint32_t)((mask >> (r + 2)) & 1u) << 16) |
+                    ((uint32_t)((mask >> (r + 3)) & 1u) << 24);
+        } else {
+            for (int r = 0; r < R; ++r) out[r] = (uint8_t)((mask >> r) & 1u);
+        }
+        if (a.token_mask) a.token_mask[t] = mask;
+        if (a.slot_bucket) {
+#pragma unroll
+            for (int k = 0; k < kMaxTopk; ++k) {
+                if (k >= K) break;
+                const int64_t e = ids[k];
+                a.slot_bucket[(int64_t)t * K + k] = (e >= 0 && e < E) ? (int8_t)((int)e / a.P) : -1;
+            }
+        }
+    }
+    __syncthreads();
+    if (s_ticket != gridDim.x - 1) return;
+    __threadfence();
+
+    const int ng = num_groups(T);
+    const int nt = T > 0 ? (int)gridDim.x : 0;
+
+    // Expert totals: issue these loads first; they overlap the group scan.
+    const int per_e = E >= kTile ? 1 : kTile / E;
+    int32_t esum[kMaxExperts / kTile];  // one partial per expert this thread sums
+#pragma unroll
+    for (int q = 0; q < kMaxExperts / kTile; ++q) {
+        esum[q] = 0;
+        const int i = tid + q * kTile;
+        if (i >= E * per_e) continue;
+        const int e = i % E, part = i / E;
+        for (int j = part; j < nt; j += per_e * kBatch) {
+            int32_t v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int jj = j + u * per_e;
+                v[u] = jj < nt ? a.tile_expert[(int64_t)jj * E + e] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) esum[q] += v[u];
+        }
+    }
+
+    // Channel-boundary partial counts (written in phase 1) staged in LDS.
+    const int nb = with_channels ? (a.C + 1) * R : 0;
+    const bool cp_in_lds = nb <= kLdsChan;
+    if (cp_in_lds)
+        for (int i = tid; i < nb; i += kTile) s_chan[i] = a.chan_part[i];
+
+    // Exclusive prefix over groups per bucket.  Bucket r owns L consecutive
+    // lanes of one wave (L a power of two, L * R <= 256); each lane takes G
+    // consecutive groups per pass and the L lanes combine their sums with a
+    // shuffle scan.  Prefixes also go to LDS when they fit, for the channel step.
+    int L = 64;
+    while (L * R > kTile) L >>= 1;
+    int G = (ng + L - 1) / L;
+    if (G > kPerThread) G = kPerThread;
+    if (G < 1) G = 1;
+    const bool gp_in_lds = ng * R <= kLdsGroups;
+    const bool scan_thread = tid < L * R;
+    const int sr = tid / L, sj = tid % L;
+    int32_t carry = 0;
+    if (scan_thread) {
+        for (int pass = 0; pass < ng; pass += L * G) {
+            const int g0 = pass + sj * G;
+            int32_t v[kPerThread];
+#pragma unroll
+            for (int u = 0; u < kPerThread; ++u)
+                v[u] = (u < G && g0 + u < ng) ? a.group_cnt[(int64_t)(g0 + u) * R + sr] : 0;
+            int32_t mine = 0;
+#pragma unroll
+            for (int u = 0; u < kPerThread; ++u) mine += v[u];
+            int32_t incl = mine;
+            for (int d = 1; d < L; d <<= 1) {
+                const int32_t n = __shfl_up(incl, d, L);
+                if (sj >= d) incl += n;
+            }
+            int32_t run = carry + incl - mine;
+#pragma unroll
+            for (int u = 0; u < kPerThread; ++u) {
+                const int gg = g0 + u;
+                if (u < G && gg < ng) {
+                    if (a.group_prefix) a.group_prefix[(int64_t)gg * R + sr] = run;
+                    if (gp_in_lds) s_gp[gg * R + sr] = run;
+                }
+                run += v[u];
+            }
+            carry += __shfl(incl, L - 1, L);
+        }
+        if (sj == 0) s_total[sr] = carry;
+    }
+    // Expert partials meet in LDS.
     for (int e = tid; e < E; e += kTile) hist[e] = 0;
     __syncthreads();
-
-    uint64_t mask = 0;
-    if (t < T) {
-        const int64_t* row = topk_idx + (int64_t)t * K;
-        int64_t ids[kMaxTopk];
 #pragma unroll
-        for (int k = 0; k < kMaxTopk; ++k) ids[k] = (k < K) ? row[k] : -1;
-#pragma unroll
-        for (int k = 0; k < kMaxTopk; ++k) {
-            if (k >= K) break;
-            const int64_t e = ids[k];
-            int8_t b = -1;
-            if (e >= 0 && e < E) {  // ids outside [0,E) are treated as empty slots
-                const int r = (int)e / P;
-                mask |= 1ull << r;
-                atomicAdd(&hist[(int)e], 1);
-                b = (int8_t)r;
-            }
-            if (slot_bucket) slot_bucket[(int64_t)t * K + k] = b;
+    for (int q = 0; q < kMaxExperts / kTile; ++q) {
+        const int i = tid + q * kTile;
+        if (i < E * per_e) {
+            if (per_e == 1) hist[i] = esum[q];
+            else atomicAdd(&hist[i % E], esum[q]);
         }
-        uint8_t* out = is_token_in_rank + (int64_t)t * R;
-        for (int r = 0; r < R; ++r) out[r] = (uint8_t)((mask >> r) & 1u);
     }
-
-    for (int r = 0; r < R; ++r) {
-        const uint64_t b = __ballot((mask >> r) & 1u);
-        if ((tid & 63) == 0) wave_cnt[wave][r] = __popcll(b);
-    }
-    __syncthreads();
-    if (tid < R) {
-        int32_t s = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) s += wave_cnt[w][tid];
-        tile_rank[(int64_t)blockIdx.x * R + tid] = s;
-    }
-    for (int e = tid; e < E; e += kTile) tile_expert[(int64_t)blockIdx.x * E + e] = hist[e];
-}
-
-__global__ __launch_bounds__(kTile) void layout_reduce_kernel(
-    const int32_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_expert, int ntiles,
-    int R, int E, int32_t* __restrict__ num_tokens_per_rank,
-    int32_t* __restrict__ num_tokens_per_expert) {
-    const int i = blockIdx.x * kTile + threadIdx.x;
-    if (i < R) {
-        int32_t s = 0;
-        for (int j = 0; j < ntiles; ++j) s += tile_rank[(int64_t)j * R + i];
-        num_tokens_per_rank[i] = s;
-    } else if (i < R + E) {
-        const int e = i - R;
-        int32_t s = 0;
-        for (int j = 0; j < ntiles; ++j) s += tile_expert[(int64_t)j * E + e];
-        num_tokens_per_expert[e] = s;
-    }
-}
-
-// One workgroup per tile of 256 tokens (at least one workgroup, so that an
-// empty batch still writes its zero counts and prefixes).
-__global__ __launch_bounds__(kTile) void scan_kernel(
-    const uint8_t* __restrict__ is_token_in_rank, int T, int R, int C, int per, int E, int ntiles,
-    const int32_t* __restrict__ tile_rank, const int32_t* __restrict__ tile_expert, ScanOut out) {
-    __shared__ int32_t s_before[kMaxRanks];  // rows of bucket r owned by earlier tiles
-    __shared__ int32_t s_total[kMaxRanks];   // rows of bucket r overall
-    __shared__ int32_t s_base[kMaxRanks];    // first row of bucket r
-    __shared__ int32_t wave_cnt[kWaves][kMaxRanks];
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int tile = blockIdx.x;
-
-    if (tid < R) {
-        int32_t before = 0, total = 0;
-        for (int j = 0; j < ntiles; ++j) {
-            const int32_t v = tile_rank[(int64_t)j * R + tid];
-            total += v;
-            before += (j < tile) ? v : 0;
-        }
-        s_before[tid] = before;
-        s_total[tid] = total;
-    }
-    __syncthreads();
     if (tid == 0) {
         int32_t run = 0;
         for (int r = 0; r < R; ++r) {
@@ -132,95 +230,37 @@ __global__ __launch_bounds__(kTile) void scan_kernel(
         }
     }
     __syncthreads();
-
-    if (tile == 0 && tid < R) {
-        out.num_tokens_per_rank[tid] = s_total[tid];
-        out.rank_prefix_matrix[tid] = s_base[tid] + s_total[tid];
-        if (tid == R - 1) *out.num_recv = s_base[tid] + s_total[tid];
+    if (tid < R) {
+        a.num_tokens_per_rank[tid] = s_total[tid];
+        if (a.rank_prefix_matrix) a.rank_prefix_matrix[tid] = s_base[tid] + s_total[tid];
+        if (a.num_recv && tid == R - 1) *a.num_recv = s_base[tid] + s_total[tid];
     }
-    for (int e = tile * kTile + tid; e < E; e += gridDim.x * kTile) {
-        int32_t s = 0;
-        for (int j = 0; j < ntiles; ++j) s += tile_expert[(int64_t)j * E + e];
-        out.num_tokens_per_expert[e] = s;
-    }
-    if (T == 0) {
-        for (int i = tid; i < R * C; i += kTile) {
-            out.channel_prefix_matrix[i] = 0;
-            out.recv_channel_prefix_matrix[i] = 0;
+    for (int e = tid; e < E; e += kTile) a.num_tokens_per_expert[e] = hist[e];
+    // Channel prefixes, one (boundary, bucket) pair per thread:
+    // excl(b, r) = group_prefix[b / 64][r] + (count from the group start to b).
+    for (int i = tid; i < nb; i += kTile) {
+        const int c = i / R, r = i % R;
+        const int64_t b = boundary(c, a.per, T);
+        int32_t val;
+        if (b >= T) {
+            val = s_total[r];
+        } else {
+            const int g = (int)(b / kGroup);
+            const int32_t gp = gp_in_lds ? s_gp[g * R + r] : a.group_prefix[(int64_t)g * R + r];
+            val = gp + (cp_in_lds ? s_chan[i] : a.chan_part[i]);
         }
-        return;
+        if (c < a.C) a.recv_channel_prefix_matrix[r * a.C + c] = val;
+        if (c > 0) a.channel_prefix_matrix[r * a.C + c - 1] = val;
     }
-
-    const int t = tile * kTile + tid;
-    uint64_t mask = 0;
-    if (t < T) {
-        const uint8_t* row = is_token_in_rank + (int64_t)t * R;
-        for (int r = 0; r < R; ++r) mask |= (uint64_t)(row[r] != 0) << r;
-    }
-    // Pass 1: per-wave counts of every bucket.
-    for (int r = 0; r < R; ++r) {
-        const uint64_t b = __ballot((mask >> r) & 1u);
-        if ((tid & 63) == 0) wave_cnt[wave][r] = __popcll(b);
-    }
-    __syncthreads();
-    if (t >= T) return;
-
-    const int c = t / per;
-    const bool chan_start = (t == c * per);
-    const int chan_end = min((c + 1) * per, T);
-    const bool chan_last = (t == chan_end - 1);
-    const bool last_token = (t == T - 1);
-    int32_t* sh = out.send_head + (int64_t)t * R;
-
-    // Pass 2: positions.  excl = tokens before t in bucket r.
-    for (int r = 0; r < R; ++r) {
-        const bool in = (mask >> r) & 1u;
-        const uint64_t b = __ballot(in);
-        int32_t excl = s_before[r] + (int32_t)count_below(b);
-        for (int w = 0; w < wave; ++w) excl += wave_cnt[w][r];
-        sh[r] = in ? excl : -1;
-        if (in) out.recv_src_idx[s_base[r] + excl] = t;
-        if (chan_start) out.recv_channel_prefix_matrix[r * C + c] = excl;
-        if (chan_last) out.channel_prefix_matrix[r * C + c] = excl + (in ? 1 : 0);
-        if (last_token) {
-            for (int c2 = c + 1; c2 < C; ++c2) {  // empty trailing channels
-                out.channel_prefix_matrix[r * C + c2] = s_total[r];
-                out.recv_channel_prefix_matrix[r * C + c2] = s_total[r];
-            }
-        }
-    }
+    if (tid == 0) atomicExch(a.ticket, 0u);
 }
+
 
 }  // namespace
 
-hipError_t launch_layout_tiles(const int64_t* topk_idx, int T, int K, int E, int R,
-                               uint8_t* is_token_in_rank, int8_t* slot_bucket,
-                               int32_t* tile_rank, int32_t* tile_expert, hipStream_t stream) {
-    const int nt = num_tiles(T);
-    if (nt == 0) return hipSuccess;
-    layout_tiles_kernel<<<nt, kTile, 0, stream>>>(topk_idx, T, K, E, R, E / R, is_token_in_rank,
-                                                  slot_bucket, tile_rank, tile_expert);
-    return hipGetLastError();
-}
-
-hipError_t launch_layout_reduce(const int32_t* tile_rank, const int32_t* tile_expert, int ntiles,
-                                int R, int E, int32_t* num_tokens_per_rank,
-                                int32_t* num_tokens_per_expert, hipStream_t stream) {
-    const int blocks = (R + E + kTile - 1) / kTile;
-    layout_reduce_kernel<<<blocks, kTile, 0, stream>>>(tile_rank, tile_expert, ntiles, R, E,
-                                                       num_tokens_per_rank,
-                                                       num_tokens_per_expert);
-    return hipGetLastError();
-}
-
-hipError_t launch_scan(const uint8_t* is_token_in_rank, int T, int R, int C, int E,
-                       const int32_t* tile_rank, const int32_t* tile_expert, const ScanOut& out,
-                       hipStream_t stream) {
-    const int nt = num_tiles(T);
-    const int per = T > 0 ? (T + C - 1) / C : 1;
-    scan_kernel<<<nt > 0 ? nt : 1, kTile, 0, stream>>>(is_token_in_rank, T, R, C, per, E, nt,
-                                                        tile_rank, tile_expert, out);
-    return hipGetLastError();
+hipError_t launch_layout(const LayoutArgs& a, const Launch& L) {
+    const int nt = num_tiles(a.T);
+    return launch_kernel(layout_kernel, dim3(nt > 0 ? nt : 1), dim3(kTile), L, a);
 }
 
 }  // namespace moedx

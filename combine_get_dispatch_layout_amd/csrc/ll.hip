@@ -173,29 +173,26 @@ int ll_slices(int T, int H8) {
 
 hipError_t launch_ll_dispatch(const void* x, const int64_t* topk_idx, int T, int K, int H, int E,
                               int cap, void* recv_x, int32_t* recv_count, int32_t* src_idx,
-                              int32_t* slot_of, hipStream_t stream) {
+                              int32_t* slot_of, const Launch& L) {
     if (T == 0) {  // no token: every count is zero
-        zero_i32_kernel<<<(E + kThreads - 1) / kThreads, kThreads, 0, stream>>>(recv_count, E);
-        return hipGetLastError();
+        return launch_kernel(zero_i32_kernel, dim3((E + kThreads - 1) / kThreads), dim3(kThreads), L,
+                             recv_count, E);
     }
     const int H8 = H / 8;
     const int slices = ll_slices(T, H8);
-    ll_dispatch_kernel<<<T * slices, kThreads, 0, stream>>>(
-        static_cast<const u32x4*>(x), topk_idx, T, K, H8, E, cap, slices,
-        static_cast<u32x4*>(recv_x), recv_count, src_idx, slot_of);
-    return hipGetLastError();
+    return launch_kernel(ll_dispatch_kernel, dim3(T * slices), dim3(kThreads), L,
+                         static_cast<const u32x4*>(x), topk_idx, T, K, H8, E, cap, slices,
+                         static_cast<u32x4*>(recv_x), recv_count, src_idx, slot_of);
 }
 
 hipError_t launch_ll_combine(const void* y, const int64_t* topk_idx, const float* topk_weights,
                              const int32_t* slot_of, int T, int K, int H, int E, int cap, void* out,
-                             hipStream_t stream) {
-    if (T == 0) return hipSuccess;
+                             const Launch& L) {
     const int H8 = H / 8;
     const int slices = ll_slices(T, H8);
-    ll_combine_kernel<<<T * slices, kThreads, 0, stream>>>(
-        static_cast<const u32x4*>(y), topk_idx, topk_weights, slot_of, T, K, H8, E, cap, slices,
-        static_cast<u32x4*>(out));
-    return hipGetLastError();
+    return launch_kernel(ll_combine_kernel, dim3(T * slices), dim3(kThreads), L,
+                         static_cast<const u32x4*>(y), topk_idx, topk_weights, slot_of, T, K, H8,
+                         E, cap, slices, static_cast<u32x4*>(out));
 }
 
 }  // namespace moedx

@@ -3,19 +3,32 @@
 // The dispatch of the normal-kernel example in the EnflameTechnology/DeepEP
 // README moves every token to each rank its routing names; on one GPU the
 // ranks are buckets of one receive buffer, so the move is a copy of x[t] to
-// rows row(t,r) = base[r] + send_head[t,r] (handle fields listed under "What
-// the Handle Contains" on the handle-reuse page).
+// the rows row(t, r) of t's buckets.  A first dispatch also completes the
+// handle ("What the Handle Contains" on the handle-reuse page) with send_head
+// and recv_src_idx; a cached dispatch only moves rows.
 //
-// Design (HBM-bound, no MFMA): one wavefront per token.  The wave reads the
-// token's row once with 16-byte loads (all of a lane's chunks in flight before
-// the first store), then writes it to each destination row with 16-byte
-// non-temporal stores; destination rows are wave-uniform (scalar registers).
-// Rows are located through send_head, so the launch shape never changes a
-// result.
+// Design (HBM-bound, no MFMA): one wavefront per token (or per 1/SPLIT of a
+// token's row).  The wave finds the token's rows itself (rows.h: one ballot per
+// destination bucket), reads its part of the row once with 16-byte loads, all
+// of a lane's chunks in flight before the first store, then writes it to each
+// destination row with 16-byte stores; destination rows are wave-uniform
+// scalars.  Positions are a function of the routing only, so the launch shape
+// never changes a result.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "launch.h"
+#include "rows.h"
+
+#ifndef MOEDX_PACK_SPLIT
+#define MOEDX_PACK_SPLIT 2  // waves per token row
+#endif
+#ifndef MOEDX_PACK_NT_LOAD
+#define MOEDX_PACK_NT_LOAD 1  // streaming (non-temporal) loads of x
+#endif
+#ifndef MOEDX_PACK_NT_STORE
+#define MOEDX_PACK_NT_STORE 0  // streaming (non-temporal) stores of receive rows (measured slower)
+#endif
 
 namespace moedx {
 
@@ -25,45 +38,65 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWavesPerBlock = 4;
+constexpr int kSplit = MOEDX_PACK_SPLIT;
 
-struct Dest {
-    int row;        // this lane's bucket row (lane = bucket), or -1
-    uint64_t mask;  // buckets the token goes to (wave-uniform)
-};
-
-__device__ __forceinline__ Dest token_rows(const RowMap& rm, int t, int lane) {
-    int row = -1;
-    if (lane < rm.R) {
-        const int pos = rm.send_head[(int64_t)t * rm.R + lane];
-        if (pos >= 0) row = rm.rank_prefix_matrix[lane] - rm.num_tokens_per_rank[lane] + pos;
-    }
-    return Dest{row, __ballot(row >= 0)};
+template <typename V>
+__device__ __forceinline__ V load_row(const V* p) {
+#if MOEDX_PACK_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
 }
 
-__device__ __forceinline__ int wave_token() {
-    return __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+template <typename V>
+__device__ __forceinline__ void store_row(V v, V* p) {
+#if MOEDX_PACK_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
 }
 
-// CPL = 16-byte chunks each lane moves per pass over the row.
+// The wave's token and part of the row; t is wave-uniform.
+__device__ __forceinline__ void wave_work(int* t, int* part) {
+    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+    *t = w / kSplit;
+    *part = w - *t * kSplit;
+}
+
+__device__ __forceinline__ void write_handle_rows(const HandleRows& hr, const TokenRows& d, int t,
+                                                  int R, int lane) {
+    if (hr.send_head == nullptr) return;
+    if (lane < R) hr.send_head[(int64_t)t * R + lane] = d.pos;
+    if (d.row >= 0) hr.recv_src_idx[d.row] = t;
+}
+
+// CPL = 16-byte chunks each lane moves per pass over its part of the row.
 template <int CPL>
 __global__ __launch_bounds__(256) void pack_bf16_kernel(
-    const u32x4* __restrict__ x, int T, int H8, RowMap rm, u32x4* __restrict__ recv_x,
-    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int K, int E,
-    int P, int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_topk_weights) {
+    const u32x4* __restrict__ x, int T, int H8, RowMap rm, HandleRows hr,
+    u32x4* __restrict__ recv_x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_weights, int K, int E, int P,
+    int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_topk_weights) {
     const int lane = threadIdx.x & 63;
-    const int t = wave_token();
+    int t, part;
+    wave_work(&t, &part);
     if (t >= T) return;
-    const Dest d = token_rows(rm, t, lane);
+    const TokenRows d = token_rows(rm, t, lane);
+    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     const u32x4* src = x + (int64_t)t * H8;
+    const int c_begin = (int)((int64_t)part * H8 / kSplit);
+    const int c_end = (int)((int64_t)(part + 1) * H8 / kSplit);
 
-    for (int base = 0; base < H8; base += CPL * 64) {
+    for (int base = c_begin; base < c_end; base += CPL * 64) {
         u32x4 v[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = base + i * 64 + lane;
-            if (c < H8) v[i] = __builtin_nontemporal_load(src + c);
+            if (c < c_end) v[i] = load_row(src + c);
         }
-        uint64_t m = d.mask;
+        uint64_t m = d.dest;
         while (m) {
             const int r = __builtin_ctzll(m);
             m &= m - 1;
@@ -72,16 +105,16 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = base + i * 64 + lane;
-                if (c < H8) __builtin_nontemporal_store(v[i], dst + c);
+                if (c < c_end) store_row(v[i], dst + c);
             }
         }
     }
 
-    if (recv_topk_idx != nullptr && lane < K) {
+    if (part == 0 && recv_topk_idx != nullptr && lane < K) {
         const int64_t e = topk_idx[(int64_t)t * K + lane];
         const float w = topk_weights ? topk_weights[(int64_t)t * K + lane] : 0.0f;
         const int eb = (e >= 0 && e < E) ? (int)e / P : -1;
-        uint64_t m = d.mask;
+        uint64_t m = d.dest;
         while (m) {
             const int r = __builtin_ctzll(m);
             m &= m - 1;
@@ -121,23 +154,28 @@ __device__ __forceinline__ uint32_t e4m3_code(float q) {
 // One 16-byte chunk = 8 bf16 values; 16 consecutive lanes form one 1x128 block.
 template <int CPL>
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__ x, int T, int H8,
-                                                       RowMap rm, u32x2* __restrict__ recv_x8,
+                                                       RowMap rm, HandleRows hr,
+                                                       u32x2* __restrict__ recv_x8,
                                                        float* __restrict__ recv_scales) {
     const int lane = threadIdx.x & 63;
-    const int t = wave_token();
+    int t, part;
+    wave_work(&t, &part);
     if (t >= T) return;
-    const Dest d = token_rows(rm, t, lane);
+    const TokenRows d = token_rows(rm, t, lane);
+    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     const u32x4* src = x + (int64_t)t * H8;
-    const int G = H8 >> 4;  // blocks per row
+    const int G = H8 >> 4;  // blocks per row; parts hold whole blocks
+    const int c_begin = (int)((int64_t)part * G / kSplit) * 16;
+    const int c_end = (int)((int64_t)(part + 1) * G / kSplit) * 16;
 
-    for (int base = 0; base < H8; base += CPL * 64) {
+    for (int base = c_begin; base < c_end; base += CPL * 64) {
         u32x2 code[CPL];
         float scale[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = base + i * 64 + lane;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (c < H8) v = __builtin_nontemporal_load(src + c);
+            if (c < c_end) v = load_row(src + c);
             float f[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -161,7 +199,7 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__
             for (int j = 0; j < 4; ++j) hi |= e4m3_code(f[4 + j] / s) << (8 * j);
             code[i] = u32x2{lo, hi};
         }
-        uint64_t m = d.mask;
+        uint64_t m = d.dest;
         while (m) {
             const int r = __builtin_ctzll(m);
             m &= m - 1;
@@ -171,8 +209,8 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = base + i * 64 + lane;
-                if (c < H8) {
-                    __builtin_nontemporal_store(code[i], dst + c);
+                if (c < c_end) {
+                    store_row(code[i], dst + c);
                     if ((lane & 15) == 0) sdst[c >> 4] = scale[i];
                 }
             }
@@ -180,60 +218,65 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__
     }
 }
 
-int pick_cpl(int H8) {
-    const int need = (H8 + 63) / 64;
+int pick_cpl(int chunks) {
+    const int need = (chunks + 63) / 64;
     if (need <= 1) return 1;
     if (need <= 2) return 2;
     if (need <= 4) return 4;
+    if (need <= 7) return 7;
     if (need <= 8) return 8;
     if (need <= 14) return 14;
     return 16;
 }
 
-}  // namespace
-
-hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, void* recv_x,
-                            const int64_t* topk_idx, const float* topk_weights, int K, int E, int P,
-                            int64_t* recv_topk_idx, float* recv_topk_weights, hipStream_t stream) {
-    if (T == 0) return hipSuccess;
-    const int H8 = H / 8;
-    const int blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
-    const u32x4* xs = static_cast<const u32x4*>(x);
-    u32x4* rx = static_cast<u32x4*>(recv_x);
-#define MOEDX_PACK(N)                                                                          \
-    pack_bf16_kernel<N><<<blocks, 256, 0, stream>>>(xs, T, H8, rm, rx, topk_idx, topk_weights, \
-                                                    K, E, P, recv_topk_idx, recv_topk_weights)
-    switch (pick_cpl(H8)) {
-        case 1: MOEDX_PACK(1); break;
-        case 2: MOEDX_PACK(2); break;
-        case 4: MOEDX_PACK(4); break;
-        case 8: MOEDX_PACK(8); break;
-        case 14: MOEDX_PACK(14); break;
-        default: MOEDX_PACK(16); break;
-    }
-#undef MOEDX_PACK
-    return hipGetLastError();
+int pack_blocks(int T) {
+    return (int)(((int64_t)T * kSplit + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
-hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, void* recv_x8,
-                           float* recv_scales, hipStream_t stream) {
-    if (T == 0) return hipSuccess;
+}  // namespace
+
+hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
+                            void* recv_x, const int64_t* topk_idx, const float* topk_weights,
+                            int K, int E, int P, int64_t* recv_topk_idx,
+                            float* recv_topk_weights, const Launch& L) {
     const int H8 = H / 8;
-    const int blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+    const dim3 grid(pack_blocks(T)), block(256);
+    const u32x4* xs = static_cast<const u32x4*>(x);
+    u32x4* rx = static_cast<u32x4*>(recv_x);
+#define MOEDX_PACK(N)                                                                         \
+    return launch_kernel(pack_bf16_kernel<N>, grid, block, L, xs, T, H8, rm, hr, rx, topk_idx, \
+                         topk_weights, K, E, P, recv_topk_idx, recv_topk_weights)
+    switch (pick_cpl((H8 + kSplit - 1) / kSplit)) {
+        case 1: MOEDX_PACK(1);
+        case 2: MOEDX_PACK(2);
+        case 4: MOEDX_PACK(4);
+        case 7: MOEDX_PACK(7);
+        case 8: MOEDX_PACK(8);
+        case 14: MOEDX_PACK(14);
+        default: MOEDX_PACK(16);
+    }
+#undef MOEDX_PACK
+}
+
+hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
+                           void* recv_x8, float* recv_scales, const Launch& L) {
+    const int H8 = H / 8;
+    const dim3 grid(pack_blocks(T)), block(256);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x2* rx = static_cast<u32x2*>(recv_x8);
+    const int per_part = ((H8 / 16 + kSplit - 1) / kSplit) * 16;
 #define MOEDX_PACK8(N) \
-    pack_fp8_kernel<N><<<blocks, 256, 0, stream>>>(xs, T, H8, rm, rx, recv_scales)
-    switch (pick_cpl(H8)) {
-        case 1: MOEDX_PACK8(1); break;
-        case 2: MOEDX_PACK8(2); break;
-        case 4: MOEDX_PACK8(4); break;
-        case 8: MOEDX_PACK8(8); break;
-        case 14: MOEDX_PACK8(14); break;
-        default: MOEDX_PACK8(16); break;
+    return launch_kernel(pack_fp8_kernel<N>, grid, block, L, xs, T, H8, rm, hr, rx, recv_scales)
+    switch (pick_cpl(per_part)) {
+        case 1: MOEDX_PACK8(1);
+        case 2: MOEDX_PACK8(2);
+        case 4: MOEDX_PACK8(4);
+        case 7: MOEDX_PACK8(7);
+        case 8: MOEDX_PACK8(8);
+        case 14: MOEDX_PACK8(14);
+        default: MOEDX_PACK8(16);
     }
 #undef MOEDX_PACK8
-    return hipGetLastError();
 }
 
 }  // namespace moedx

@@ -89,19 +89,24 @@ typedef struct moedx_handle moedx_handle;
  *            destroys it.  If NULL, the call blocks until the op has finished
  *            (async_finish=False), unless MOEDX_ASYNC is set.
  *   flags  : MOEDX_ON_CTX_STREAM | MOEDX_ASYNC.
- * Passing a NULL moedx_exec* means {0, NULL, NULL, 0}. */
+ * Passing a NULL moedx_exec* means {0, NULL, NULL, 0, NULL, NULL}. */
 typedef struct moedx_exec {
     hipStream_t stream;
     const moedx_event *prev;
     moedx_event **done;
     uint32_t flags;
+    /* Optional events from moedx_event_create: stamped when the op's kernel
+     * starts and when it ends (kernel-accurate timing; every op launches one
+     * kernel).  An op that launches no kernel (no token) records both on the
+     * stream instead. */
+    moedx_event *kernel_start;
+    moedx_event *kernel_stop;
 } moedx_exec;
 
 /* Kernel launch counters of a ctx (the cached path launches no layout or
  * scan kernel, [HR] Performance Contract and Constraints). */
 typedef struct moedx_stats {
     int64_t layout_launches;
-    int64_t scan_launches;
     int64_t pack_launches;
     int64_t pack_fp8_launches;
     int64_t combine_launches;
@@ -116,9 +121,11 @@ enum {
     MOEDX_T_RANK_PREFIX_MATRIX = 0,         /* int32 [R], inclusive prefix of per-bucket counts */
     MOEDX_T_CHANNEL_PREFIX_MATRIX = 1,      /* int32 [R, C], inclusive prefix over channels */
     MOEDX_T_RECV_CHANNEL_PREFIX_MATRIX = 2, /* int32 [R, C], exclusive prefix over channels */
-    MOEDX_T_RECV_SRC_IDX = 3,               /* int32 [N] (N rows valid), source token of each row */
+    MOEDX_T_RECV_SRC_IDX = 3,               /* int32 [N] (N rows valid), source token of each row;
+                                               written by the first moedx_dispatch on the handle */
     MOEDX_T_IS_TOKEN_IN_RANK = 4,           /* uint8 [T, R], 0/1 */
-    MOEDX_T_SEND_HEAD = 5,                  /* int32 [T, R], position in bucket or -1 */
+    MOEDX_T_SEND_HEAD = 5,                  /* int32 [T, R], position in bucket or -1;
+                                               written by the first moedx_dispatch on the handle */
     MOEDX_T_NUM_TOKENS_PER_RANK = 6,        /* int32 [R] */
     MOEDX_T_NUM_TOKENS_PER_EXPERT = 7,      /* int32 [E] */
     MOEDX_T_NUM_RECV = 8,                   /* int32 [1], N on the device */
@@ -149,6 +156,9 @@ MOEDX_API int moedx_ctx_stream(const moedx_ctx *ctx, hipStream_t *out);
 
 /* Record a new event on `stream` (Buffer.capture()).  Timing-capable. */
 MOEDX_API int moedx_event_record(moedx_event **out, hipStream_t stream);
+/* A new, not yet recorded, timing-capable event (for moedx_exec.kernel_start /
+ * kernel_stop). */
+MOEDX_API int moedx_event_create(moedx_event **out);
 /* Make `stream` wait for the event without blocking the host
  * (current_stream_wait()). */
 MOEDX_API int moedx_event_wait(const moedx_event *ev, hipStream_t stream);

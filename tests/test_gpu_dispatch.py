@@ -142,7 +142,6 @@ def test_handle_reuse(oracle):
             assert_equal("reuse combine == x", bits_to_f32(np_(comb)), bits_to_f32(bf16_bits(x2)))
     after = buf.stats()
     assert after["layout_launches"] == before["layout_launches"]
-    assert after["scan_launches"] == before["scan_launches"]
     assert after["host_syncs"] == before["host_syncs"]
     assert after["pack_launches"] == before["pack_launches"] + len(w.reuse_seeds)
 
