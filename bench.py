@@ -5,14 +5,19 @@ Workload: 4096 tokens x 7168 hidden bf16, 256 experts top-8 with group-limited
 routing (8 groups of 32 experts, 4 groups kept), 8 logical rank buckets, 24
 channels; seeded synthetic inputs (x ~ N(0,1) in bf16, softmax gate weights).
 
-One step = layout + scan + bf16 pack (with recv_topk_idx / recv_topk_weights)
-+ gate-weighted combine of the identity expert's rows, in capacity mode (no
-host synchronisation inside the step).  Each step's dispatch and combine are
-timed with HIP events on the stream the kernels run on, each after a 1 GiB read
-that evicts the caches, so the figure is HBM-resident work.  The value is
-algorithmic bytes / time (GB/s); tokens/s and the fraction of the 8 TB/s HBM
-peak are reported beside it, with the CPU oracle timed on a sample of the same
-workload as a baseline.
+One step = layout (counts, masks and every prefix) + bf16 pack (with
+recv_topk_idx / recv_topk_weights and the handle's send_head / recv_src_idx) +
+gate-weighted combine of the identity expert's rows, in capacity mode (no host
+synchronisation inside the step); each is one kernel launch.
+
+Timing: each op is launched back to back `--steps` times over three rotating
+buffer sets between two HIP events on its stream, so that no launch reads data
+a recent launch touched (the 256 MB Infinity Cache otherwise serves a good part
+of a just-written receive buffer); a step's time is the sum of the three
+per-op means.  The value is algorithmic bytes / step time (GB/s); tokens/s and
+the fraction of the 8 TB/s HBM peak are reported beside it, with whole steps
+back to back (cache-assisted, labelled as such) and the CPU oracle timed on the
+same workload as a baseline.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -42,19 +47,35 @@ def log(*a):
 def algorithmic_bytes(T, H, K, E, R, C, N):
     """Bytes each step must move (caching re-reads not credited).
 
-    layout : read topk_idx (8TK), write is_token_in_rank (TR) and the R + E + RC counts
-    scan   : read the mask (TR), write send_head (4TR), recv_src_idx (4N),
-             two [R, C] prefix matrices and the [R] rank prefix
-    pack   : read x (2TH) + topk_idx and weights (12TK); write N rows (2NH) and
-             recv_topk_idx / recv_topk_weights (12NK)
+    layout : read topk_idx (8TK); write is_token_in_rank (TR), the R + E counts,
+             the [R] rank prefix and the two [R, C] channel prefix matrices
+    pack   : read x (2TH) + topk_idx and weights (12TK); write N rows (2NH),
+             recv_topk_idx / recv_topk_weights (12NK), and the handle's
+             send_head (4TR) and recv_src_idx (4N)
     combine: read N rows (2NH), send_head (4TR), topk ids and gate weights
              (8TK + 4TK); write T rows (2TH)
     """
-    layout = 8 * T * K + T * R + 4 * (R + E + R * C)
-    scan = T * R + 4 * (T * R + N + 2 * R * C + R)
-    pack = 2 * T * H + 2 * N * H + 12 * T * K + 12 * N * K
+    layout = 8 * T * K + T * R + 4 * (R + E + R + 2 * R * C)
+    pack = 2 * T * H + 2 * N * H + 12 * T * K + 12 * N * K + 4 * T * R + 4 * N
     combine = 2 * N * H + 2 * T * H + 4 * T * R + 8 * T * K + 4 * T * K
-    return {"layout": layout, "scan": scan, "pack": pack, "combine": combine}
+    return {"layout": layout, "pack": pack, "combine": combine}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None once the kernel source differs from the one profiled."""
+    import hashlib
+
+    src = {"pack": "pack.hip", "combine": "combine.hip"}[kernel]
+    path = os.path.join(ROOT, "combine_get_dispatch_layout_amd", "csrc", src)
+    digest = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    summary = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_4096x7168.json")
+    if not os.path.exists(summary):
+        return None
+    rec = json.load(open(summary)).get(kernel)
+    if not rec or rec.get("source_sha256_16") != digest:
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def cpu_baseline(inp, w, budget_s):
@@ -108,128 +129,124 @@ def main():
     inp = wl.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x = inp.x.to(dev)
-    idx = inp.topk_idx.to(dev)
-    gw = inp.topk_weights.to(dev)
     cap = T * min(K, R)
     buf = Buffer(E, R, num_channels=Ch, max_tokens=T)
     ctx = buf.ctx
     nbytes = ctypes.c_size_t()
     C.check(C.moedx_handle_workspace_bytes(ctx, T, K, cap, ctypes.byref(nbytes)))
-    ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
-    recv_x = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
-    rti = torch.empty(cap, K, dtype=torch.int64, device=dev)
-    rtw = torch.empty(cap, K, dtype=torch.float32, device=dev)
-    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    # NSETS independent buffer sets, used in rotation so that no launch reads
+    # data a recent launch touched (the 256 MB Infinity Cache holds a good part
+    # of a freshly written receive buffer).
+    NSETS = 3
+    idx = inp.topk_idx.to(dev)
+    gw = inp.topk_weights.to(dev)
+    sets = []
+    for _ in range(NSETS):
+        sets.append({
+            "x": inp.x.to(dev),
+            "ws": torch.empty(nbytes.value, dtype=torch.uint8, device=dev),
+            "recv": torch.empty(cap, H, dtype=torch.bfloat16, device=dev),
+            "rti": torch.empty(cap, K, dtype=torch.int64, device=dev),
+            "rtw": torch.empty(cap, K, dtype=torch.float32, device=dev),
+            "out": torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+        })
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
     sink = torch.empty((), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    p_idx, p_x, p_gw, p_ws = P(idx), P(x), P(gw), P(ws)
-    p_recv, p_rti, p_rtw, p_out = P(recv_x), P(rti), P(rtw), P(out)
-
-    def new_event():
-        ev = ctypes.c_void_p()
-        C.check(C.moedx_event_create(ctypes.byref(ev)))
-        return ev.value
-
-    def make_ex(ev_pair=None):
-        a, b = ev_pair if ev_pair else (None, None)
-        return C.make_exec(stream.cuda_stream, None, None, C.MOEDX_ASYNC, a, b)
-
-    def elapsed(pair):
-        ms = ctypes.c_float()
-        C.check(C.moedx_event_elapsed_ms(pair[0], pair[1], ctypes.byref(ms)))
-        return ms.value
+    p_idx, p_gw = P(idx), P(gw)
+    ex = C.make_exec(stream.cuda_stream, None, None, C.MOEDX_ASYNC)
+    exr = ctypes.byref(ex)
 
     def flush():
         torch.sum(flush_buf, dim=(0,), out=sink)
 
-    def prepare(ex):
+    def prepare(s_):
         h = ctypes.c_void_p()
-        C.check(C.moedx_dispatch_prepare(ctx, p_idx, T, K, p_ws, nbytes.value, cap,
-                                         ctypes.byref(h), ctypes.byref(ex)))
+        C.check(C.moedx_dispatch_prepare(ctx, p_idx, T, K, P(s_["ws"]), nbytes.value, cap,
+                                         ctypes.byref(h), exr))
         return h
 
-    def pack(h, ex):
-        C.check(C.moedx_dispatch(ctx, h, p_x, T, H, C.MOEDX_QUANT_NONE, p_idx, p_gw, p_recv, None,
-                                 p_rti, p_rtw, ctypes.byref(ex)))
+    def pack(h, s_):
+        C.check(C.moedx_dispatch(ctx, h, P(s_["x"]), T, H, C.MOEDX_QUANT_NONE, p_idx, p_gw,
+                                 P(s_["recv"]), None, P(s_["rti"]), P(s_["rtw"]), exr))
 
-    def combine(h, ex):
-        C.check(C.moedx_combine(ctx, h, p_recv, H, p_gw, None, p_out, None, ctypes.byref(ex)))
+    def combine(h, s_):
+        C.check(C.moedx_combine(ctx, h, P(s_["recv"]), H, p_gw, None, P(s_["out"]), None, exr))
 
-    plain = make_ex()
+    def record():
+        ev = ctypes.c_void_p()
+        C.check(C.moedx_event_record(ctypes.byref(ev), stream.cuda_stream))
+        return ev.value
 
-    # Kernel-accurate per-op timing: each op is one kernel, stamped at its own
-    # start and end; a 1 GiB read before the dispatch and before the combine
-    # evicts the caches, so every op starts from HBM.
-    def flushed_steps(n):
-        recs = []
-        for _ in range(n):
-            evs = {k: (new_event(), new_event()) for k in ("layout", "pack", "combine")}
-            flush()
-            h = prepare(make_ex(evs["layout"]))
-            pack(h, make_ex(evs["pack"]))
-            flush()
-            combine(h, make_ex(evs["combine"]))
-            C.moedx_handle_destroy(h)
-            recs.append(evs)
-        return recs
+    def elapsed_ms(a, b):
+        ms = ctypes.c_float()
+        C.check(C.moedx_event_elapsed_ms(a, b, ctypes.byref(ms)))
+        C.moedx_event_destroy(a)
+        C.moedx_event_destroy(b)
+        return ms.value
 
-    def finish(recs):
+    handles = [prepare(s_) for s_ in sets]
+    for h, s_ in zip(handles, sets):
+        pack(h, s_)
+
+    def op_avg_ms(op, n):
+        """Average duration of n back-to-back launches of one op over rotating sets."""
+        flush()
+        a = record()
+        for i in range(n):
+            j = i % NSETS
+            if op == "layout":
+                C.moedx_handle_destroy(prepare(sets[j]))
+            elif op == "pack":
+                pack(handles[j], sets[j])
+            else:
+                combine(handles[j], sets[j])
+        b = record()
         torch.cuda.synchronize()
-        out_ = {k: [elapsed(r[k]) for r in recs] for k in ("layout", "pack", "combine")}
-        for r in recs:
-            for a, b in r.values():
-                C.moedx_event_destroy(a)
-                C.moedx_event_destroy(b)
-        return out_
+        return elapsed_ms(a, b) / n
 
-    log(f"[bench] warmup {args.warmup} steps")
-    finish(flushed_steps(args.warmup))
-    h = prepare(plain)
+    def pipelined_ms(n):
+        """n whole steps back to back (layout, pack, combine each), rotating sets."""
+        flush()
+        a = record()
+        for i in range(n):
+            s_ = sets[i % NSETS]
+            h = prepare(s_)
+            pack(h, s_)
+            combine(h, s_)
+            C.moedx_handle_destroy(h)
+        b = record()
+        torch.cuda.synchronize()
+        return elapsed_ms(a, b) / n
+
+    log(f"[bench] warmup {args.warmup}")
+    for op in ("layout", "pack", "combine"):
+        op_avg_ms(op, max(args.warmup, 1))
+    pipelined_ms(max(args.warmup, 1))
+    torch.cuda.synchronize()
+    h = handles[0]
     dev_n = ctypes.c_void_p()
     shape = (ctypes.c_int64 * 2)()
     C.check(C.moedx_handle_tensor(h, C.MOEDX_T_NUM_RECV, ctypes.byref(dev_n), shape))
-    torch.cuda.synchronize()
-    off = dev_n.value - ws.data_ptr()
-    N = int(ws[off:off + 4].view(torch.int32).item())
-    C.moedx_handle_destroy(h)
+    off = dev_n.value - sets[0]["ws"].data_ptr()
+    N = int(sets[0]["ws"][off:off + 4].view(torch.int32).item())
     bytes_ = algorithmic_bytes(T, H, K, E, R, Ch, N)
     step_bytes = sum(bytes_.values())
     log(f"[bench] N={N} receive rows; {step_bytes / 1e6:.1f} MB per step")
 
-    log(f"[bench] {args.steps} steps, each op timed at its kernel, caches flushed")
-    torch.cuda.synchronize()
-    times = finish(flushed_steps(args.steps))
-    torch.cuda.synchronize()
-    step_ms = [a + b + c for a, b, c in zip(times["layout"], times["pack"], times["combine"])]
-    ms_flushed = statistics.mean(step_ms)
-    t_lay = statistics.mean(times["layout"])
-    t_pack = statistics.mean(times["pack"])
-    t_comb = statistics.mean(times["combine"])
-
-    log(f"[bench] {args.steps} steps back to back, bracketed by two events")
+    log(f"[bench] timing: {args.steps} launches per op (HBM-cold rotation), {args.steps} pipelined steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ea = ctypes.c_void_p()
-    C.check(C.moedx_event_record(ctypes.byref(ea), stream.cuda_stream))
-    for _ in range(args.steps):
-        hh = prepare(plain)
-        pack(hh, plain)
-        combine(hh, plain)
-        C.moedx_handle_destroy(hh)
-    eb = ctypes.c_void_p()
-    C.check(C.moedx_event_record(ctypes.byref(eb), stream.cuda_stream))
-    torch.cuda.synchronize()
+    t_lay = op_avg_ms("layout", args.steps)
+    t_pack = op_avg_ms("pack", args.steps)
+    t_comb = op_avg_ms("combine", args.steps)
+    ms_pipe = pipelined_ms(args.steps)
     wall = time.perf_counter() - wall0
-    ms_b2b = elapsed((ea.value, eb.value)) / args.steps
-    for ev in (ea.value, eb.value):
-        C.moedx_event_destroy(ev)
-
-    # Headline: the slower (more conservative) of the two measurements.
-    ms = max(ms_flushed, ms_b2b)
+    ms = t_lay + t_pack + t_comb
     gbs = step_bytes / (ms * 1e-3) / 1e9
+    for h in handles:
+        C.moedx_handle_destroy(h)
 
     log("[bench] plain device copy of one receive buffer (context: practical ceiling)")
     nb = 2 * N * H
@@ -252,6 +269,7 @@ def main():
     dom = max(kern, key=lambda k: kern[k][0])
     dom_ms, dom_bytes = kern[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic(dom)
 
     cpu = None
     if args.cpu_budget_s > 0:
@@ -260,7 +278,7 @@ def main():
         assert n_cpu == N
         cpu = {"value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
                "kind": "oracle", "tokens_per_s": round(T / t_cpu, 1),
-               "sample": f"median of {reps} full {T}x{H} steps (layout+scan+pack+weighted "
+               "sample": f"median of {reps} full {T}x{H} steps (layout+prefix+pack+weighted "
                          f"combine), single-threaded C oracle"}
 
     result = {
@@ -279,23 +297,22 @@ def main():
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": E, "topk": K,
                    "ranks": R, "channels": Ch, "routing": w.routing, "recv_rows": N,
                    "mode": "capacity (no host sync)",
-                   "timing": "max of (kernel-stamped ops, caches flushed) and (back-to-back steps)"},
+                   "timing": "sum over layout, pack, combine of each op's mean over back-to-back "
+                             "launches on 3 rotating buffer sets (HBM-cold), HIP events"},
         "tokens_per_s": round(T / (ms * 1e-3), 1),
         "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernels_us": {"layout": round(t_lay * 1e3, 2), "pack": round(t_pack * 1e3, 2),
                        "combine": round(t_comb * 1e3, 2)},
         "kernel_GBps": {"pack": round(bytes_["pack"] / (t_pack * 1e-3) / 1e9, 1),
                         "combine": round(bytes_["combine"] / (t_comb * 1e-3) / 1e9, 1)},
-        "ms_per_step_flushed_kernels": round(ms_flushed, 5),
-        "ms_per_step_back_to_back": round(ms_b2b, 5),
-        "step_ms_p10_p50_p90_flushed": [round(v, 5) for v in statistics.quantiles(step_ms, n=10)[::4]]
-        if len(step_ms) >= 10 else None,
+        "pipelined_ms_per_step": round(ms_pipe, 5),
+        "pipelined_GBps_cache_assisted": round(step_bytes / (ms_pipe * 1e-3) / 1e9, 1),
         "copy_ceiling_GBps": round(copy_gbs, 1),
         "algorithmic_bytes": bytes_,
-        "wall_s_back_to_back": round(wall, 4),
+        "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kWaves = kTile / 64;
 constexpr int kPerThread = 16;  // groups per finishing thread per pass
-constexpr int kBatch = 8;       // loads issued together for the expert totals
+constexpr int kBatch = 16;      // loads issued together for the expert totals
 constexpr int kLdsGroups = 8192;  // LDS slots for group prefixes (32 KB)
 constexpr int kLdsChan = 2048;    // LDS slots for channel-boundary partials (8 KB)
 
@@ -109,7 +109,9 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
     }
 
     // ---- phase 2: publish the partials; the last workgroup finishes the job ----
-    __threadfence();
+    // Release at device scope: the partials are visible to every XCD's L2
+    // before the ticket moves.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (tid == 0) s_ticket = atomicAdd(a.ticket, 1u);
 
@@ -137,7 +139,8 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
     }
     __syncthreads();
     if (s_ticket != gridDim.x - 1) return;
-    __threadfence();
+    // Acquire: drop stale lines before reading the other workgroups' partials.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     const int ng = num_groups(T);
     const int nt = T > 0 ? (int)gridDim.x : 0;

@@ -21,13 +21,13 @@
 #include "rows.h"
 
 #ifndef MOEDX_PACK_SPLIT
-#define MOEDX_PACK_SPLIT 2  // waves per token row
+#define MOEDX_PACK_SPLIT 4  // waves per token row
 #endif
 #ifndef MOEDX_PACK_NT_LOAD
-#define MOEDX_PACK_NT_LOAD 1  // streaming (non-temporal) loads of x
+#define MOEDX_PACK_NT_LOAD 0  // streaming (non-temporal) loads of x
 #endif
 #ifndef MOEDX_PACK_NT_STORE
-#define MOEDX_PACK_NT_STORE 0  // streaming (non-temporal) stores of receive rows (measured slower)
+#define MOEDX_PACK_NT_STORE 1  // streaming (non-temporal) stores of receive rows
 #endif
 
 namespace moedx {
