@@ -103,6 +103,287 @@ def cpu_baseline(inp, w, budget_s):
     return statistics.median(times), len(times), N
 
 
+def row_bytes(kind, T, H, K, E, N=0, V=0, R=0):
+    """Algorithmic bytes of one launch of a further step of the path.
+
+    pack_fp8       : read x (2TH); write N rows of codes (NH) and their 1x128
+                     scales (4N*H/128)
+    cached_dispatch: read x (2TH); write N rows (2NH)
+    get_layout     : read topk_idx (8TK); write is_token_in_rank (TR) and the
+                     R + E counts
+    ll_dispatch    : read x (2TH) and topk_idx (8TK); write the V filled slots
+                     (2VH), their src_idx (4V), slot_of (4TK) and counts (4E)
+    ll_combine     : read the V slots (2VH), topk_idx, weights and slot_of
+                     (16TK); write T rows (2TH)
+    """
+    return {
+        "pack_fp8": 2 * T * H + N * H + 4 * N * (H // 128),
+        "cached_dispatch": 2 * T * H + 2 * N * H,
+        "get_layout": 8 * T * K + T * R + 4 * (R + E),
+        "ll_dispatch": 2 * T * H + 8 * T * K + 2 * V * H + 4 * V + 4 * T * K + 4 * E,
+        "ll_combine": 2 * V * H + 16 * T * K + 2 * T * H,
+    }[kind]
+
+
+def _median_time(fn, budget_s, max_reps=5):
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s or len(times) >= max_reps:
+            return statistics.median(times), len(times)
+
+
+def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
+    """Every further step of the path on its own workload: the FP8 pack, the
+    cached (handle-reuse) dispatch, the standalone layout and the low-latency
+    pair.  Each is launched back to back over rotating buffer sets between two
+    HIP events, like the step above; the CPU oracle is timed on a bounded
+    sample of the same workload."""
+    import numpy as np
+    import torch
+
+    from combine_get_dispatch_layout_amd import Buffer
+    from combine_get_dispatch_layout_amd import _capi as C
+    from combine_get_dispatch_layout_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    ex = C.make_exec(stream.cuda_stream, None, None, C.MOEDX_ASYNC)
+    exr = ctypes.byref(ex)
+    NSETS = 3
+    o = None
+    if cpu_budget_s > 0:
+        import oracle as om
+        o = om.Oracle()
+
+    def record():
+        ev = ctypes.c_void_p()
+        C.check(C.moedx_event_record(ctypes.byref(ev), stream.cuda_stream))
+        return ev.value
+
+    def rot_ms(fns, n):
+        flush()
+        a = record()
+        for i in range(n):
+            fns[i % len(fns)]()
+        b = record()
+        torch.cuda.synchronize()
+        ms = ctypes.c_float()
+        C.check(C.moedx_event_elapsed_ms(a, b, ctypes.byref(ms)))
+        C.moedx_event_destroy(a)
+        C.moedx_event_destroy(b)
+        return ms.value / n
+
+    def timed(fns):
+        rot_ms(fns, max(warmup, 1))
+        return rot_ms(fns, steps)
+
+    def u16(t):
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    def entry(w, kind, ms, nbytes, extra, cpu=None):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        r = {"workload": w.name, "us": round(ms * 1e3, 2), "bytes": int(nbytes),
+             "GBps": round(gbs, 1), "roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
+             "tokens_per_s": round(w.tokens / (ms * 1e-3), 1)}
+        r.update(extra)
+        if cpu is not None:
+            r["cpu_oracle"] = cpu
+        return r
+
+    def cpu_entry(nbytes, secs, reps, sample):
+        return {"GBps": round(nbytes / secs / 1e9, 4), "cores": 1, "sample": sample,
+                "reps": reps}
+
+    def handle_rows(buf, h, ws):
+        dev_n = ctypes.c_void_p()
+        shape = (ctypes.c_int64 * 2)()
+        C.check(C.moedx_handle_tensor(h, C.MOEDX_T_NUM_RECV, ctypes.byref(dev_n), shape))
+        off = dev_n.value - ws.data_ptr()
+        return int(ws[off:off + 4].view(torch.int32).item())
+
+    def normal_sets(w, fp8, seeds):
+        T, H, K, E, R, Ch = w.tokens, w.hidden, w.topk, w.experts, w.ranks, w.channels
+        inp = wl.make_inputs(w)
+        buf = Buffer(E, R, num_channels=Ch, max_tokens=T)
+        cap = T * min(K, R)
+        nb = ctypes.c_size_t()
+        C.check(C.moedx_handle_workspace_bytes(buf.ctx, T, K, cap, ctypes.byref(nb)))
+        idx = inp.topk_idx.to(dev)
+        sets = []
+        for s in seeds:
+            x = (inp.x if s is None else wl.fresh_x(w, s)).to(dev)
+            ws = torch.empty(nb.value, dtype=torch.uint8, device=dev)
+            h = ctypes.c_void_p()
+            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, P(ws), nb.value, cap,
+                                             ctypes.byref(h), exr))
+            if fp8:
+                recv = torch.empty(cap, H, dtype=torch.uint8, device=dev)
+                scales = torch.empty(cap, H // 128, dtype=torch.float32, device=dev)
+            else:
+                recv = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
+                scales = None
+            sets.append({"x": x, "ws": ws, "h": h, "recv": recv, "scales": scales})
+        torch.cuda.synchronize()
+        N = handle_rows(buf, sets[0]["h"], sets[0]["ws"])
+        return inp, buf, idx, sets, N
+
+    rows = {}
+
+    # -- FP8 pack (per-1x128 E4M3) on the skewed 8192-token workload --------------
+    w = wl.FP8_SKEWED
+    log_fn(f"[bench] row pack_fp8: {w.name}")
+    inp, buf, idx, sets, N = normal_sets(w, True, [None] * NSETS)
+    T, H, K, E = w.tokens, w.hidden, w.topk, w.experts
+
+    def fp8_pack(s):
+        return lambda: C.check(C.moedx_dispatch(
+            buf.ctx, s["h"], P(s["x"]), T, H, C.MOEDX_QUANT_FP8_E4M3_1X128, None, None,
+            P(s["recv"]), P(s["scales"]), None, None, exr))
+
+    ms = timed([fp8_pack(s) for s in sets])
+    nbytes = row_bytes("pack_fp8", T, H, K, E, N=N)
+    cpu = None
+    if o is not None:
+        ts = 512
+        si = wl.make_inputs(w, tokens=ts)
+        lay = o.layout(si.topk_idx.numpy(), E, w.ranks)
+        pre = o.prefix(lay.is_token_in_rank, w.channels)
+        xs = u16(si.x)
+        secs, reps = _median_time(lambda: o.pack_fp8(xs, pre), cpu_budget_s / 4)
+        cpu = cpu_entry(row_bytes("pack_fp8", ts, H, K, E, N=pre.num_recv), secs, reps,
+                        f"oracle pack_fp8 on {ts} tokens of the same workload")
+    rows["pack_fp8"] = entry(w, "pack_fp8", ms, nbytes, {"recv_rows": N, "dtype": "bf16->e4m3"}, cpu)
+    for s in sets:
+        C.moedx_handle_destroy(s["h"])
+    del sets, buf
+
+    # -- cached dispatch (handle reuse) on the 16384-token workload --------------
+    w = wl.HANDLE_REUSE
+    log_fn(f"[bench] row cached_dispatch: {w.name}")
+    inp, buf, idx, sets, N = normal_sets(w, False, list(w.reuse_seeds[:NSETS]))
+    T, H, K, E = w.tokens, w.hidden, w.topk, w.experts
+
+    def cached(s):
+        return lambda: C.check(C.moedx_dispatch(
+            buf.ctx, s["h"], P(s["x"]), T, H, C.MOEDX_QUANT_NONE, None, None,
+            P(s["recv"]), None, None, None, exr))
+
+    for s in sets:  # the first dispatch on each handle writes its rows
+        cached(s)()
+    ms = timed([cached(s) for s in sets])
+    nbytes = row_bytes("cached_dispatch", T, H, K, E, N=N)
+    cpu = None
+    if o is not None:
+        ts = 2048
+        si = wl.make_inputs(w, tokens=ts)
+        lay = o.layout(si.topk_idx.numpy(), E, w.ranks)
+        pre = o.prefix(lay.is_token_in_rank, w.channels)
+        xs, ids = u16(si.x), si.topk_idx.numpy()
+        secs, reps = _median_time(lambda: o.pack_bf16(xs, ids, None, E, pre, with_topk=False),
+                                     cpu_budget_s / 4)
+        cpu = cpu_entry(row_bytes("cached_dispatch", ts, H, K, E, N=pre.num_recv), secs, reps,
+                        f"oracle pack_bf16 on {ts} tokens of the same workload")
+    rows["cached_dispatch"] = entry(w, "cached_dispatch", ms, nbytes,
+                                    {"recv_rows": N, "dtype": "bf16"}, cpu)
+    for s in sets:
+        C.moedx_handle_destroy(s["h"])
+    del sets, buf
+
+    # -- standalone get_dispatch_layout on the prefill workload -------------------
+    w = wl.PREFILL
+    log_fn(f"[bench] row get_layout: {w.name}")
+    inp = wl.make_inputs(w)
+    T, H, K, E, R = w.tokens, w.hidden, w.topk, w.experts, w.ranks
+    buf = Buffer(E, R, num_channels=w.channels, max_tokens=T)
+    lsets = []
+    for _ in range(NSETS):
+        lsets.append({"idx": inp.topk_idx.to(dev),
+                      "ntpr": torch.empty(R, dtype=torch.int32, device=dev),
+                      "ntpe": torch.empty(E, dtype=torch.int32, device=dev),
+                      "itir": torch.empty(T, R, dtype=torch.uint8, device=dev)})
+
+    def get_layout(s):
+        return lambda: C.check(C.moedx_get_dispatch_layout(
+            buf.ctx, P(s["idx"]), T, K, P(s["ntpr"]), P(s["ntpe"]), P(s["itir"]), exr))
+
+    ms = timed([get_layout(s) for s in lsets])
+    cpu = None
+    if o is not None:
+        ids = inp.topk_idx.numpy()
+        secs, reps = _median_time(lambda: o.layout(ids, E, R), cpu_budget_s / 8, max_reps=20)
+        cpu = cpu_entry(row_bytes("get_layout", T, H, K, E, R=R), secs, reps,
+                        f"oracle layout on the full {T}-token workload")
+    rows["get_layout"] = entry(w, "get_layout", ms, row_bytes("get_layout", T, H, K, E, R=R),
+                               {"bound_note": "latency (under 0.3 MB)"}, cpu)
+    del lsets, buf
+
+    # -- low-latency dispatch and combine on the 128-token decode workload -------
+    w = wl.LL_DECODE
+    log_fn(f"[bench] rows ll_dispatch / ll_combine: {w.name}")
+    inp = wl.make_inputs(w)
+    T, H, K, E, cap = w.tokens, w.hidden, w.topk, w.experts, w.ll_capacity
+    buf = Buffer(E, w.ranks, num_channels=1, max_tokens=T)
+    nb = ctypes.c_size_t()
+    C.check(C.moedx_ll_workspace_bytes(buf.ctx, T, K, cap, ctypes.byref(nb)))
+    ids = inp.topk_idx.to(dev)
+    wts = inp.topk_weights.to(dev)
+    llsets = []
+    for _ in range(NSETS):
+        llsets.append({"x": inp.x.to(dev), "ws": torch.empty(nb.value, dtype=torch.uint8, device=dev),
+                       "recv": torch.empty(E, cap, H, dtype=torch.bfloat16, device=dev),
+                       "cnt": torch.empty(E, dtype=torch.int32, device=dev),
+                       "out": torch.empty(T, H, dtype=torch.bfloat16, device=dev), "h": None})
+
+    def ll_dispatch(s):
+        def f():
+            h = ctypes.c_void_p()
+            C.check(C.moedx_ll_dispatch(buf.ctx, P(s["x"]), P(ids), T, K, H, cap, P(s["recv"]),
+                                        P(s["cnt"]), P(s["ws"]), nb.value, ctypes.byref(h), exr))
+            if s["h"] is not None:
+                C.moedx_handle_destroy(s["h"])
+            s["h"] = h
+        return f
+
+    def ll_combine(s):
+        return lambda: C.check(C.moedx_ll_combine(buf.ctx, P(s["recv"]), P(ids), P(wts), s["h"], H,
+                                                  P(s["out"]), exr))
+
+    ms_d = timed([ll_dispatch(s) for s in llsets])
+    ms_c = timed([ll_combine(s) for s in llsets])
+    V = int((inp.topk_idx >= 0).sum())
+    cpu_d = cpu_c = None
+    if o is not None:
+        xs, idn, wn = u16(inp.x), inp.topk_idx.numpy(), inp.topk_weights.numpy()
+        res = {}
+
+        def run_d():
+            res["d"] = o.ll_dispatch(xs, idn, E, cap)
+
+        secs, reps = _median_time(run_d, cpu_budget_s / 8)
+        cpu_d = cpu_entry(row_bytes("ll_dispatch", T, H, K, E, V=V), secs, reps,
+                          f"oracle ll_dispatch on the full {T}-token workload")
+        recv_o, _, _, slot_o = res["d"]
+        secs, reps = _median_time(lambda: o.ll_combine(recv_o, idn, wn, slot_o), cpu_budget_s / 8)
+        cpu_c = cpu_entry(row_bytes("ll_combine", T, H, K, E, V=V), secs, reps,
+                          f"oracle ll_combine on the full {T}-token workload")
+    note = {"bound_note": "latency: a few MB per launch", "slots_filled": V}
+    rows["ll_dispatch"] = entry(w, "ll_dispatch", ms_d, row_bytes("ll_dispatch", T, H, K, E, V=V),
+                                note, cpu_d)
+    rows["ll_combine"] = entry(w, "ll_combine", ms_c, row_bytes("ll_combine", T, H, K, E, V=V),
+                               note, cpu_c)
+    for s in llsets:
+        if s["h"] is not None:
+            C.moedx_handle_destroy(s["h"])
+    del llsets, buf
+    torch.cuda.synchronize()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +391,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget-s", type=float, default=10.0,
                     help="seconds of CPU time for the oracle baseline (0 skips it)")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the further steps (FP8 pack, cached dispatch, standalone "
+                         "layout, low-latency pair) on their own workloads")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the exchange (logical ranks are buckets "
@@ -281,6 +565,10 @@ def main():
                "sample": f"median of {reps} full {T}x{H} steps (layout+prefix+pack+weighted "
                          f"combine), single-threaded C oracle"}
 
+    rows = None
+    if not args.no_rows:
+        rows = measure_rows(args.steps, args.warmup, args.cpu_budget_s, flush, log)
+
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -314,6 +602,7 @@ def main():
         "algorithmic_bytes": bytes_,
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,
+        "rows": rows,
     }
     print(json.dumps(result), flush=True)
 

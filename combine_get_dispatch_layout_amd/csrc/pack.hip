@@ -21,7 +21,7 @@
 #include "rows.h"
 
 #ifndef MOEDX_PACK_SPLIT
-#define MOEDX_PACK_SPLIT 4  // waves per token row
+#define MOEDX_PACK_SPLIT 8  // waves per token row
 #endif
 #ifndef MOEDX_PACK_NT_LOAD
 #define MOEDX_PACK_NT_LOAD 0  // streaming (non-temporal) loads of x
@@ -134,24 +134,44 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Nearest OCP E4M3FN code, ties to even, saturating at +/-448 (code 0x7E);
 // NaN -> 0x7F.  Normal range (|q| >= 2^-6): round the fp32 mantissa to 3 bits
 // with the round-half-even bias and re-bias the exponent from 127 to 7;
-// subnormal range: the code is round-half-even(|q| * 2^9) directly.
+// subnormal range: the code is round-half-even(|q| * 2^9).  Branch-free: both
+// ranges are computed and one is selected.
 __device__ __forceinline__ uint32_t e4m3_code(float q) {
     const uint32_t u = __float_as_uint(q);
-    const uint32_t sign = (u >> 24) & 0x80u;
     const uint32_t mag = u & 0x7fffffffu;
-    if (mag > 0x7f800000u) return 0x7fu;
-    uint32_t code;
-    if (mag >= 0x3c800000u) {  // 2^-6
-        const uint32_t r = (mag + 0x7ffffu + ((mag >> 20) & 1u)) >> 20;
-        const int c = (int)r - (120 << 3);
-        code = c > 0x7e ? 0x7eu : (uint32_t)c;
-    } else {
-        code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
-    }
-    return sign | code;
+    const uint32_t rn = (mag + 0x7ffffu + ((mag >> 20) & 1u)) >> 20;
+    const uint32_t cn = min(rn - (120u << 3), 0x7eu);  // unused (wrapped) below 2^-6
+    const uint32_t cs = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
+    const uint32_t c = (mag >= 0x3c800000u ? cn : cs) | ((u >> 24) & 0x80u);
+    return mag > 0x7f800000u ? 0x7fu : c;
 }
 
-// One 16-byte chunk = 8 bf16 values; 16 consecutive lanes form one 1x128 block.
+// Maximum over the 16 lanes of a DPP row (the lanes of one 1x128 block), by
+// lane permutations within the row: swap neighbours, swap pairs, mirror each
+// half, mirror the row.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+    return v;
+}
+
+// Correctly rounded a / s from rs = 1/s (itself correctly rounded): the
+// product's error is removed with one exact residual, r = a - q0 * s by a fused
+// multiply-add, and q0 + r * rs rounds to the IEEE quotient.  This holds for
+// every fp32 divisor significand and every bf16 numerator significand (checked
+// exhaustively; scaling by powers of two is exact), which covers a block's
+// values over its scale away from overflow and underflow.
+__device__ __forceinline__ float quotient(float a, float s, float rs) {
+    const float q0 = a * rs;
+    const float r = __builtin_fmaf(-q0, s, a);
+    return __builtin_fmaf(r, rs, q0);
+}
+
+// One 16-byte chunk = 8 bf16 values; 16 consecutive lanes (one DPP row) form
+// one 1x128 block.  Codes are bit-identical to encoding the IEEE quotient
+// x / s with e4m3_code, the definition the scale and codes follow.
 template <int CPL>
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__ x, int T, int H8,
                                                        RowMap rm, HandleRows hr,
@@ -169,35 +189,84 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__
     const int c_end = (int)((int64_t)(part + 1) * G / kSplit) * 16;
 
     for (int base = c_begin; base < c_end; base += CPL * 64) {
+        u32x4 v[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = base + i * 64 + lane;
+            v[i] = c < c_end ? load_row(src + c) : u32x4{0u, 0u, 0u, 0u};
+        }
         u32x2 code[CPL];
         float scale[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const int c = base + i * 64 + lane;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (c < c_end) v = load_row(src + c);
-            float f[8];
+            // Block maximum of |x| on the bit patterns: for non-negative
+            // floats the integer order is the numeric order, and inf / NaN
+            // sort above every finite value.
+            uint32_t ab = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f[2 * j] = bf16_lo(v[j]);
-                f[2 * j + 1] = bf16_hi(v[j]);
+            for (int j = 0; j < 4; ++j)
+                ab = max(ab, max((v[i][j] << 16) & 0x7fffffffu, v[i][j] & 0x7fff0000u));
+            ab = row16_max(ab);
+            uint32_t w0, w1;
+            float s;
+            if (ab < 0x7f800000u) {
+                // Finite block: s = max(amax, 1e-4) / 448 and every q = x / s
+                // as correctly rounded quotients, then gfx950's fp32 -> E4M3FN
+                // pack conversion (round to nearest even).  That instruction
+                // gives e4m3_code's result on every |q| <= 448 * (1 + 2^-23)
+                // of either sign (checked exhaustively on the device), and
+                // |q| cannot exceed that bound here, so no saturation or NaN
+                // case reaches it.
+                constexpr float kFloorScale = 1e-4f / 448.0f;
+                constexpr float kR448 = 1.0f / 448.0f;
+                s = ab > __float_as_uint(1e-4f) ? quotient(__uint_as_float(ab), 448.0f, kR448)
+                                                 : kFloorScale;
+                const float rs = 1.0f / s;
+                float qs[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t fb = (j & 1) ? (v[i][j >> 1] & 0xffff0000u) : (v[i][j >> 1] << 16);
+                    const float q = quotient(fabsf(__uint_as_float(fb)), s, rs);
+                    qs[j] = __uint_as_float(__float_as_uint(q) | (fb & 0x80000000u));
+                }
+                w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qs[0], qs[1], 0, false);
+                w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qs[2], qs[3], (int)w0, true);
+                w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qs[4], qs[5], 0, false);
+                w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qs[6], qs[7], (int)w1, true);
+            } else {
+                // A block holding inf or NaN (all 16 lanes take this branch):
+                // amax ignores NaN, then IEEE quotients through the general
+                // encoder (saturation, NaN -> 0x7F).
+                float f[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    f[2 * j] = bf16_lo(v[i][j]);
+                    f[2 * j + 1] = bf16_hi(v[i][j]);
+                }
+                float amax = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+                amax = fmaxf(amax, __shfl_xor(amax, 8));
+                amax = fmaxf(amax, __shfl_xor(amax, 4));
+                amax = fmaxf(amax, __shfl_xor(amax, 2));
+                amax = fmaxf(amax, __shfl_xor(amax, 1));
+                s = fmaxf(amax, 1e-4f) / 448.0f;
+                uint32_t cj[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) cj[j] = e4m3_code(f[j] / s);
+                w0 = cj[0] | (cj[1] << 8) | (cj[2] << 16) | (cj[3] << 24);
+                w1 = cj[4] | (cj[5] << 8) | (cj[6] << 16) | (cj[7] << 24);
             }
-            float amax = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
-            // max over the 16 lanes of the block (all in the same 16-lane group)
-            amax = fmaxf(amax, __shfl_xor(amax, 8));
-            amax = fmaxf(amax, __shfl_xor(amax, 4));
-            amax = fmaxf(amax, __shfl_xor(amax, 2));
-            amax = fmaxf(amax, __shfl_xor(amax, 1));
-            const float s = fmaxf(amax, 1e-4f) / 448.0f;
             scale[i] = s;
-            uint32_t lo = 0, hi = 0;
+            code[i] = u32x2{w0, w1};
+        }
+        // Even lanes take their odd neighbour's 8 code bytes and store 16.
+        u32x4 code2[CPL];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) lo |= e4m3_code(f[j] / s) << (8 * j);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hi |= e4m3_code(f[4 + j] / s) << (8 * j);
-            code[i] = u32x2{lo, hi};
+        for (int i = 0; i < CPL; ++i) {
+            const uint32_t nx = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)code[i][0], 0xF5, 0xf, 0xf, false);
+            const uint32_t ny = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)code[i][1], 0xF5, 0xf, 0xf, false);
+            code2[i] = u32x4{code[i][0], code[i][1], nx, ny};
         }
         uint64_t m = d.dest;
         while (m) {
@@ -210,7 +279,7 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__
             for (int i = 0; i < CPL; ++i) {
                 const int c = base + i * 64 + lane;
                 if (c < c_end) {
-                    store_row(code[i], dst + c);
+                    if ((lane & 1) == 0) store_row(code2[i], reinterpret_cast<u32x4*>(dst + c));
                     if ((lane & 15) == 0) sdst[c >> 4] = scale[i];
                 }
             }

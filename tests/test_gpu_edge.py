@@ -117,3 +117,53 @@ def test_fp8_zero_blocks_and_negative_zero(oracle):
 
 def test_fp8_capacity(oracle):
     run_case(oracle, _rand(500, 64, 6, seed=8), 384, 64, 16, 5, fp8=True, capacity=True)
+
+
+def _blocks_enumerating(limit_bits: int, amax_bits: int, rng) -> np.ndarray:
+    """1x128 blocks that together hold every bf16 magnitude up to `limit_bits`
+    (random signs); each block also holds `amax_bits` once, so its maximum and
+    hence its scale are fixed."""
+    vals = np.arange(limit_bits + 1, dtype=np.uint16)
+    vals = vals | (rng.integers(0, 2, vals.size).astype(np.uint16) << 15)
+    nb = -(-vals.size // 127)
+    out = np.zeros((nb, 128), np.uint16)
+    flat = np.concatenate([vals, np.zeros(nb * 127 - vals.size, np.uint16)]).reshape(nb, 127)
+    for b in range(nb):
+        pos = int(rng.integers(0, 128))
+        out[b] = np.insert(flat[b], pos, np.uint16(amax_bits))
+    return out
+
+
+def test_fp8_every_bf16_magnitude(oracle):
+    """Quotients at scale exactly 1 (block maximum 448) cover every bf16
+    magnitude up to 448, every E4M3 midpoint among them; a block maximum of 3
+    gives a scale that is not a power of two."""
+    rng = np.random.default_rng(11)
+    H = 1024
+    blocks = np.concatenate([_blocks_enumerating(0x43E0, 0x43E0, rng),   # 448 -> s = 1
+                             _blocks_enumerating(0x4040, 0x4040, rng),   # 3.0 -> s = 3 / 448
+                             _blocks_enumerating(0x3C00, 0x3C00, rng),   # 2^-7: above the 1e-4 floor
+                             _blocks_enumerating(0x38D0, 0x38D0, rng)])  # below it: s = 1e-4 / 448
+    per_row = H // 128
+    T = -(-blocks.shape[0] // per_row)
+    pad = np.tile(blocks[:1], (T * per_row - blocks.shape[0], 1))
+    x = np.concatenate([blocks, pad]).reshape(T, H)
+    run_case(oracle, _rand(T, 16, 2, seed=12), H, 16, 4, 2, x_u16=x, fp8=True)
+
+
+def test_fp8_inf_and_nan_blocks(oracle):
+    """Blocks holding +inf, -inf or NaN: the scale becomes inf (or ignores the
+    NaN), and codes follow the IEEE quotients (NaN -> 0x7F)."""
+    T, H = 8, 512
+    rng = np.random.default_rng(13)
+    x = np.asarray(rng.integers(0, 1 << 16, (T, H)), np.uint16)
+    x[(x & 0x7F80) == 0x7F80] = 0x3F80
+    x[0, 5] = 0x7F80           # +inf
+    x[1, 130] = 0xFF80         # -inf
+    x[2, 300] = 0x7FC0         # NaN
+    x[3, 0:128] = 0x7FC1       # a block of NaN only
+    x[4, 256:384] = 0x8000     # -0.0 block next to
+    x[4, 300] = 0xFFC0         # a negative NaN
+    x[5, 400] = 0x7F80
+    x[5, 401] = 0xFF80         # inf and -inf: inf / inf is NaN
+    run_case(oracle, _rand(T, 16, 2, seed=14), H, 16, 4, 2, x_u16=x, fp8=True)
