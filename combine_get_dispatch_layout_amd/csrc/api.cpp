@@ -655,6 +655,8 @@ int moedx_ll_dispatch(moedx_ctx* ctx, const uint16_t* x, const int64_t* topk_idx
     if (cap < 1) return fail(MOEDX_EINVAL, "num_max_dispatch_tokens_per_rank < 1");
     if (T > cap)
         return fail(MOEDX_ECAPACITY, "T=%d exceeds num_max_dispatch_tokens_per_rank=%d", T, cap);
+    if ((int64_t)ctx->E * cap > INT32_MAX)
+        return fail(MOEDX_EINVAL, "num_experts * num_max_dispatch_tokens_per_rank exceeds 2^31 - 1");
     if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
     if (!recv_count || !workspace || (T > 0 && (!x || !topk_idx || !recv_x)))
         return fail(MOEDX_EINVAL, "NULL device pointer");

@@ -12,11 +12,24 @@
 // the dispatch is a single launch: each workgroup owns one token (or a slice
 // of its row) and finds the token's slot in every chosen expert by counting,
 // with wave ballots, the earlier tokens that chose the same expert.  That is
-// O(T*K) reads per workgroup, all from L2, and saves a separate count kernel.
+// O(T*K) reads per workgroup, all from L2, and saves a separate count kernel;
+// one extra workgroup of the same launch writes the per-expert counts.  The
+// row chunk is loaded before the counting so the two latencies overlap, and
+// the combine issues the loads of up to 8 slot rows before its first FMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "launch.h"
+
+#ifndef MOEDX_LL_TARGET_WG
+#define MOEDX_LL_TARGET_WG 512  // dispatch workgroups a small batch is spread over
+#endif
+#ifndef MOEDX_LL_COMBINE_TARGET_WG
+#define MOEDX_LL_COMBINE_TARGET_WG 1024  // combine workgroups
+#endif
+#ifndef MOEDX_LL_MIN_CHUNKS
+#define MOEDX_LL_MIN_CHUNKS 64  // fewest 16-byte chunks of a row per workgroup
+#endif
 
 namespace moedx {
 
@@ -36,83 +49,22 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// grid = T * slices; workgroup b handles token b / slices, row slice b % slices.
+constexpr int kCountBatch = 4;  // earlier entries each thread loads per pass
+constexpr int kVisitBatch = 8;  // slot rows whose loads one combine pass issues together
+
+// grid = T * slices (+1): workgroup b < T * slices handles token b / slices,
+// row slice b % slices; the extra last workgroup writes every expert's count.
 __global__ __launch_bounds__(kThreads) void ll_dispatch_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx, int T, int K, int H8,
     int E, int cap, int slices, u32x4* __restrict__ recv_x, int32_t* __restrict__ recv_count,
     int32_t* __restrict__ src_idx, int32_t* __restrict__ slot_of) {
     __shared__ int32_t wave_cnt[kWaves][kMaxTopk];
-    __shared__ int32_t s_slot[kMaxTopk];
-    __shared__ int32_t s_expert[kMaxTopk];
     __shared__ int32_t hist[kMaxExperts];
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
-    const int t = blockIdx.x / slices;
-    const int slice = blockIdx.x - t * slices;
+    const int lane = tid & 63;
 
-    // This token's experts (uniform; invalid ids become -1).
-    int64_t ek[kMaxTopk];
-#pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) {
-        int64_t e = (k < K) ? topk_idx[(int64_t)t * K + k] : -1;
-        ek[k] = (e >= 0 && e < E) ? e : -1;
-    }
-    // Count earlier (token, slot) entries naming each of those experts.
-    int32_t cnt[kMaxTopk];
-#pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) cnt[k] = 0;
-    const int n_before = t * K;
-    for (int i0 = 0; i0 < n_before; i0 += kThreads) {
-        const int i = i0 + tid;
-        const int64_t v = (i < n_before) ? topk_idx[i] : -2;
-#pragma unroll
-        for (int k = 0; k < kMaxTopk; ++k) {
-            if (k < K) cnt[k] += __popcll(__ballot(v == ek[k] && ek[k] >= 0));
-        }
-    }
-    if ((tid & 63) == 0) {
-#pragma unroll
-        for (int k = 0; k < kMaxTopk; ++k)
-            if (k < K) wave_cnt[wave][k] = cnt[k];
-    }
-    __syncthreads();
-    if (tid < K) {
-        int32_t s = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) s += wave_cnt[w][tid];
-        s_slot[tid] = s;
-    }
-    if (tid == 0) {
-#pragma unroll
-        for (int k = 0; k < kMaxTopk; ++k)
-            if (k < K) s_expert[k] = (int32_t)ek[k];
-    }
-    __syncthreads();
-
-    if (slice == 0 && tid < K) {
-        const int e = s_expert[tid];
-        const int s = s_slot[tid];
-        const bool ok = e >= 0 && s < cap;
-        slot_of[(int64_t)t * K + tid] = ok ? s : -1;
-        if (ok) src_idx[(int64_t)e * cap + s] = t;
-    }
-
-    // Rows: this slice's chunk range of x[t] to every chosen expert's slot.
-    const int c0 = (int)((int64_t)H8 * slice / slices);
-    const int c1 = (int)((int64_t)H8 * (slice + 1) / slices);
-    const u32x4* src = x + (int64_t)t * H8;
-    for (int c = c0 + tid; c < c1; c += kThreads) {
-        const u32x4 v = __builtin_nontemporal_load(src + c);
-        for (int k = 0; k < K; ++k) {
-            const int e = s_expert[k];
-            const int s = s_slot[k];
-            if (e >= 0 && s < cap)
-                __builtin_nontemporal_store(v, recv_x + ((int64_t)e * cap + s) * H8 + c);
-        }
-    }
-
-    // The last token's first slice also writes every expert's count.
-    if (t == T - 1 && slice == 0) {
+    if ((int)blockIdx.x == T * slices) {  // counts: a histogram of every valid entry
         for (int e = tid; e < E; e += kThreads) hist[e] = 0;
         __syncthreads();
         for (int i = tid; i < T * K; i += kThreads) {
@@ -121,32 +73,134 @@ __global__ __launch_bounds__(kThreads) void ll_dispatch_kernel(
         }
         __syncthreads();
         for (int e = tid; e < E; e += kThreads) recv_count[e] = hist[e];
+        return;
+    }
+    const int t = blockIdx.x / slices;
+    const int slice = blockIdx.x - t * slices;
+    // This slice's chunk range of x[t]; the first chunk of each thread is
+    // loaded now, so that its latency overlaps the slot counting below.
+    const int c0 = (int)((int64_t)H8 * slice / slices);
+    const int c1 = (int)((int64_t)H8 * (slice + 1) / slices);
+    const u32x4* src = x + (int64_t)t * H8;
+    u32x4 first = {0u, 0u, 0u, 0u};
+    if (c0 + tid < c1) first = __builtin_nontemporal_load(src + c0 + tid);
+
+    // Lane k holds the token's k-th expert (-1 when empty or out of range).
+    int64_t ek = -1;
+    if (lane < K) {
+        const int64_t e = topk_idx[(int64_t)t * K + lane];
+        ek = (e >= 0 && e < E) ? e : -1;
+    }
+    // Slot of (t, k) = earlier (token, slot) entries naming the same expert:
+    // each pass loads kCountBatch entries per thread, then one ballot per
+    // (entry, k) counts the matches of 64 entries at once.
+    int32_t cnt[kMaxTopk];
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k) cnt[k] = 0;
+    const int n_before = t * K;
+    for (int i0 = 0; i0 < n_before; i0 += kThreads * kCountBatch) {
+        int64_t v[kCountBatch];
+#pragma unroll
+        for (int b = 0; b < kCountBatch; ++b) {
+            const int i = i0 + b * kThreads + tid;
+            v[b] = i < n_before ? topk_idx[i] : -2;
+        }
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k) {
+            if (k < K) {
+                const int64_t e = __builtin_amdgcn_readlane((int)ek, k);
+#pragma unroll
+                for (int b = 0; b < kCountBatch; ++b)
+                    cnt[k] += __popcll(__ballot(v[b] == e && e >= 0));
+            }
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k)
+            if (k < K) wave_cnt[wave][k] = cnt[k];
+    }
+    __syncthreads();
+    // lane k: the slot, or -1 when the entry is empty or past the capacity
+    int slot = -1;
+    if (lane < K) {
+        int32_t sum = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += wave_cnt[w][lane];
+        slot = (ek >= 0 && sum < cap) ? sum : -1;
+    }
+    if (slice == 0 && wave == 0 && lane < K) {
+        slot_of[(int64_t)t * K + lane] = slot;
+        if (slot >= 0) src_idx[ek * cap + slot] = t;
+    }
+    const uint64_t dests = __ballot(slot >= 0);
+    // slot row of lane k, as a row index of recv_x [E * cap, H]
+    const int row_l = slot >= 0 ? (int)ek * cap + slot : 0;
+
+    // Rows: this slice's chunk range of x[t] to every chosen expert's slot.
+    for (int c = c0 + tid; c < c1; c += kThreads) {
+        const u32x4 v = c == c0 + tid ? first : __builtin_nontemporal_load(src + c);
+        uint64_t m = dests;
+        while (m) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            const int64_t row = __builtin_amdgcn_readlane(row_l, k);
+            __builtin_nontemporal_store(v, recv_x + row * H8 + c);
+        }
     }
 }
 
-// grid = T * slices; each thread owns 16-byte chunks of one token's output.
+// grid = T * slices; each thread owns 16-byte chunks of one token's output and
+// sums the token's slot rows in k order (fp32 fused multiply-adds from +0.0).
 __global__ __launch_bounds__(kThreads) void ll_combine_kernel(
     const u32x4* __restrict__ y, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_weights, const int32_t* __restrict__ slot_of, int T, int K,
     int H8, int E, int cap, int slices, u32x4* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
     const int t = blockIdx.x / slices;
     const int slice = blockIdx.x - t * slices;
+    // lane k: row index of slot k in y [E * cap, H], its weight, whether valid
+    int row_l = 0;
+    float w_l = 0.0f;
+    bool ok = false;
+    if (lane < K) {
+        const int64_t e = topk_idx[(int64_t)t * K + lane];
+        const int s = slot_of[(int64_t)t * K + lane];
+        ok = e >= 0 && e < E && s >= 0 && s < cap;
+        row_l = ok ? (int)e * cap + s : 0;
+        w_l = topk_weights[(int64_t)t * K + lane];
+    }
+    const uint64_t valid = __ballot(ok);
     const int c0 = (int)((int64_t)H8 * slice / slices);
     const int c1 = (int)((int64_t)H8 * (slice + 1) / slices);
-    for (int c = c0 + threadIdx.x; c < c1; c += kThreads) {
+    for (int c = c0 + (int)threadIdx.x; c < c1; c += kThreads) {
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const int64_t e = topk_idx[(int64_t)t * K + k];
-            const int s = slot_of[(int64_t)t * K + k];
-            if (e < 0 || e >= E || s < 0 || s >= cap) continue;
-            const float w = topk_weights[(int64_t)t * K + k];
-            const u32x4 v = __builtin_nontemporal_load(y + (e * cap + s) * H8 + c);
+        for (int k0 = 0; k0 < K; k0 += kVisitBatch) {
+            // every load of the pass is issued before the first FMA; a slot
+            // that is empty (or past K) reads row 0 and adds nothing
+            u32x4 v[kVisitBatch];
+            float wt[kVisitBatch];
+            bool use[kVisitBatch];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[2 * j] = __builtin_fmaf(w, bf16_lo(v[j]), acc[2 * j]);
-                acc[2 * j + 1] = __builtin_fmaf(w, bf16_hi(v[j]), acc[2 * j + 1]);
+            for (int b = 0; b < kVisitBatch; ++b) {
+                const int k = min(k0 + b, K - 1);
+                use[b] = k0 + b < K && ((valid >> k) & 1);
+                const int64_t row = __builtin_amdgcn_readlane(row_l, k);
+                wt[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), k));
+                v[b] = __builtin_nontemporal_load(y + row * H8 + c);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < kVisitBatch; ++b) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float lo = __builtin_fmaf(wt[b], bf16_lo(v[b][j]), acc[2 * j]);
+                    const float hi = __builtin_fmaf(wt[b], bf16_hi(v[b][j]), acc[2 * j + 1]);
+                    acc[2 * j] = use[b] ? lo : acc[2 * j];
+                    acc[2 * j + 1] = use[b] ? hi : acc[2 * j + 1];
+                }
             }
         }
         u32x4 o;
@@ -163,9 +217,9 @@ __global__ __launch_bounds__(kThreads) void zero_i32_kernel(int32_t* __restrict_
 
 // Enough workgroups per token that a small decode batch still spreads over
 // the 256 compute units, and at least 64 chunks per workgroup.
-int ll_slices(int T, int H8) {
+int ll_slices(int T, int H8, int target_wg) {
     int s = 1;
-    while (s < 16 && (int64_t)T * s < 1024 && H8 / (s * 2) >= 64) s *= 2;
+    while (s < 16 && (int64_t)T * s < target_wg && H8 / (s * 2) >= MOEDX_LL_MIN_CHUNKS) s *= 2;
     return s;
 }
 
@@ -179,8 +233,8 @@ hipError_t launch_ll_dispatch(const void* x, const int64_t* topk_idx, int T, int
                              recv_count, E);
     }
     const int H8 = H / 8;
-    const int slices = ll_slices(T, H8);
-    return launch_kernel(ll_dispatch_kernel, dim3(T * slices), dim3(kThreads), L,
+    const int slices = ll_slices(T, H8, MOEDX_LL_TARGET_WG);
+    return launch_kernel(ll_dispatch_kernel, dim3(T * slices + 1), dim3(kThreads), L,
                          static_cast<const u32x4*>(x), topk_idx, T, K, H8, E, cap, slices,
                          static_cast<u32x4*>(recv_x), recv_count, src_idx, slot_of);
 }
@@ -189,7 +243,7 @@ hipError_t launch_ll_combine(const void* y, const int64_t* topk_idx, const float
                              const int32_t* slot_of, int T, int K, int H, int E, int cap, void* out,
                              const Launch& L) {
     const int H8 = H / 8;
-    const int slices = ll_slices(T, H8);
+    const int slices = ll_slices(T, H8, MOEDX_LL_COMBINE_TARGET_WG);
     return launch_kernel(ll_combine_kernel, dim3(T * slices), dim3(kThreads), L,
                          static_cast<const u32x4*>(y), topk_idx, topk_weights, slot_of, T, K, H8,
                          E, cap, slices, static_cast<u32x4*>(out));

@@ -276,7 +276,10 @@ MOEDX_API int moedx_ll_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  *   (bf16 [E, cap, H]; slots past the count untouched), and in the handle
  *   src_idx[e][s] = L_e[s] and slot_of[t][k] = position of t in L_{topk_idx[t,k]}
  *   (-1 for an empty slot).  Runs as a single kernel launch; there is no
- *   deferred receive hook (no network receive exists on one GPU). */
+ *   deferred receive hook (no network receive exists on one GPU).
+ * Errors: MOEDX_ECAPACITY when T > cap or the workspace is too small;
+ * MOEDX_EINVAL when E * cap exceeds 2^31 - 1 rows, H % 8 != 0, a pointer is
+ * NULL or misaligned (x, recv_x 16-byte; workspace 256-byte). */
 MOEDX_API int moedx_ll_dispatch(moedx_ctx *ctx, const uint16_t *x, const int64_t *topk_idx,
                                 int T, int K, int H, int num_max_dispatch_tokens_per_rank,
                                 uint16_t *recv_x, int32_t *recv_count, void *workspace,
