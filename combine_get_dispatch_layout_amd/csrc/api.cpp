@@ -29,6 +29,7 @@ struct moedx_event {
 struct moedx_ctx {
     int device;
     int E, R, P, C, max_tokens;
+    BucketDiv bucket;        // e / P as a multiply and shift on the device
     hipStream_t stream;      // the ctx's own stream (default priority)
     hipEvent_t order_event;  // orders the ctx stream after the caller's
     void* scratch;           // layout ticket + partial counts of the standalone layout
@@ -247,6 +248,11 @@ int moedx_create(moedx_ctx** out, int device, int num_experts, int num_ranks, in
     c->E = num_experts;
     c->R = num_ranks;
     c->P = num_experts / num_ranks;
+    c->bucket = bucket_div(num_experts, c->P);
+    if (c->bucket.mul == 0) {
+        delete c;
+        return fail(MOEDX_EINVAL, "no exact multiply-shift for num_experts / num_ranks");
+    }
     c->C = num_channels;
     c->max_tokens = max_tokens;
     const int nt = std::max(num_tiles(max_tokens), 1);
@@ -378,6 +384,7 @@ int moedx_get_dispatch_layout(moedx_ctx* ctx, const int64_t* topk_idx, int T, in
     a.E = ctx->E;
     a.R = ctx->R;
     a.P = ctx->P;
+    a.bucket = ctx->bucket;
     a.C = ctx->C;
     a.per = T > 0 ? (T + ctx->C - 1) / ctx->C : 1;
     a.is_token_in_rank = is_token_in_rank;
@@ -448,6 +455,7 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
         a.E = h->E;
         a.R = h->R;
         a.P = h->P;
+        a.bucket = ctx->bucket;
         a.C = h->C;
         a.per = T > 0 ? (T + h->C - 1) / h->C : 1;
         a.is_token_in_rank = h->is_token_in_rank;
@@ -589,7 +597,8 @@ int moedx_dispatch(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, 
         HIP_OR_FAIL(ex.no_kernel());
     } else if (quant == MOEDX_QUANT_NONE) {
         HIP_OR_FAIL(launch_pack_bf16(x, T, H, rm, hr, recv_x, topk_idx, topk_weights, h->K, h->E,
-                                     h->P, recv_topk_idx, recv_topk_weights, ex.launch()));
+                                     h->P, ctx->bucket, recv_topk_idx, recv_topk_weights,
+                                     ex.launch()));
         ctx->stats.pack_launches += 1;
     } else {
         HIP_OR_FAIL(launch_pack_fp8(x, T, H, rm, hr, recv_x, recv_scales, ex.launch()));

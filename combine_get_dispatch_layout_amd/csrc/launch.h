@@ -49,9 +49,22 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 
 // Everything the layout kernel reads and writes.  Pointers marked "handle" are
 // null for the standalone get_dispatch_layout.
+// Bucket of expert e, e / P, as (e * mul) >> shift: exact for every e in
+// [0, E) (the host picks mul and shift and checks each e), and a multiply and a
+// shift on the device instead of an integer division.
+struct BucketDiv {
+    uint32_t mul;
+    uint32_t shift;
+    __device__ __forceinline__ int of(int e) const { return (int)(((uint32_t)e * mul) >> shift); }
+};
+
+// mul == 0 when no such pair exists (not the case for E <= 1024).
+BucketDiv bucket_div(int E, int P);
+
 struct LayoutArgs {
     const int64_t* topk_idx;  // [T, K]
     int T, K, E, R, P, C, per;
+    BucketDiv bucket;
     uint8_t* is_token_in_rank;             // [T, R]
     uint64_t* token_mask;                  // [T] bucket bit mask (handle)
     int8_t* slot_bucket;                   // [T, K] bucket of each slot or -1 (handle)
@@ -92,7 +105,7 @@ struct HandleRows {
 
 hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
                             void* recv_x, const int64_t* topk_idx, const float* topk_weights,
-                            int K, int E, int P, int64_t* recv_topk_idx,
+                            int K, int E, int P, BucketDiv bucket, int64_t* recv_topk_idx,
                             float* recv_topk_weights, const Launch& L);
 
 hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
                 if (k >= K) break;
                 const int64_t e = ids[k];
                 if (e >= 0 && e < E) {  // ids outside [0, E) are treated as empty slots
-                    mask |= 1ull << ((int)e / a.P);
+                    mask |= 1ull << a.bucket.of((int)e);
                     atomicAdd(&hist[(int)e], 1);
                 }
             }
@@ -133,7 +133,8 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
             for (int k = 0; k < kMaxTopk; ++k) {
                 if (k >= K) break;
                 const int64_t e = ids[k];
-                a.slot_bucket[(int64_t)t * K + k] = (e >= 0 && e < E) ? (int8_t)((int)e / a.P) : -1;
+                a.slot_bucket[(int64_t)t * K + k] =
+                    (e >= 0 && e < E) ? (int8_t)a.bucket.of((int)e) : (int8_t)-1;
             }
         }
     }
@@ -260,6 +261,19 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
 
 
 }  // namespace
+
+BucketDiv bucket_div(int E, int P) {
+    // Smallest shift whose rounded-up reciprocal is exact on [0, E) and keeps
+    // e * mul inside 32 bits.
+    for (uint32_t shift = 0; shift < 32; ++shift) {
+        const uint64_t mul = (((uint64_t)1 << shift) + (uint64_t)P - 1) / (uint64_t)P;
+        if (mul * (uint64_t)E >= ((uint64_t)1 << 32)) break;
+        bool exact = true;
+        for (int e = 0; e < E && exact; ++e) exact = (int)(((uint64_t)e * mul) >> shift) == e / P;
+        if (exact) return BucketDiv{(uint32_t)mul, shift};
+    }
+    return BucketDiv{0u, 0u};  // not reached for E <= 1024
+}
 
 hipError_t launch_layout(const LayoutArgs& a, const Launch& L) {
     const int nt = num_tiles(a.T);

@@ -77,7 +77,7 @@ template <int CPL>
 __global__ __launch_bounds__(256) void pack_bf16_kernel(
     const u32x4* __restrict__ x, int T, int H8, RowMap rm, HandleRows hr,
     u32x4* __restrict__ recv_x, const int64_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_weights, int K, int E, int P,
+    const float* __restrict__ topk_weights, int K, int E, int P, BucketDiv bucket,
     int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_topk_weights) {
     const int lane = threadIdx.x & 63;
     int t, part;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(
     if (part == 0 && recv_topk_idx != nullptr && lane < K) {
         const int64_t e = topk_idx[(int64_t)t * K + lane];
         const float w = topk_weights ? topk_weights[(int64_t)t * K + lane] : 0.0f;
-        const int eb = (e >= 0 && e < E) ? (int)e / P : -1;
+        const int eb = (e >= 0 && e < E) ? bucket.of((int)e) : -1;
         uint64_t m = d.dest;
         while (m) {
             const int r = __builtin_ctzll(m);
@@ -306,7 +306,7 @@ int pack_blocks(int T) {
 
 hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
                             void* recv_x, const int64_t* topk_idx, const float* topk_weights,
-                            int K, int E, int P, int64_t* recv_topk_idx,
+                            int K, int E, int P, BucketDiv bucket, int64_t* recv_topk_idx,
                             float* recv_topk_weights, const Launch& L) {
     const int H8 = H / 8;
     const dim3 grid(pack_blocks(T)), block(256);
@@ -314,7 +314,7 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
     u32x4* rx = static_cast<u32x4*>(recv_x);
 #define MOEDX_PACK(N)                                                                         \
     return launch_kernel(pack_bf16_kernel<N>, grid, block, L, xs, T, H8, rm, hr, rx, topk_idx, \
-                         topk_weights, K, E, P, recv_topk_idx, recv_topk_weights)
+                         topk_weights, K, E, P, bucket, recv_topk_idx, recv_topk_weights)
     switch (pick_cpl((H8 + kSplit - 1) / kSplit)) {
         case 1: MOEDX_PACK(1);
         case 2: MOEDX_PACK(2);
