@@ -221,6 +221,15 @@ int check_tokens(const moedx_ctx* ctx, int T, int K) {
 
 }  // namespace
 
+// Every row kernel runs one wave per (token, slice of 64 or more chunks of 16
+// bytes); keep the wave count inside a 32-bit index.
+static int check_waves(int T, int H) {
+    const int64_t slices = (int64_t)(H / 8 + 63) / 64;
+    if ((int64_t)T * slices > ((int64_t)1 << 30))
+        return fail(MOEDX_EINVAL, "T=%d x H=%d exceeds the supported row count", T, H);
+    return MOEDX_OK;
+}
+
 extern "C" {
 
 const char* moedx_last_error(void) { return g_err; }
@@ -565,6 +574,7 @@ int moedx_dispatch(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, 
     if (h->E != ctx->E || h->R != ctx->R || h->C != ctx->C)
         return fail(MOEDX_ESTATE, "handle was prepared on a ctx with a different E/R/C");
     if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
+    if (int rc = check_waves(T, H)) return rc;
     if (quant != MOEDX_QUANT_NONE && quant != MOEDX_QUANT_FP8_E4M3_1X128)
         return fail(MOEDX_EINVAL, "unknown quant mode %d", quant);
     if (quant == MOEDX_QUANT_FP8_E4M3_1X128 && H % 128 != 0)
@@ -616,6 +626,7 @@ int moedx_combine(moedx_ctx* ctx, const moedx_handle* h, const uint16_t* y, int 
     if (h->E != ctx->E || h->R != ctx->R || h->C != ctx->C)
         return fail(MOEDX_ESTATE, "handle was prepared on a ctx with a different E/R/C");
     if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
+    if (int rc = check_waves(h->T, H)) return rc;
     // y may be NULL only when there is provably no receive row (exact mode, N = 0)
     const bool no_rows = h->capacity == 0 && h->n_host == 0;
     if (h->T > 0 && (!out || (!y && !no_rows))) return fail(MOEDX_EINVAL, "NULL device pointer");

@@ -43,10 +43,13 @@ constexpr int kWaves = kThreads / 64;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.  Both
+// results are computed and one is selected (no branch per value).
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
     const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x40u;
+    return (u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded;
 }
 
 constexpr int kCountBatch = 4;  // earlier entries each thread loads per pass

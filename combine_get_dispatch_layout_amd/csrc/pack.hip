@@ -20,8 +20,11 @@
 #include "launch.h"
 #include "rows.h"
 
-#ifndef MOEDX_PACK_SPLIT
-#define MOEDX_PACK_SPLIT 8  // waves per token row
+#ifndef MOEDX_PACK_WAVE_CHUNKS
+#define MOEDX_PACK_WAVE_CHUNKS 64  // 16-byte chunks of a bf16 row per wave (at most)
+#endif
+#ifndef MOEDX_PACK_FP8_WAVE_BLOCKS
+#define MOEDX_PACK_FP8_WAVE_BLOCKS 8  // 1x128 blocks of an FP8 row per wave (at most)
 #endif
 #ifndef MOEDX_PACK_NT_LOAD
 #define MOEDX_PACK_NT_LOAD 0  // streaming (non-temporal) loads of x
@@ -38,7 +41,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWavesPerBlock = 4;
-constexpr int kSplit = MOEDX_PACK_SPLIT;
+constexpr int kWaveChunks = MOEDX_PACK_WAVE_CHUNKS;
+constexpr int kWaveBlocks = MOEDX_PACK_FP8_WAVE_BLOCKS;
 
 template <typename V>
 __device__ __forceinline__ V load_row(const V* p) {
@@ -59,10 +63,10 @@ __device__ __forceinline__ void store_row(V v, V* p) {
 }
 
 // The wave's token and part of the row; t is wave-uniform.
-__device__ __forceinline__ void wave_work(int* t, int* part) {
+__device__ __forceinline__ void wave_work(int split, int* t, int* part) {
     const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-    *t = w / kSplit;
-    *part = w - *t * kSplit;
+    *t = w / split;
+    *part = w - *t * split;
 }
 
 __device__ __forceinline__ void write_handle_rows(const HandleRows& hr, const TokenRows& d, int t,
@@ -75,19 +79,19 @@ __device__ __forceinline__ void write_handle_rows(const HandleRows& hr, const To
 // CPL = 16-byte chunks each lane moves per pass over its part of the row.
 template <int CPL>
 __global__ __launch_bounds__(256) void pack_bf16_kernel(
-    const u32x4* __restrict__ x, int T, int H8, RowMap rm, HandleRows hr,
+    const u32x4* __restrict__ x, int T, int H8, int split, RowMap rm, HandleRows hr,
     u32x4* __restrict__ recv_x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_weights, int K, int E, int P, BucketDiv bucket,
     int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_topk_weights) {
     const int lane = threadIdx.x & 63;
     int t, part;
-    wave_work(&t, &part);
+    wave_work(split, &t, &part);
     if (t >= T) return;
     const TokenRows d = token_rows(rm, t, lane);
     if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     const u32x4* src = x + (int64_t)t * H8;
-    const int c_begin = (int)((int64_t)part * H8 / kSplit);
-    const int c_end = (int)((int64_t)(part + 1) * H8 / kSplit);
+    const int c_begin = (int)((int64_t)part * H8 / split);
+    const int c_end = (int)((int64_t)(part + 1) * H8 / split);
 
     for (int base = c_begin; base < c_end; base += CPL * 64) {
         u32x4 v[CPL];
@@ -174,19 +178,19 @@ __device__ __forceinline__ float quotient(float a, float s, float rs) {
 // x / s with e4m3_code, the definition the scale and codes follow.
 template <int CPL>
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__ x, int T, int H8,
-                                                       RowMap rm, HandleRows hr,
+                                                       int split, RowMap rm, HandleRows hr,
                                                        u32x2* __restrict__ recv_x8,
                                                        float* __restrict__ recv_scales) {
     const int lane = threadIdx.x & 63;
     int t, part;
-    wave_work(&t, &part);
+    wave_work(split, &t, &part);
     if (t >= T) return;
     const TokenRows d = token_rows(rm, t, lane);
     if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     const u32x4* src = x + (int64_t)t * H8;
     const int G = H8 >> 4;  // blocks per row; parts hold whole blocks
-    const int c_begin = (int)((int64_t)part * G / kSplit) * 16;
-    const int c_end = (int)((int64_t)(part + 1) * G / kSplit) * 16;
+    const int c_begin = (int)((int64_t)part * G / split) * 16;
+    const int c_end = (int)((int64_t)(part + 1) * G / split) * 16;
 
     for (int base = c_begin; base < c_end; base += CPL * 64) {
         u32x4 v[CPL];
@@ -298,8 +302,17 @@ int pick_cpl(int chunks) {
     return 16;
 }
 
-int pack_blocks(int T) {
-    return (int)(((int64_t)T * kSplit + kWavesPerBlock - 1) / kWavesPerBlock);
+// Waves per token row: enough that no wave moves more than kWaveChunks chunks
+// (kWaveBlocks whole 1x128 blocks for FP8), parts of near-equal size.  Short
+// parts keep many small waves in flight (measured best for bf16 rows); the
+// FP8 pack, which also computes, does best with 128 chunks per wave.
+int pack_split(int units, int units_per_wave) {
+    const int s = (units + units_per_wave - 1) / units_per_wave;
+    return s < 1 ? 1 : s;
+}
+
+int pack_blocks(int T, int split) {
+    return (int)(((int64_t)T * split + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
 }  // namespace
@@ -309,13 +322,14 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
                             int K, int E, int P, BucketDiv bucket, int64_t* recv_topk_idx,
                             float* recv_topk_weights, const Launch& L) {
     const int H8 = H / 8;
-    const dim3 grid(pack_blocks(T)), block(256);
+    const int split = pack_split(H8, kWaveChunks);
+    const dim3 grid(pack_blocks(T, split)), block(256);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x4* rx = static_cast<u32x4*>(recv_x);
 #define MOEDX_PACK(N)                                                                         \
-    return launch_kernel(pack_bf16_kernel<N>, grid, block, L, xs, T, H8, rm, hr, rx, topk_idx, \
+    return launch_kernel(pack_bf16_kernel<N>, grid, block, L, xs, T, H8, split, rm, hr, rx, topk_idx, \
                          topk_weights, K, E, P, bucket, recv_topk_idx, recv_topk_weights)
-    switch (pick_cpl((H8 + kSplit - 1) / kSplit)) {
+    switch (pick_cpl((H8 + split - 1) / split)) {
         case 1: MOEDX_PACK(1);
         case 2: MOEDX_PACK(2);
         case 4: MOEDX_PACK(4);
@@ -330,12 +344,13 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
 hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
                            void* recv_x8, float* recv_scales, const Launch& L) {
     const int H8 = H / 8;
-    const dim3 grid(pack_blocks(T)), block(256);
+    const int split = pack_split(H8 / 16, kWaveBlocks);
+    const dim3 grid(pack_blocks(T, split)), block(256);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x2* rx = static_cast<u32x2*>(recv_x8);
-    const int per_part = ((H8 / 16 + kSplit - 1) / kSplit) * 16;
+    const int per_part = ((H8 / 16 + split - 1) / split) * 16;
 #define MOEDX_PACK8(N) \
-    return launch_kernel(pack_fp8_kernel<N>, grid, block, L, xs, T, H8, rm, hr, rx, recv_scales)
+    return launch_kernel(pack_fp8_kernel<N>, grid, block, L, xs, T, H8, split, rm, hr, rx, recv_scales)
     switch (pick_cpl(per_part)) {
         case 1: MOEDX_PACK8(1);
         case 2: MOEDX_PACK8(2);
