@@ -643,8 +643,7 @@ int moedx_combine(moedx_ctx* ctx, const moedx_handle* h, const uint16_t* y, int 
         HIP_OR_FAIL(ex.no_kernel());
     } else {
         HIP_OR_FAIL(launch_combine(y, h->T, H, h->K, rm, h->slot_bucket, gate_weights,
-                                   recv_topk_weights, out, combined_topk_weights, h->send_head,
-                                   ex.launch()));
+                                   recv_topk_weights, out, combined_topk_weights, ex.launch()));
         ctx->stats.combine_launches += 1;
     }
     return exec_end(ex);

@@ -14,10 +14,12 @@
 // 16-byte chunks of its row); many small waves keep more gathers in flight than
 // a few long ones (measured: a wave per token slice sustains ~10% more read
 // bandwidth than a wave per token).  The wave locates the token's rows itself
-// (rows.h); lanes 0..K-1 hold the slots, and first occurrence and the
-// per-bucket weight come from lane reads, so every visited row, its weight and
-// its address are wave-uniform.  The visit order is fixed, so the result does
-// not depend on the launch shape.
+// (rows.h); lanes 0..K-1 hold the slots, and for each bucket of the token one
+// ballot names its slots: the first is the visit, and the bucket's weight is
+// the sum over them in ascending order, so every visited row, its weight and
+// its address are wave-uniform.  Up to 4 visits' loads are issued before the
+// first FMA.  The visit order is fixed, so the result does not depend on the
+// launch shape.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,9 +31,6 @@
 #endif
 #ifndef MOEDX_COMBINE_VISIT_BATCH
 #define MOEDX_COMBINE_VISIT_BATCH 4  // visited rows whose loads are issued together
-#endif
-#ifndef MOEDX_COMBINE_ROWS_FROM_SEND_HEAD
-#define MOEDX_COMBINE_ROWS_FROM_SEND_HEAD 0  // rows from send_head instead of the token masks
 #endif
 #ifndef MOEDX_COMBINE_NT_LOAD
 #define MOEDX_COMBINE_NT_LOAD 1
@@ -78,71 +77,87 @@ __device__ __forceinline__ void store_row(u32x4 v, u32x4* p) {
 #endif
 }
 
+// What locates one item's rows, loaded before they are needed: lane i holds
+// the token mask of token (group start + i); lane r < R the group prefix of
+// bucket r; lane k < K the bucket of slot k and its gate weight.
+struct ItemLoads {
+    uint64_t gm;
+    int pfx;
+    int rk;
+    float wk;
+};
+
+__device__ __forceinline__ ItemLoads item_loads(const RowMap& rm, const int8_t* slot_bucket,
+                                                const float* gate_weights, int K, int t,
+                                                int lane) {
+    ItemLoads a;
+    const int tj = (t & ~63) + lane;
+    a.gm = tj < rm.T ? rm.token_mask[tj] : 0ull;
+    a.pfx = lane < rm.R ? rm.group_prefix[(int64_t)(t >> 6) * rm.R + lane] : 0;
+    a.rk = lane < K ? (int)slot_bucket[(int64_t)t * K + lane] : -1;
+    a.wk = (lane < K && gate_weights) ? gate_weights[(int64_t)t * K + lane] : 0.0f;
+    return a;
+}
+
+// The token's visits: bucket r of the token is visited at its first slot k0
+// (the visit order is ascending k0); lane k0 holds the bucket's row and its
+// weight, the sum of the bucket's slot weights in ascending slot order from
+// +0.0 (1 without gate weights).  Rows follow rows.h; a row outside the
+// receive buffer (impossible for a consistent handle) is dropped.
+struct Visits {
+    uint64_t lanes;
+    int row;
+    float w;
+};
+
+__device__ __forceinline__ Visits item_visits(const ItemLoads& a, int base, int64_t rows, int t,
+                                              int lane, bool weighted) {
+    const int j = t & 63;
+    const uint64_t mine = readlane64(a.gm, j);
+    const uint64_t below = (j == 0) ? 0ull : (~0ull >> (64 - j));
+    Visits v{0ull, -1, 0.0f};
+    uint64_t m = mine;
+    while (m) {
+        const int r = __builtin_ctzll(m);
+        m &= m - 1;
+        const int pfx = __builtin_amdgcn_readlane(a.pfx, r);
+        const int b = __builtin_amdgcn_readlane(base, r);
+        const int64_t row = (int64_t)b + pfx + __popcll(__ballot((a.gm >> r) & 1u) & below);
+        const uint64_t slots = __ballot(a.rk == r);
+        if (slots == 0 || row < 0 || row >= rows) continue;
+        float w = 0.0f;
+        for (uint64_t s = slots; s; s &= s - 1)
+            w = w + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a.wk),
+                                                             __builtin_ctzll(s)));
+        const int k0 = __builtin_ctzll(slots);
+        v.lanes |= 1ull << k0;
+        if (lane == k0) {
+            v.row = (int)row;
+            v.w = weighted ? w : 1.0f;
+        }
+    }
+    return v;
+}
+
+// One wave per (token, slice of 64 * CPL chunks of its row).
 __global__ __launch_bounds__(256) void combine_kernel(
     const u32x4* __restrict__ y, int T, int H8, int K, RowMap rm,
     const int8_t* __restrict__ slot_bucket, const float* __restrict__ gate_weights,
     const float* __restrict__ recv_topk_weights, u32x4* __restrict__ out,
-    float* __restrict__ combined_topk_weights, int slices, const int32_t* __restrict__ send_head) {
+    float* __restrict__ combined_topk_weights, int slices) {
     constexpr int CPL = kCPL;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
     const int t = w / slices;
     const int part = w - t * slices;
     if (t >= T) return;
-#if MOEDX_COMBINE_ROWS_FROM_SEND_HEAD
-    TokenRows d;
-    {
-        int row = -1;
-        if (lane < rm.R) {
-            const int pos = send_head[(int64_t)t * rm.R + lane];
-            const int64_t r64 = pos >= 0 ? (int64_t)rm.rank_prefix_matrix[lane] -
-                                               rm.num_tokens_per_rank[lane] + pos
-                                         : -1;
-            row = r64 < rm.rows ? (int)r64 : -1;
-        }
-        d.row = row;
-        d.dest = __ballot(row >= 0);
-    }
-#else
-    const TokenRows d = token_rows(rm, t, lane);
-#endif
-
-    int rk = -1;
-    float wk = 0.0f;
-    if (lane < K) {
-        rk = slot_bucket[(int64_t)t * K + lane];
-        if (gate_weights) wk = gate_weights[(int64_t)t * K + lane];
-    }
-    // A slot is visited if it is the first slot of its bucket; its weight is the
-    // sum, in ascending slot order from +0.0, of the gate weights of its bucket.
-    bool first = rk >= 0;
-    float om = 0.0f;
-    for (int kk = 0; kk < K; ++kk) {
-        const int r2 = __builtin_amdgcn_readlane(rk, kk);
-        const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), kk));
-        if (r2 == rk) {
-            if (kk < lane) first = false;
-            om = om + w2;
-        }
-    }
-    if (!gate_weights) om = 1.0f;
-    // lane k (a visited slot) holds the row of its bucket
-    int vrow = -1;
-    {
-        uint64_t m = d.dest;
-        while (m) {
-            const int r = __builtin_ctzll(m);
-            m &= m - 1;
-            const int row_r = __builtin_amdgcn_readlane(d.row, r);
-            if (first && rk == r) vrow = row_r;
-        }
-    }
-    const uint64_t visits = __ballot(first && vrow >= 0);
+    const int base = lane < rm.R ? rm.rank_prefix_matrix[lane] - rm.num_tokens_per_rank[lane] : 0;
+    const ItemLoads ld = item_loads(rm, slot_bucket, gate_weights, K, t, lane);
+    const Visits vs = item_visits(ld, base, rm.rows, t, lane, gate_weights != nullptr);
 
     // This wave's chunks; lanes past the row end read a valid chunk and store nothing.
     const int c_begin = part * CPL * 64;
     const int c_end = min(c_begin + CPL * 64, H8);
-    u32x4* dst = out + (int64_t)t * H8;
     int cs[CPL];
     bool act[CPL];
 #pragma unroll
@@ -156,11 +171,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
-    uint64_t m = visits;
-    int k_last = visits ? __builtin_ctzll(visits) : 0;
+    uint64_t m = vs.lanes;
+    int k_last = m ? __builtin_ctzll(m) : 0;
     while (m) {
-        // kVB visited rows per batch: every load is issued before the first FMA
-        // (a batch past the last visit re-reads that visit's row and adds nothing).
+        // kVB visited rows per batch: every load is issued before the first
+        // FMA (a batch past the last visit re-reads that visit's row and
+        // adds nothing).
         const u32x4* src[kVB];
         float wt[kVB];
         bool use[kVB];
@@ -171,8 +187,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
                 k_last = __builtin_ctzll(m);
                 m &= m - 1;
             }
-            src[b] = y + (int64_t)__builtin_amdgcn_readlane(vrow, k_last) * H8;
-            wt[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(om), k_last));
+            src[b] = y + (int64_t)__builtin_amdgcn_readlane(vs.row, k_last) * H8;
+            wt[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vs.w), k_last));
         }
         u32x4 v[kVB][CPL];
 #pragma unroll
@@ -180,8 +196,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
             for (int i = 0; i < CPL; ++i) v[b][i] = load_row(src[b] + cs[i]);
         __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of its FMAs
-        // Branch-free: an unused slot of the batch computes and discards its FMA,
-        // so no control flow separates the loads from one another.
+        // Branch-free: an unused slot of the batch computes and discards its
+        // FMA, so no control flow separates the loads from one another.
 #pragma unroll
         for (int b = 0; b < kVB; ++b) {
 #pragma unroll
@@ -189,12 +205,14 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float lo = __builtin_fmaf(wt[b], bf16_lo(v[b][i][j]), acc[i][2 * j]);
-                    const float hi = __builtin_fmaf(wt[b], bf16_hi(v[b][i][j]), acc[i][2 * j + 1]);
+                    const float hi =
+                        __builtin_fmaf(wt[b], bf16_hi(v[b][i][j]), acc[i][2 * j + 1]);
                     acc[i][2 * j] = use[b] ? lo : acc[i][2 * j];
                     acc[i][2 * j + 1] = use[b] ? hi : acc[i][2 * j + 1];
                 }
         }
     }
+    u32x4* dst = out + (int64_t)t * H8;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         if (!act[i]) continue;
@@ -208,11 +226,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
     if (part == 0 && combined_topk_weights != nullptr && recv_topk_weights != nullptr &&
         lane < K) {
         float s = 0.0f;
-        uint64_t m = visits;
-        while (m) {
-            const int k = __builtin_ctzll(m);
-            m &= m - 1;
-            const int64_t r = __builtin_amdgcn_readlane(vrow, k);
+        for (uint64_t mm = vs.lanes; mm; mm &= mm - 1) {
+            const int64_t r = __builtin_amdgcn_readlane(vs.row, __builtin_ctzll(mm));
             s = s + recv_topk_weights[r * K + lane];
         }
         combined_topk_weights[(int64_t)t * K + lane] = s;
@@ -224,14 +239,15 @@ __global__ __launch_bounds__(256) void combine_kernel(
 hipError_t launch_combine(const void* y, int T, int H, int K, const RowMap& rm,
                           const int8_t* slot_bucket, const float* gate_weights,
                           const float* recv_topk_weights, void* out,
-                          float* combined_topk_weights, const int32_t* send_head,
-                          const Launch& L) {
+                          float* combined_topk_weights, const Launch& L) {
     const int H8 = H / 8;
     const int slices = (H8 + kCPL * 64 - 1) / (kCPL * 64);
-    const dim3 grid((int)(((int64_t)T * slices + kWavesPerBlock - 1) / kWavesPerBlock));
-    return launch_kernel(combine_kernel, grid, dim3(256), L, static_cast<const u32x4*>(y), T, H8, K,
-                         rm, slot_bucket, gate_weights, recv_topk_weights,
-                         static_cast<u32x4*>(out), combined_topk_weights, slices, send_head);
+    const int64_t blocks = ((int64_t)T * slices + kWavesPerBlock - 1) / kWavesPerBlock;
+    const u32x4* ys = static_cast<const u32x4*>(y);
+    u32x4* os = static_cast<u32x4*>(out);
+    return launch_kernel(combine_kernel, dim3((int)blocks), dim3(256), L, ys, T, H8, K, rm,
+                         slot_bucket, gate_weights, recv_topk_weights, os, combined_topk_weights,
+                         slices);
 }
 
 }  // namespace moedx

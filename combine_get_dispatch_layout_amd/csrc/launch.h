@@ -114,8 +114,7 @@ hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const 
 hipError_t launch_combine(const void* y, int T, int H, int K, const RowMap& rm,
                           const int8_t* slot_bucket, const float* gate_weights,
                           const float* recv_topk_weights, void* out,
-                          float* combined_topk_weights, const int32_t* send_head,
-                          const Launch& L);
+                          float* combined_topk_weights, const Launch& L);
 
 hipError_t launch_ll_dispatch(const void* x, const int64_t* topk_idx, int T, int K, int H, int E,
                               int cap, void* recv_x, int32_t* recv_count, int32_t* src_idx,

@@ -52,7 +52,7 @@ __device__ __forceinline__ TokenRows token_rows(const RowMap& rm, int t, int lan
     // A row past the receive buffer (impossible for a consistent handle) is
     // dropped rather than written: the kernels stay inside their buffers.
     const int64_t row64 = pos >= 0 ? (int64_t)base + pos : -1;
-    const int row = row64 < rm.rows ? (int)row64 : -1;
+    const int row = (row64 >= 0 && row64 < rm.rows) ? (int)row64 : -1;
     return TokenRows{row, pos, mine, __ballot(row >= 0)};
 }
 
