@@ -61,18 +61,23 @@ def algorithmic_bytes(T, H, K, E, R, C, N):
     return {"layout": layout, "pack": pack, "combine": combine}
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None once the kernel source differs from the one profiled."""
+TRAFFIC_SOURCES = {"layout": "layout.hip", "get_layout": "layout.hip", "pack": "pack.hip",
+                   "pack_fp8": "pack.hip", "cached_dispatch": "pack.hip",
+                   "combine": "combine.hip", "ll_dispatch": "ll.hip", "ll_combine": "ll.hip"}
+
+
+def measured_traffic(op):
+    """HBM bytes per launch of `op` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size), or
+    None once the kernel source differs from the one profiled."""
     import hashlib
 
-    src = {"pack": "pack.hip", "combine": "combine.hip"}[kernel]
-    path = os.path.join(ROOT, "combine_get_dispatch_layout_amd", "csrc", src)
+    path = os.path.join(ROOT, "combine_get_dispatch_layout_amd", "csrc", TRAFFIC_SOURCES[op])
     digest = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
-    summary = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_4096x7168.json")
+    summary = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(summary):
         return None
-    rec = json.load(open(summary)).get(kernel)
+    rec = json.load(open(summary)).get("ops", {}).get(op)
     if not rec or rec.get("source_sha256_16") != digest:
         return None
     return rec["traffic_bytes_per_launch"]
@@ -189,6 +194,7 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
         gbs = nbytes / (ms * 1e-3) / 1e9
         r = {"workload": w.name, "us": round(ms * 1e3, 2), "bytes": int(nbytes),
              "GBps": round(gbs, 1), "roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
+             "traffic": measured_traffic(kind),
              "tokens_per_s": round(w.tokens / (ms * 1e-3), 1)}
         r.update(extra)
         if cpu is not None:
