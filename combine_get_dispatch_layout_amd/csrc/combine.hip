@@ -45,7 +45,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWavesPerBlock = 4;
 constexpr int kCPL = MOEDX_COMBINE_CPL;
 constexpr int kVB = MOEDX_COMBINE_VISIT_BATCH;
 
@@ -147,7 +146,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     float* __restrict__ combined_topk_weights, int slices) {
     constexpr int CPL = kCPL;
     const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+    const int w = row_wave();
     const int t = w / slices;
     const int part = w - t * slices;
     if (t >= T) return;
@@ -242,7 +241,7 @@ hipError_t launch_combine(const void* y, int T, int H, int K, const RowMap& rm,
                           float* combined_topk_weights, const Launch& L) {
     const int H8 = H / 8;
     const int slices = (H8 + kCPL * 64 - 1) / (kCPL * 64);
-    const int64_t blocks = ((int64_t)T * slices + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t blocks = row_blocks(T, slices);
     const u32x4* ys = static_cast<const u32x4*>(y);
     u32x4* os = static_cast<u32x4*>(out);
     return launch_kernel(combine_kernel, dim3((int)blocks), dim3(256), L, ys, T, H8, K, rm,

@@ -12,7 +12,10 @@
 
 namespace moedx {
 
-constexpr int kTile = 256;         // tokens per workgroup of the layout kernel
+#ifndef MOEDX_LAYOUT_TILE
+#define MOEDX_LAYOUT_TILE 256
+#endif
+constexpr int kTile = MOEDX_LAYOUT_TILE;  // tokens per workgroup of the layout kernel
 constexpr int kGroup = 64;         // tokens per receive-position group (one wavefront)
 constexpr int kMaxRanks = 64;      // buckets fit one 64-bit mask
 constexpr int kMaxExperts = 1024;  // LDS histogram bound
@@ -20,6 +23,22 @@ constexpr int kMaxTopk = 16;
 
 __host__ __device__ inline int num_tiles(int T) { return (T + kTile - 1) / kTile; }
 __host__ __device__ inline int num_groups(int T) { return (T + kGroup - 1) / kGroup; }
+
+// ---- work order of the row kernels ------------------------------------------
+// The pack and combine kernels run one wave per (token, slice of its row), 4
+// waves per workgroup; wave index = token * waves_per_token + slice, in
+// workgroup order.  (Keeping each 64-token group on one XCD was measured
+// slower: it spreads the rows in flight over more of HBM.)
+constexpr int kRowWavesPerBlock = 4;
+
+inline int64_t row_blocks(int T, int waves_per_token) {
+    return ((int64_t)T * waves_per_token + kRowWavesPerBlock - 1) / kRowWavesPerBlock;
+}
+
+// This wave's index (wave-uniform).
+__device__ __forceinline__ int row_wave() {
+    return __builtin_amdgcn_readfirstlane(blockIdx.x * kRowWavesPerBlock + (threadIdx.x >> 6));
+}
 
 // Where a launch goes and, optionally, events stamped with the kernel's own
 // start and end (hipExtLaunchKernel), for kernel-accurate timing.

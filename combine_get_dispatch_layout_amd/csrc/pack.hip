@@ -40,7 +40,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWavesPerBlock = 4;
 constexpr int kWaveChunks = MOEDX_PACK_WAVE_CHUNKS;
 constexpr int kWaveBlocks = MOEDX_PACK_FP8_WAVE_BLOCKS;
 
@@ -64,7 +63,7 @@ __device__ __forceinline__ void store_row(V v, V* p) {
 
 // The wave's token and part of the row; t is wave-uniform.
 __device__ __forceinline__ void wave_work(int split, int* t, int* part) {
-    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+    const int w = row_wave();
     *t = w / split;
     *part = w - *t * split;
 }
@@ -311,9 +310,7 @@ int pack_split(int units, int units_per_wave) {
     return s < 1 ? 1 : s;
 }
 
-int pack_blocks(int T, int split) {
-    return (int)(((int64_t)T * split + kWavesPerBlock - 1) / kWavesPerBlock);
-}
+int pack_blocks(int T, int split) { return (int)row_blocks(T, split); }
 
 }  // namespace
 

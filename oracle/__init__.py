@@ -55,6 +55,11 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
         "oracle_pack_bf16": (None, [_P, _I64, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
         "oracle_quant_row_fp8": (None, [_P, _I64, _P, _P]),
         "oracle_pack_fp8": (None, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
+        "oracle_pow2_scale": (ctypes.c_float, [ctypes.c_float]),
+        "oracle_quant_row_fp8_mode": (None, [_P, _I64, _I32, ctypes.c_float, _P, _P, _P]),
+        "oracle_pack_fp8_mode": (None, [_P, _I64, _I64, _I32, _P, _P, _I32, ctypes.c_float, _P, _P,
+                                        _P]),
+        "oracle_pack_rows_bytes": (None, [_P, _I64, _I64, _I32, _P, _P, _P]),
         "oracle_combine": (None, [_P, _I64, _I64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
         "oracle_ll_dispatch": (_I32, [_P, _I64, _I64, _P, _I32, _I32, _I64, _P, _P, _P, _P]),
         "oracle_ll_combine": (None, [_P, _I64, _I64, _P, _P, _I64, _I32, _P, _P]),
@@ -193,6 +198,52 @@ class Oracle:
         self.lib.oracle_pack_fp8(_ptr(x), T, H, R, _ptr(pre.send_head),
                                  _ptr(pre.rank_prefix_matrix), _ptr(codes), _ptr(scales))
         return codes, scales
+
+    # FP8 scale modes (oracle_quant_row_fp8_mode): per-group amax / 448, the
+    # power-of-two scale, the same as UE8M0 exponent bytes, one tensor scale.
+    FP8_AMAX, FP8_POW2, FP8_UE8M0, FP8_TENSOR = 0, 1, 2, 3
+
+    def pow2_scale(self, ap: float) -> float:
+        return float(self.lib.oracle_pow2_scale(ap))
+
+    def quant_row_fp8_mode(self, xrow_u16: np.ndarray, mode: int, tensor_scale: float = 0.0):
+        """(codes [H] u8, scales [H/128]: fp32, u8 (UE8M0) or None (tensor))."""
+        x = _c(xrow_u16, np.uint16).reshape(-1)
+        H = x.size
+        G = H // 128
+        codes = np.empty(H, np.uint8)
+        sf = np.zeros(max(G, 1), np.float32)
+        su = np.zeros(max(G, 1), np.uint8)
+        self.lib.oracle_quant_row_fp8_mode(_ptr(x), H, mode, tensor_scale, _ptr(codes), _ptr(sf),
+                                           _ptr(su))
+        scales = {self.FP8_UE8M0: su[:G], self.FP8_TENSOR: None}.get(mode, sf[:G])
+        return codes, scales
+
+    def pack_fp8_mode(self, x_u16: np.ndarray, pre: Prefix, mode: int, tensor_scale: float = 0.0):
+        x = _c(x_u16, np.uint16)
+        T, H = x.shape
+        G = H // 128
+        R = pre.send_head.shape[1]
+        N = pre.num_recv
+        codes = np.zeros((N, H), np.uint8)
+        sf = np.zeros((N, G), np.float32) if mode in (self.FP8_AMAX, self.FP8_POW2) else None
+        su = np.zeros((N, G), np.uint8) if mode == self.FP8_UE8M0 else None
+        self.lib.oracle_pack_fp8_mode(_ptr(x), T, H, R, _ptr(pre.send_head),
+                                      _ptr(pre.rank_prefix_matrix), mode, tensor_scale,
+                                      _ptr(codes), _ptr(sf), _ptr(su))
+        return codes, (su if mode == self.FP8_UE8M0 else sf)
+
+    def pack_rows_bytes(self, src: np.ndarray, pre: Prefix) -> np.ndarray:
+        """Receive rows of a [T, W] byte array (pre-quantised codes or scales)."""
+        a = np.ascontiguousarray(src).view(np.uint8)
+        T = a.shape[0]
+        a = a.reshape(T, -1)
+        W = a.shape[1]
+        R = pre.send_head.shape[1]
+        out = np.zeros((pre.num_recv, W), np.uint8)
+        self.lib.oracle_pack_rows_bytes(_ptr(a), T, W, R, _ptr(pre.send_head),
+                                        _ptr(pre.rank_prefix_matrix), _ptr(out))
+        return out
 
     # -- combine ------------------------------------------------------------
     def combine(self, y_u16: np.ndarray, topk_idx, num_experts: int, pre: Prefix,

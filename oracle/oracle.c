@@ -243,8 +243,37 @@ void oracle_pack_bf16(const uint16_t *x, int64_t T, int64_t H,
  * per-group scales).  Groups are 1x128 blocks of a row.  For block j of token t:
  *   a = max |x| over the block, a' = max(a, 1e-4), s = a' / 448 (fp32 division)
  *   code = E4M3FN(x / s) (fp32 division, then nearest-even E4M3FN)
- * Every receive row of t gets the same codes; recv_scales[row, j] = s. */
-void oracle_quant_row_fp8(const uint16_t *xrow, int64_t H, uint8_t *codes, float *scales)
+ * Every receive row of t gets the same codes; recv_scales[row, j] = s.
+ *
+ * FP8 scale modes ([GCU] feature notes: FP8 dispatch supports round_scale,
+ * power-of-two scales, and use_ue8m0, the UE8M0 scale format; a single
+ * per-tensor scale can be given with fp8_quant_scale, exclusive with
+ * use_ue8m0).  With a' = max(amax, 1e-4) of the block:
+ *   ORACLE_FP8_AMAX   s = a' / 448 (fp32 division); scale stored as fp32
+ *   ORACLE_FP8_POW2   s = the smallest power of two with s >= a' / 448 (the
+ *                     real quotient); scale stored as fp32
+ *   ORACLE_FP8_UE8M0  s as POW2; stored as one byte, log2(s) + 127
+ *   ORACLE_FP8_TENSOR s = the caller's scale for every block; nothing stored
+ * and in every mode code = E4M3FN(x / s) with an fp32 division (exact for a
+ * power of two), saturating at +/-448.  A block whose a' is infinite has
+ * s = inf (UE8M0 byte 0xFF). */
+enum { ORACLE_FP8_AMAX = 0, ORACLE_FP8_POW2 = 1, ORACLE_FP8_UE8M0 = 2, ORACLE_FP8_TENSOR = 3 };
+
+/* a' / 448 = m * 2^e with m in [0.5, 1): the quotient is itself a power of two
+ * exactly when m == 0.5 (then s = 2^(e-1)), else s = 2^e.  The double quotient
+ * cannot round onto a power of two from elsewhere: a' has at most 24
+ * significant bits, so a' / 448 is a power of two only for a' = 7 * 2^k, and
+ * every other quotient lies far more than 2^-53 (relative) from one. */
+float oracle_pow2_scale(float ap)
+{
+    if (isinf(ap)) return INFINITY;
+    int e;
+    double m = frexp((double)ap / 448.0, &e);
+    return (float)ldexp(1.0, m == 0.5 ? e - 1 : e);
+}
+
+void oracle_quant_row_fp8_mode(const uint16_t *xrow, int64_t H, int mode, float tensor_scale,
+                               uint8_t *codes, float *scales_f32, uint8_t *scales_u8)
 {
     for (int64_t j = 0; j < H / 128; ++j) {
         float a = 0.0f;
@@ -253,34 +282,72 @@ void oracle_quant_row_fp8(const uint16_t *xrow, int64_t H, uint8_t *codes, float
             if (v > a) a = v;
         }
         float ap = a > 1e-4f ? a : 1e-4f;
-        float s = ap / 448.0f;
-        scales[j] = s;
-        for (int m = 0; m < 128; ++m) {
-            float q = oracle_bf16_to_f32(xrow[j * 128 + m]) / s;
-            codes[j * 128 + m] = oracle_e4m3_encode(q);
+        float s;
+        if (mode == ORACLE_FP8_AMAX) s = ap / 448.0f;  /* the default per-group scale */
+        else if (mode == ORACLE_FP8_TENSOR) s = tensor_scale;
+        else s = oracle_pow2_scale(ap);
+        for (int m = 0; m < 128; ++m)
+            codes[j * 128 + m] = oracle_e4m3_encode(oracle_bf16_to_f32(xrow[j * 128 + m]) / s);
+        if (mode == ORACLE_FP8_AMAX || mode == ORACLE_FP8_POW2) scales_f32[j] = s;
+        if (mode == ORACLE_FP8_UE8M0) scales_u8[j] = isinf(s) ? 0xFF : (uint8_t)(ilogbf(s) + 127);
+    }
+}
+
+void oracle_pack_fp8_mode(const uint16_t *x, int64_t T, int64_t H, int R,
+                          const int32_t *send_head, const int32_t *rank_prefix_matrix, int mode,
+                          float tensor_scale, uint8_t *recv_x8, float *recv_scales_f32,
+                          uint8_t *recv_scales_u8)
+{
+    int64_t G = H / 128;
+    uint8_t *codes = (uint8_t *)malloc((size_t)H);
+    float *sf = (float *)malloc((size_t)(G ? G : 1) * sizeof(float));
+    uint8_t *su = (uint8_t *)malloc((size_t)(G ? G : 1));
+    for (int64_t t = 0; t < T; ++t) {
+        oracle_quant_row_fp8_mode(x + t * H, H, mode, tensor_scale, codes, sf, su);
+        for (int r = 0; r < R; ++r) {
+            int32_t pos = send_head[t * R + r];
+            if (pos < 0) continue;
+            int64_t row = bucket_base(rank_prefix_matrix, r) + pos;
+            memcpy(recv_x8 + row * H, codes, (size_t)H);
+            if (mode == ORACLE_FP8_AMAX || mode == ORACLE_FP8_POW2)
+                memcpy(recv_scales_f32 + row * G, sf, (size_t)G * sizeof(float));
+            if (mode == ORACLE_FP8_UE8M0) memcpy(recv_scales_u8 + row * G, su, (size_t)G);
         }
     }
+    free(codes);
+    free(sf);
+    free(su);
+}
+
+/* Pre-quantised input passed through ([GCU]: the dispatch of an (x_fp8,
+ * scales) tuple): every W-byte row of src goes unchanged to the receive rows
+ * of its token, as the bf16 pack moves x. */
+void oracle_pack_rows_bytes(const uint8_t *src, int64_t T, int64_t W, int R,
+                            const int32_t *send_head, const int32_t *rank_prefix_matrix,
+                            uint8_t *dst)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int r = 0; r < R; ++r) {
+            int32_t pos = send_head[t * R + r];
+            if (pos < 0) continue;
+            int64_t row = bucket_base(rank_prefix_matrix, r) + pos;
+            memcpy(dst + row * W, src + t * W, (size_t)W);
+        }
+}
+
+/* The default FP8 dispatch (per-group fp32 scale s = a' / 448) as used by the
+ * plain FP8 pack. */
+void oracle_quant_row_fp8(const uint16_t *xrow, int64_t H, uint8_t *codes, float *scales)
+{
+    oracle_quant_row_fp8_mode(xrow, H, ORACLE_FP8_AMAX, 0.0f, codes, scales, NULL);
 }
 
 void oracle_pack_fp8(const uint16_t *x, int64_t T, int64_t H, int R,
                      const int32_t *send_head, const int32_t *rank_prefix_matrix,
                      uint8_t *recv_x8, float *recv_scales)
 {
-    int64_t G = H / 128;
-    uint8_t *codes = (uint8_t *)malloc((size_t)H);
-    float *scales = (float *)malloc((size_t)(G ? G : 1) * sizeof(float));
-    for (int64_t t = 0; t < T; ++t) {
-        oracle_quant_row_fp8(x + t * H, H, codes, scales);
-        for (int r = 0; r < R; ++r) {
-            int32_t pos = send_head[t * R + r];
-            if (pos < 0) continue;
-            int64_t row = bucket_base(rank_prefix_matrix, r) + pos;
-            memcpy(recv_x8 + row * H, codes, (size_t)H);
-            memcpy(recv_scales + row * G, scales, (size_t)G * sizeof(float));
-        }
-    }
-    free(codes);
-    free(scales);
+    oracle_pack_fp8_mode(x, T, H, R, send_head, rank_prefix_matrix, ORACLE_FP8_AMAX, 0.0f,
+                         recv_x8, recv_scales, NULL);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle as om
+from tests import test_oracle_fp8_modes as fm
 from tests import test_oracle_handworked as hw
 from tests import test_oracle_properties as pr
 
@@ -26,7 +27,14 @@ MUTANTS = {
     "local_expert_id": ("recv_topk_idx[row * K + k] = mine ? e - (int64_t)r * P : -1;",
                         "recv_topk_idx[row * K + k] = mine ? e - (int64_t)r : -1;"),
     "weight_not_zeroed": ("mine ? topk_weights[t * K + k] : 0.0f;", "topk_weights[t * K + k];"),
-    "fp8_fnuz_max": ("float s = ap / 448.0f;", "float s = ap / 240.0f;"),
+    "fp8_fnuz_max": ("if (mode == ORACLE_FP8_AMAX) s = ap / 448.0f;",
+                     "if (mode == ORACLE_FP8_AMAX) s = ap / 240.0f;"),
+    "pow2_floor": ("return (float)ldexp(1.0, m == 0.5 ? e - 1 : e);", "return (float)ldexp(1.0, e - 1);"),
+    "ue8m0_bias": ("(uint8_t)(ilogbf(s) + 127)", "(uint8_t)(ilogbf(s) + 126)"),
+    "tensor_scale_ignored": ("else if (mode == ORACLE_FP8_TENSOR) s = tensor_scale;",
+                             "else if (mode == ORACLE_FP8_TENSOR) s = 1.0f;"),
+    "passthrough_row": ("memcpy(dst + row * W, src + t * W, (size_t)W);",
+                        "memcpy(dst + row * W, src + (t > 0 ? t - 1 : 0) * W, (size_t)W);"),
     "fp8_tie_odd": ("else code = (uint8_t)((c & 1) ? c + 1 : c);", "else code = (uint8_t)((c & 1) ? c : c + 1);"),
     "fp8_no_floor": ("float ap = a > 1e-4f ? a : 1e-4f;", "float ap = a;"),
     "combine_no_dedup": ("if (seen) continue;", "(void)seen;"),
@@ -65,6 +73,11 @@ def battery(o: om.Oracle) -> None:
         pr.test_combine_identity_closed_forms(o, w)
     pr.test_ll_layout_properties.hypothesis.inner_test(o, 3, 40, 16, 4, 0.0)
     pr.test_ll_combine_unit_weights(o)
+    fm.test_pow2_scale_worked_values(o)
+    for mode in ("pow2", "ue8m0"):
+        fm.test_pow2_block_codes_and_scale(o, mode)
+    fm.test_tensor_scale_codes_and_saturation(o)
+    fm.test_pack_modes_and_rows_bytes_against_indexing(o, 1)
 
 
 @pytest.fixture(scope="module")
