@@ -62,7 +62,9 @@ def algorithmic_bytes(T, H, K, E, R, C, N):
 
 
 TRAFFIC_SOURCES = {"layout": "layout.hip", "get_layout": "layout.hip", "pack": "pack.hip",
-                   "pack_fp8": "pack.hip", "cached_dispatch": "pack.hip",
+                   "pack_fp8": "pack.hip", "pack_fp8_ue8m0": "pack.hip",
+                   "pack_fp8_tensor": "pack.hip", "pack_fp8_prequant": "pack.hip",
+                   "cached_dispatch": "pack.hip",
                    "combine": "combine.hip", "ll_dispatch": "ll.hip", "ll_combine": "ll.hip"}
 
 
@@ -112,7 +114,10 @@ def row_bytes(kind, T, H, K, E, N=0, V=0, R=0):
     """Algorithmic bytes of one launch of a further step of the path.
 
     pack_fp8       : read x (2TH); write N rows of codes (NH) and their 1x128
-                     scales (4N*H/128)
+                     scales (4N*H/128); with UE8M0 scales 1 byte each, with
+                     one per-tensor scale none
+    pack_fp8_prequant: read codes (TH) and fp32 scales (4T*H/128); write them
+                     to N rows
     cached_dispatch: read x (2TH); write N rows (2NH)
     get_layout     : read topk_idx (8TK); write is_token_in_rank (TR) and the
                      R + E counts
@@ -123,6 +128,9 @@ def row_bytes(kind, T, H, K, E, N=0, V=0, R=0):
     """
     return {
         "pack_fp8": 2 * T * H + N * H + 4 * N * (H // 128),
+        "pack_fp8_ue8m0": 2 * T * H + N * H + N * (H // 128),
+        "pack_fp8_tensor": 2 * T * H + N * H,
+        "pack_fp8_prequant": T * H + 4 * T * (H // 128) + N * H + 4 * N * (H // 128),
         "cached_dispatch": 2 * T * H + 2 * N * H,
         "get_layout": 8 * T * K + T * R + 4 * (R + E),
         "ll_dispatch": 2 * T * H + 8 * T * K + 2 * V * H + 4 * V + 4 * T * K + 4 * E,
@@ -264,9 +272,56 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
         cpu = cpu_entry(row_bytes("pack_fp8", ts, H, K, E, N=pre.num_recv), secs, reps,
                         f"oracle pack_fp8 on {ts} tokens of the same workload")
     rows["pack_fp8"] = entry(w, "pack_fp8", ms, nbytes, {"recv_rows": N, "dtype": "bf16->e4m3"}, cpu)
+
+    # the other scale modes and the pre-quantised pass-through, same workload
+    def fp8_opt(s, opts, x_ptr, scales_ptr):
+        return lambda: C.check(C.moedx_dispatch_fp8(buf.ctx, s["h"], x_ptr, T, H, ctypes.byref(opts),
+                                                    P(s["recv"]), scales_ptr, exr))
+
+    ue8m0 = C.moedx_fp8(C.MOEDX_FP8_SCALE_UE8M0, 0, 0.0, None)
+    tensor = C.moedx_fp8(C.MOEDX_FP8_SCALE_TENSOR, 0, 0.0123, None)
+    u8 = [torch.empty(T * min(K, w.ranks), H // 128, dtype=torch.uint8, device=dev) for _ in sets]
+    # pre-quantised input: the codes and scales of the first receive rows
+    pq = [(s["recv"][:T].contiguous(), s["scales"][:T].contiguous()) for s in sets]
+    pre_opts = [C.moedx_fp8(C.MOEDX_FP8_SCALE_AMAX, 1, 0.0, ctypes.c_void_p(q[1].data_ptr()))
+                for q in pq]
+    variants = (
+        ("pack_fp8_ue8m0", [fp8_opt(s, ue8m0, P(s["x"]), P(u)) for s, u in zip(sets, u8)],
+         o.FP8_UE8M0 if o else None),
+        ("pack_fp8_tensor", [fp8_opt(s, tensor, P(s["x"]), None) for s in sets],
+         o.FP8_TENSOR if o else None),
+        ("pack_fp8_prequant", [fp8_opt(s, op, P(q[0]), P(s["scales"]))
+                               for s, q, op in zip(sets, pq, pre_opts)], None),
+    )
+    for name, fns, omode in variants:
+        log_fn(f"[bench] row {name}: {w.name}")
+        ms = timed(fns)
+        cpu = None
+        if o is not None:
+            ts = 512
+            si = wl.make_inputs(w, tokens=ts)
+            lay = o.layout(si.topk_idx.numpy(), E, w.ranks)
+            pre = o.prefix(lay.is_token_in_rank, w.channels)
+            if omode is None:
+                codes8 = np.zeros((ts, H), np.uint8)
+                sc = np.zeros((ts, H // 128), np.float32)
+
+                def run():
+                    o.pack_rows_bytes(codes8, pre)
+                    o.pack_rows_bytes(sc, pre)
+            else:
+                xs = u16(si.x)
+
+                def run(xs=xs, omode=omode):
+                    o.pack_fp8_mode(xs, pre, omode, 0.0123)
+            secs, reps = _median_time(run, cpu_budget_s / 8)
+            cpu = cpu_entry(row_bytes(name, ts, H, K, E, N=pre.num_recv), secs, reps,
+                            f"oracle on {ts} tokens of the same workload")
+        rows[name] = entry(w, name, ms, row_bytes(name, T, H, K, E, N=N),
+                           {"recv_rows": N}, cpu)
     for s in sets:
         C.moedx_handle_destroy(s["h"])
-    del sets, buf
+    del sets, buf, u8, pq
 
     # -- cached dispatch (handle reuse) on the 16384-token workload --------------
     w = wl.HANDLE_REUSE

@@ -29,6 +29,11 @@ MOEDX_ASYNC = 2
 MOEDX_QUANT_NONE = 0
 MOEDX_QUANT_FP8_E4M3_1X128 = 1
 
+MOEDX_FP8_SCALE_AMAX = 0
+MOEDX_FP8_SCALE_POW2 = 1
+MOEDX_FP8_SCALE_UE8M0 = 2
+MOEDX_FP8_SCALE_TENSOR = 3
+
 # handle tensors
 MOEDX_T_RANK_PREFIX_MATRIX = 0
 MOEDX_T_CHANNEL_PREFIX_MATRIX = 1
@@ -53,6 +58,11 @@ class moedx_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "layout_launches", "pack_launches", "pack_fp8_launches",
         "combine_launches", "ll_dispatch_launches", "ll_combine_launches", "host_syncs")]
+
+
+class moedx_fp8(ctypes.Structure):
+    _fields_ = [("scale_mode", ctypes.c_int), ("prequantized", ctypes.c_int),
+                ("tensor_scale", ctypes.c_float), ("x_scales", ctypes.c_void_p)]
 
 
 class MoedxError(RuntimeError):
@@ -88,6 +98,7 @@ SIGNATURES = {
     "moedx_handle_tensor": (_I, [_P, _I, _PP, ctypes.POINTER(_I64)]),
     "moedx_handle_destroy": (_I, [_P]),
     "moedx_dispatch": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _EX]),
+    "moedx_dispatch_fp8": (_I, [_P, _P, _P, _I, _I, ctypes.POINTER(moedx_fp8), _P, _P, _EX]),
     "moedx_combine": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _EX]),
     "moedx_ll_workspace_bytes": (_I, [_P, _I, _I, _I, ctypes.POINTER(_SZ)]),
     "moedx_ll_dispatch": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _PP, _EX]),

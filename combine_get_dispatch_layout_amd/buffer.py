@@ -205,14 +205,30 @@ class Buffer:
                  topk_idx: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
                  previous_event: Optional[EventOverlap] = None, async_finish: bool = False,
                  allocate_on_comm_stream: bool = False, num_worst_tokens: int = 0,
-                 fp8: bool = False, out: Optional[torch.Tensor] = None,
+                 fp8: bool = False, round_scale: bool = False, use_ue8m0: bool = False,
+                 fp8_quant_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                  out_scales: Optional[torch.Tensor] = None, no_sync: bool = False):
         """Returns (recv_x, recv_topk_idx, recv_topk_weights,
         num_recv_tokens_per_expert_list, handle, event); recv_x is
-        (codes, scales) when fp8.  With ``handle`` (cached dispatch) topk_idx and
+        (codes, scales) for FP8 (scales None with a per-tensor scale).  ``x``
+        may be a pre-quantised (codes uint8 [T, H], scales) pair, dispatched
+        unchanged.  FP8 scales: per 1x128 block amax / 448 by default;
+        ``round_scale`` rounds them up to powers of two; ``use_ue8m0`` stores
+        them as UE8M0 exponent bytes (and implies ``round_scale``);
+        ``fp8_quant_scale`` is one scale for the whole tensor (exclusive with
+        ``use_ue8m0``).  With ``handle`` (cached dispatch) topk_idx and
         topk_weights must be None and only recv_x is produced.  The layout
         arguments are accepted for call-shape compatibility; the handle is
         computed from topk_idx on the device."""
+        prequant = isinstance(x, tuple)
+        x_scales = None
+        if prequant:
+            x, x_scales = x
+            x_scales = x_scales.contiguous() if x_scales is not None else None
+            fp8 = True
+        assert not (use_ue8m0 and fp8_quant_scale is not None), \
+            "fp8_quant_scale and use_ue8m0 are exclusive"
+        fp8 = fp8 or round_scale or use_ue8m0 or fp8_quant_scale is not None
         x = x.contiguous()
         T, H = x.shape
         first = handle is None
@@ -230,10 +246,15 @@ class Buffer:
         # At least one row is allocated so that an empty receive side still
         # passes a valid device pointer; the returned views have `rows` rows.
         alloc = max(rows, 1)
+        mode = (C.MOEDX_FP8_SCALE_TENSOR if fp8_quant_scale is not None else
+                C.MOEDX_FP8_SCALE_UE8M0 if use_ue8m0 else
+                C.MOEDX_FP8_SCALE_POW2 if round_scale else C.MOEDX_FP8_SCALE_AMAX)
         if fp8:
             recv_x = out if out is not None else torch.empty(alloc, H, dtype=torch.uint8, device=dev)
-            recv_s = out_scales if out_scales is not None else torch.empty(
-                alloc, H // 128, dtype=torch.float32, device=dev)
+            sdt = torch.uint8 if mode == C.MOEDX_FP8_SCALE_UE8M0 else torch.float32
+            recv_s = None if mode == C.MOEDX_FP8_SCALE_TENSOR else (
+                out_scales if out_scales is not None else
+                torch.empty(alloc, H // 128, dtype=sdt, device=dev))
         else:
             recv_x = out if out is not None else torch.empty(alloc, H, dtype=torch.bfloat16, device=dev)
             recv_s = None
@@ -243,12 +264,20 @@ class Buffer:
             if topk_weights is not None:
                 rtw = torch.empty(alloc, K, dtype=torch.float32, device=dev)
         ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream, no_sync)
-        tw = topk_weights.contiguous() if topk_weights is not None else None
-        ti = topk_idx.contiguous() if (first and not fp8) else None
-        C.check(C.moedx_dispatch(self.ctx, handle.ptr, _ptr(x), T, H,
-                                 C.MOEDX_QUANT_FP8_E4M3_1X128 if fp8 else C.MOEDX_QUANT_NONE,
-                                 _ptr(ti), _ptr(tw if (first and not fp8) else None), _ptr(recv_x),
-                                 _ptr(recv_s), _ptr(rti), _ptr(rtw), ctypes.byref(ex)))
+        if fp8 and (mode != C.MOEDX_FP8_SCALE_AMAX or prequant):
+            opts = C.moedx_fp8(mode, int(prequant),
+                               float(fp8_quant_scale) if fp8_quant_scale is not None else 0.0,
+                               _ptr(x_scales))
+            C.check(C.moedx_dispatch_fp8(self.ctx, handle.ptr, _ptr(x), T, H, ctypes.byref(opts),
+                                         _ptr(recv_x), _ptr(recv_s), ctypes.byref(ex)))
+        else:
+            tw = topk_weights.contiguous() if topk_weights is not None else None
+            ti = topk_idx.contiguous() if (first and not fp8) else None
+            C.check(C.moedx_dispatch(self.ctx, handle.ptr, _ptr(x), T, H,
+                                     C.MOEDX_QUANT_FP8_E4M3_1X128 if fp8 else C.MOEDX_QUANT_NONE,
+                                     _ptr(ti), _ptr(tw if (first and not fp8) else None),
+                                     _ptr(recv_x), _ptr(recv_s), _ptr(rti), _ptr(rtw),
+                                     ctypes.byref(ex)))
         per_expert = handle.recv_tokens_per_expert(self.num_experts) if (
             first and handle.capacity == 0) else None
         if out is None:

@@ -147,6 +147,7 @@ size_t carve_ll(moedx_handle* h, char* base, int T, int K, int E, int cap) {
 int64_t worst_rows(int T, int K, int R) { return (int64_t)T * std::min(K, R); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Stream choice and the previous_event wait; see moedx_exec.
 struct Exec {
@@ -611,7 +612,64 @@ int moedx_dispatch(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, 
                                      ex.launch()));
         ctx->stats.pack_launches += 1;
     } else {
-        HIP_OR_FAIL(launch_pack_fp8(x, T, H, rm, hr, recv_x, recv_scales, ex.launch()));
+        HIP_OR_FAIL(launch_pack_fp8(x, T, H, rm, hr, recv_x, recv_scales, MOEDX_FP8_SCALE_AMAX,
+                                    0.0f, ex.launch()));
+        ctx->stats.pack_fp8_launches += 1;
+    }
+    h->rows_written = true;
+    return exec_end(ex);
+}
+
+int moedx_dispatch_fp8(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, int H,
+                       const moedx_fp8* fp8, uint8_t* recv_x, void* recv_scales,
+                       const moedx_exec* exec) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!h || h->kind != kNormal) return fail(MOEDX_EINVAL, "a normal handle is required");
+    if (T != h->T) return fail(MOEDX_ESTATE, "T=%d differs from the handle's T=%d", T, h->T);
+    if (h->E != ctx->E || h->R != ctx->R || h->C != ctx->C)
+        return fail(MOEDX_ESTATE, "handle was prepared on a ctx with a different E/R/C");
+    if (!fp8) return fail(MOEDX_EINVAL, "fp8 options are NULL");
+    const int mode = fp8->scale_mode;
+    if (mode < MOEDX_FP8_SCALE_AMAX || mode > MOEDX_FP8_SCALE_TENSOR)
+        return fail(MOEDX_EINVAL, "unknown FP8 scale mode %d", mode);
+    if (H < 128 || H % 128 != 0)
+        return fail(MOEDX_EINVAL, "FP8 dispatch needs H %% 128 == 0 (H=%d)", H);
+    if (int rc = check_waves(T, H)) return rc;
+    const bool tensor = mode == MOEDX_FP8_SCALE_TENSOR;
+    if (tensor) {
+        const float s = fp8->tensor_scale;
+        // a positive normal scale whose reciprocal is normal too
+        if (!(s >= 0x1p-126f && s < 0x1p126f))
+            return fail(MOEDX_EINVAL, "tensor_scale=%g outside [2^-126, 2^126)", (double)s);
+    }
+    if (fp8->prequantized && !tensor && !fp8->x_scales)
+        return fail(MOEDX_EINVAL, "pre-quantised input needs x_scales");
+    if ((!fp8->prequantized || tensor) && fp8->x_scales)
+        return fail(MOEDX_EINVAL, "x_scales is read only for pre-quantised input with scales");
+    if (T > 0 && (!x || !recv_x)) return fail(MOEDX_EINVAL, "NULL device pointer");
+    if (T > 0 && (!aligned16(x) || !aligned16(recv_x)))
+        return fail(MOEDX_EINVAL, "x and recv_x must be 16-byte aligned");
+    if (T > 0 && !tensor && !recv_scales) return fail(MOEDX_EINVAL, "recv_scales is NULL");
+    if (tensor && recv_scales) return fail(MOEDX_EINVAL, "a per-tensor scale writes no recv_scales");
+    if ((T > 0 && !tensor && !aligned4(recv_scales)) ||
+        (fp8->x_scales && mode != MOEDX_FP8_SCALE_UE8M0 && !aligned4(fp8->x_scales)))
+        return fail(MOEDX_EINVAL, "fp32 scales must be 4-byte aligned");
+    Exec ex;
+    if (int rc = exec_begin(ctx, exec, &ex)) return rc;
+    const RowMap rm{h->token_mask, h->group_prefix, h->rank_prefix_matrix, h->num_tokens_per_rank,
+                    h->R, h->T, h->capacity > 0 ? h->capacity : h->n_host};
+    const HandleRows hr = h->rows_written ? HandleRows{nullptr, nullptr}
+                                          : HandleRows{h->send_head, h->recv_src_idx};
+    if (T == 0) {
+        HIP_OR_FAIL(ex.no_kernel());
+    } else if (fp8->prequantized) {
+        const int sb = tensor ? 0 : (H / 128) * (mode == MOEDX_FP8_SCALE_UE8M0 ? 1 : 4);
+        HIP_OR_FAIL(launch_pack_bytes(x, fp8->x_scales, T, H, sb, rm, hr, recv_x, recv_scales,
+                                      ex.launch()));
+        ctx->stats.pack_fp8_launches += 1;
+    } else {
+        HIP_OR_FAIL(launch_pack_fp8(x, T, H, rm, hr, recv_x, recv_scales, mode,
+                                    fp8->tensor_scale, ex.launch()));
         ctx->stats.pack_fp8_launches += 1;
     }
     h->rows_written = true;

@@ -127,8 +127,17 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
                             int K, int E, int P, BucketDiv bucket, int64_t* recv_topk_idx,
                             float* recv_topk_weights, const Launch& L);
 
+// mode: MOEDX_FP8_SCALE_* (AMAX 0, POW2 1, UE8M0 2, TENSOR 3); recv_scales fp32,
+// uint8 (UE8M0) or unused (TENSOR).
 hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
-                           void* recv_x8, float* recv_scales, const Launch& L);
+                           void* recv_x8, void* recv_scales, int mode, float tensor_scale,
+                           const Launch& L);
+
+// Pre-quantised rows: codes uint8 [T, H] and scale rows of scale_bytes bytes
+// (scales may be NULL when scale_bytes == 0).
+hipError_t launch_pack_bytes(const void* codes, const void* scales, int T, int H, int scale_bytes,
+                             const RowMap& rm, const HandleRows& hr, void* recv_codes,
+                             void* recv_scales, const Launch& L);
 
 hipError_t launch_combine(const void* y, int T, int H, int K, const RowMap& rm,
                           const int8_t* slot_bucket, const float* gate_weights,

@@ -172,14 +172,30 @@ __device__ __forceinline__ float quotient(float a, float s, float rs) {
     return __builtin_fmaf(r, rs, q0);
 }
 
+// Scale modes of the FP8 pack (the values of moedx.h's MOEDX_FP8_SCALE_*).
+enum Fp8Mode { kAmax = 0, kPow2 = 1, kUe8m0 = 2, kTensor = 3 };
+
+// The smallest power of two >= t, for a positive normal or infinite t (inf
+// stays inf).  For t = the correctly rounded a' / 448 this is also the smallest
+// power of two >= the real quotient: t is a power of two only when the real
+// quotient is one (a' has at most 24 significant bits, so a' / 448 is a power
+// of two only for a' = 7 * 2^k and lies far from one otherwise).
+__device__ __forceinline__ float pow2_ceil(float t) {
+    const uint32_t b = __float_as_uint(t);
+    return __uint_as_float((b & 0x7fffffu) ? (b & 0x7f800000u) + 0x800000u : b);
+}
+
 // One 16-byte chunk = 8 bf16 values; 16 consecutive lanes (one DPP row) form
 // one 1x128 block.  Codes are bit-identical to encoding the IEEE quotient
-// x / s with e4m3_code, the definition the scale and codes follow.
-template <int CPL>
+// x / s with e4m3_code, the definition the scale and codes follow; the scale
+// s of a block depends on kMode (moedx.h).  tensor_s / tensor_rs: the caller's
+// scale and its correctly rounded reciprocal (kTensor only).
+template <int CPL, int kMode>
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__ x, int T, int H8,
                                                        int split, RowMap rm, HandleRows hr,
                                                        u32x2* __restrict__ recv_x8,
-                                                       float* __restrict__ recv_scales) {
+                                                       void* __restrict__ recv_scales,
+                                                       float tensor_s, float tensor_rs) {
     const int lane = threadIdx.x & 63;
     int t, part;
     wave_work(split, &t, &part);
@@ -213,23 +229,48 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__
             uint32_t w0, w1;
             float s;
             if (ab < 0x7f800000u) {
-                // Finite block: s = max(amax, 1e-4) / 448 and every q = x / s
-                // as correctly rounded quotients, then gfx950's fp32 -> E4M3FN
-                // pack conversion (round to nearest even).  That instruction
-                // gives e4m3_code's result on every |q| <= 448 * (1 + 2^-23)
-                // of either sign (checked exhaustively on the device), and
-                // |q| cannot exceed that bound here, so no saturation or NaN
-                // case reaches it.
+                // Finite block: every q = x / s as a correctly rounded quotient
+                // (exact when s is a power of two), then gfx950's fp32 ->
+                // E4M3FN pack conversion (round to nearest even).  That
+                // instruction gives e4m3_code's result on every
+                // |q| <= 448 * (1 + 2^-23) of either sign (checked exhaustively
+                // on the device), and |q| never exceeds that bound here (the
+                // per-tensor scale clamps), so no saturation or NaN case
+                // reaches it.
                 constexpr float kFloorScale = 1e-4f / 448.0f;
                 constexpr float kR448 = 1.0f / 448.0f;
-                s = ab > __float_as_uint(1e-4f) ? quotient(__uint_as_float(ab), 448.0f, kR448)
-                                                 : kFloorScale;
-                const float rs = 1.0f / s;
+                float rs;
+                if (kMode == kTensor) {
+                    s = tensor_s;
+                    rs = tensor_rs;
+                } else {
+                    const float sa = ab > __float_as_uint(1e-4f)
+                                         ? quotient(__uint_as_float(ab), 448.0f, kR448)
+                                         : kFloorScale;
+                    if (kMode == kAmax) {
+                        s = sa;
+                        rs = 1.0f / s;
+                    } else {  // a power of two: its reciprocal flips the exponent
+                        s = pow2_ceil(sa);
+                        rs = __uint_as_float((254u << 23) - __float_as_uint(s));
+                    }
+                }
                 float qs[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const uint32_t fb = (j & 1) ? (v[i][j >> 1] & 0xffff0000u) : (v[i][j >> 1] << 16);
-                    const float q = quotient(fabsf(__uint_as_float(fb)), s, rs);
+                    const uint32_t fb =
+                        (j & 1) ? (v[i][j >> 1] & 0xffff0000u) : (v[i][j >> 1] << 16);
+                    const float a = fabsf(__uint_as_float(fb));
+                    float q;
+                    if (kMode == kPow2 || kMode == kUe8m0) {
+                        q = a * rs;  // exact
+                    } else if (kMode == kTensor) {
+                        // Past 2^30 the quotient saturates whatever its rounding.
+                        const float q0 = a * rs;
+                        q = fminf(q0 < 1073741824.0f ? quotient(a, s, rs) : 448.0f, 448.0f);
+                    } else {
+                        q = quotient(a, s, rs);
+                    }
                     qs[j] = __uint_as_float(__float_as_uint(q) | (fb & 0x80000000u));
                 }
                 w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qs[0], qs[1], 0, false);
@@ -253,7 +294,9 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__
                 amax = fmaxf(amax, __shfl_xor(amax, 4));
                 amax = fmaxf(amax, __shfl_xor(amax, 2));
                 amax = fmaxf(amax, __shfl_xor(amax, 1));
-                s = fmaxf(amax, 1e-4f) / 448.0f;
+                if (kMode == kTensor) s = tensor_s;
+                else s = fmaxf(amax, 1e-4f) / 448.0f;
+                if (kMode == kPow2 || kMode == kUe8m0) s = pow2_ceil(s);
                 uint32_t cj[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) cj[j] = e4m3_code(f[j] / s);
@@ -267,8 +310,10 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__
         u32x4 code2[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const uint32_t nx = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)code[i][0], 0xF5, 0xf, 0xf, false);
-            const uint32_t ny = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)code[i][1], 0xF5, 0xf, 0xf, false);
+            const uint32_t nx =
+                (uint32_t)__builtin_amdgcn_update_dpp(0, (int)code[i][0], 0xF5, 0xf, 0xf, false);
+            const uint32_t ny =
+                (uint32_t)__builtin_amdgcn_update_dpp(0, (int)code[i][1], 0xF5, 0xf, 0xf, false);
             code2[i] = u32x4{code[i][0], code[i][1], nx, ny};
         }
         uint64_t m = d.dest;
@@ -277,14 +322,71 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__
             m &= m - 1;
             const int64_t row = __builtin_amdgcn_readlane(d.row, r);
             u32x2* dst = recv_x8 + row * H8;
-            float* sdst = recv_scales + row * G;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = base + i * 64 + lane;
                 if (c < c_end) {
                     if ((lane & 1) == 0) store_row(code2[i], reinterpret_cast<u32x4*>(dst + c));
-                    if ((lane & 15) == 0) sdst[c >> 4] = scale[i];
+                    if ((lane & 15) == 0) {
+                        if (kMode == kAmax || kMode == kPow2)
+                            static_cast<float*>(recv_scales)[row * G + (c >> 4)] = scale[i];
+                        else if (kMode == kUe8m0)  // the exponent field of s (0xFF for inf)
+                            static_cast<uint8_t*>(recv_scales)[row * G + (c >> 4)] =
+                                (uint8_t)(__float_as_uint(scale[i]) >> 23);
+                    }
                 }
+            }
+        }
+    }
+}
+
+// Pre-quantised rows: code rows (C16 16-byte chunks) and scale rows (SB bytes)
+// of token t go unchanged to every receive row of t.  One wave per (token,
+// part of the code row); part 0 also moves the scale row.
+template <int CPL>
+__global__ __launch_bounds__(256) void pack_bytes_kernel(const u32x4* __restrict__ codes,
+                                                         const uint8_t* __restrict__ scales, int T,
+                                                         int C16, int SB, int split, RowMap rm,
+                                                         HandleRows hr, u32x4* __restrict__ recv,
+                                                         uint8_t* __restrict__ recv_scales) {
+    const int lane = threadIdx.x & 63;
+    int t, part;
+    wave_work(split, &t, &part);
+    if (t >= T) return;
+    const TokenRows d = token_rows(rm, t, lane);
+    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
+    const u32x4* src = codes + (int64_t)t * C16;
+    const int c_begin = (int)((int64_t)part * C16 / split);
+    const int c_end = (int)((int64_t)(part + 1) * C16 / split);
+    for (int base = c_begin; base < c_end; base += CPL * 64) {
+        u32x4 v[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = base + i * 64 + lane;
+            if (c < c_end) v[i] = load_row(src + c);
+        }
+        uint64_t m = d.dest;
+        while (m) {
+            const int r = __builtin_ctzll(m);
+            m &= m - 1;
+            const int64_t row = __builtin_amdgcn_readlane(d.row, r);
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = base + i * 64 + lane;
+                if (c < c_end) store_row(v[i], recv + row * C16 + c);
+            }
+        }
+    }
+    if (part == 0 && scales != nullptr) {
+        for (int b0 = 0; b0 < SB; b0 += 64) {
+            const int b = b0 + lane;
+            const uint8_t sv = b < SB ? scales[(int64_t)t * SB + b] : 0;
+            uint64_t m = d.dest;
+            while (m) {
+                const int r = __builtin_ctzll(m);
+                m &= m - 1;
+                const int64_t row = __builtin_amdgcn_readlane(d.row, r);
+                if (b < SB) recv_scales[row * SB + b] = sv;
             }
         }
     }
@@ -339,25 +441,45 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
 }
 
 hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
-                           void* recv_x8, float* recv_scales, const Launch& L) {
+                           void* recv_x8, void* recv_scales, int mode, float tensor_scale,
+                           const Launch& L) {
     const int H8 = H / 8;
     const int split = pack_split(H8 / 16, kWaveBlocks);
     const dim3 grid(pack_blocks(T, split)), block(256);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x2* rx = static_cast<u32x2*>(recv_x8);
-    const int per_part = ((H8 / 16 + split - 1) / split) * 16;
-#define MOEDX_PACK8(N) \
-    return launch_kernel(pack_fp8_kernel<N>, grid, block, L, xs, T, H8, split, rm, hr, rx, recv_scales)
-    switch (pick_cpl(per_part)) {
-        case 1: MOEDX_PACK8(1);
-        case 2: MOEDX_PACK8(2);
-        case 4: MOEDX_PACK8(4);
-        case 7: MOEDX_PACK8(7);
-        case 8: MOEDX_PACK8(8);
-        case 14: MOEDX_PACK8(14);
-        default: MOEDX_PACK8(16);
+    const int per_part = ((H8 / 16 + split - 1) / split) * 16;  // at most 16 * kWaveBlocks
+    const float trs = mode == kTensor ? 1.0f / tensor_scale : 0.0f;
+    const bool two = pick_cpl(per_part) > 1;
+#define MOEDX_PACK8(M)                                                                          \
+    return two ? launch_kernel(pack_fp8_kernel<2, M>, grid, block, L, xs, T, H8, split, rm, hr, \
+                               rx, recv_scales, tensor_scale, trs)                              \
+               : launch_kernel(pack_fp8_kernel<1, M>, grid, block, L, xs, T, H8, split, rm, hr, \
+                               rx, recv_scales, tensor_scale, trs)
+    switch (mode) {
+        case kAmax: MOEDX_PACK8(kAmax);
+        case kPow2: MOEDX_PACK8(kPow2);
+        case kUe8m0: MOEDX_PACK8(kUe8m0);
+        default: MOEDX_PACK8(kTensor);
     }
 #undef MOEDX_PACK8
+}
+
+hipError_t launch_pack_bytes(const void* codes, const void* scales, int T, int H, int scale_bytes,
+                             const RowMap& rm, const HandleRows& hr, void* recv_codes,
+                             void* recv_scales, const Launch& L) {
+    const int C16 = H / 16;
+    const int split = pack_split(C16, kWaveChunks);
+    const dim3 grid(pack_blocks(T, split)), block(256);
+    const u32x4* cs = static_cast<const u32x4*>(codes);
+    u32x4* rc = static_cast<u32x4*>(recv_codes);
+    const uint8_t* ss = static_cast<const uint8_t*>(scales);
+    uint8_t* rs = static_cast<uint8_t*>(recv_scales);
+    if (pick_cpl((C16 + split - 1) / split) > 1)
+        return launch_kernel(pack_bytes_kernel<2>, grid, block, L, cs, ss, T, C16, scale_bytes,
+                             split, rm, hr, rc, rs);
+    return launch_kernel(pack_bytes_kernel<1>, grid, block, L, cs, ss, T, C16, scale_bytes, split,
+                         rm, hr, rc, rs);
 }
 
 }  // namespace moedx

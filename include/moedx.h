@@ -248,6 +248,46 @@ MOEDX_API int moedx_dispatch(moedx_ctx *ctx, const moedx_handle *h, const void *
                              void *recv_x, float *recv_scales, int64_t *recv_topk_idx,
                              float *recv_topk_weights, const moedx_exec *exec);
 
+/* FP8 dispatch options ([GCU] feature notes: FP8 dispatch supports
+ * round_scale, power-of-two scales, and use_ue8m0, the UE8M0 scale format; a
+ * single per-tensor scale may be given with fp8_quant_scale, exclusive with
+ * use_ue8m0; FP8 dispatch of an already-quantised (codes, scales) input).
+ * For each 1x128 block with a' = max(amax, 1e-4):
+ *   MOEDX_FP8_SCALE_AMAX   s = a' / 448 (IEEE fp32); scales fp32
+ *   MOEDX_FP8_SCALE_POW2   s = the smallest power of two >= a' / 448; scales fp32
+ *   MOEDX_FP8_SCALE_UE8M0  s as POW2; scales uint8, log2(s) + 127 (0xFF: inf)
+ *   MOEDX_FP8_SCALE_TENSOR s = tensor_scale for every block; no scales written
+ * codes = E4M3FN(x / s) (IEEE fp32 quotient, nearest even, saturating at
+ * +/-448, NaN -> 0x7F).  A block holding inf has s = inf. */
+enum {
+    MOEDX_FP8_SCALE_AMAX = 0,
+    MOEDX_FP8_SCALE_POW2 = 1,
+    MOEDX_FP8_SCALE_UE8M0 = 2,
+    MOEDX_FP8_SCALE_TENSOR = 3
+};
+
+typedef struct moedx_fp8 {
+    int scale_mode;        /* MOEDX_FP8_SCALE_* */
+    int prequantized;      /* 1: x already holds E4M3FN codes uint8 [T, H] */
+    float tensor_scale;    /* MOEDX_FP8_SCALE_TENSOR: positive, in [2^-126, 2^126) */
+    const void *x_scales;  /* prequantized: the scales of x, in the scale_mode's format
+                              ([T, H/128] fp32 or uint8); NULL for TENSOR */
+} moedx_fp8;
+
+/* FP8 dispatch with options: recv_x uint8 [rows, H]; recv_scales [rows, H/128]
+ * in the scale_mode's format (NULL for MOEDX_FP8_SCALE_TENSOR).  Quantising:
+ * x is bf16 [T, H] and codes / scales follow the definition above.
+ * Pre-quantised (prequantized = 1): the code rows and scale rows of x are
+ * copied unchanged to every receive row of their token.  Handle rows, capacity
+ * mode and cached use behave as in moedx_dispatch; recv_topk_* are not
+ * produced.  H % 128 == 0.  Errors: MOEDX_EINVAL for an unknown mode, a
+ * tensor_scale out of range, x_scales missing or given where unused, NULL or
+ * misaligned buffers (x, recv_x 16-byte); MOEDX_ESTATE for a handle of another
+ * ctx or another T. */
+MOEDX_API int moedx_dispatch_fp8(moedx_ctx *ctx, const moedx_handle *h, const void *x, int T, int H,
+                                 const moedx_fp8 *fp8, uint8_t *recv_x, void *recv_scales,
+                                 const moedx_exec *exec);
+
 /* ---- combine ([GCU] combine_forward, dispatch_backward; [HR] Combining) --- */
 
 /* out[t] (bf16 [T, H]) = bf16_rne( sum over t's distinct buckets r, in
