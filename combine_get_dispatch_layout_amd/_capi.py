@@ -102,6 +102,7 @@ SIGNATURES = {
     "moedx_combine": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _EX]),
     "moedx_ll_workspace_bytes": (_I, [_P, _I, _I, _I, ctypes.POINTER(_SZ)]),
     "moedx_ll_dispatch": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _PP, _EX]),
+    "moedx_ll_dispatch_recv": (_I, [_P, _P, _P, _P, _I, _P, _EX]),
     "moedx_ll_combine": (_I, [_P, _P, _P, _P, _P, _I, _P, _EX]),
 }
 

@@ -315,10 +315,11 @@ class Buffer:
                              num_max_dispatch_tokens_per_rank: int, num_experts: int,
                              previous_event=None, async_finish: bool = False,
                              return_recv_hook: bool = False, no_sync: bool = False):
-        """Returns (recv_x [E, cap, H], recv_count [E] int32, handle, event, None).
-        There is no deferred receive: the hook slot is None."""
+        """Returns (recv_x [E, cap, H], recv_count [E] int32, handle, event, hook).
+        With return_recv_hook the call fills counts and the handle only, and
+        the rows arrive when hook() runs (a second kernel launch on the
+        current stream); otherwise hook is None."""
         assert num_experts == self.num_experts
-        assert not return_recv_hook, "no deferred receive phase exists on one GPU"
         x = x.contiguous()
         topk_idx = topk_idx.contiguous()
         T, H = x.shape
@@ -332,23 +333,41 @@ class Buffer:
         cnt = torch.empty(num_experts, dtype=torch.int32, device=dev)
         h = ctypes.c_void_p()
         ex, done = self._exec(previous_event, async_finish, False, no_sync)
-        C.check(C.moedx_ll_dispatch(self.ctx, _ptr(x), _ptr(topk_idx), T, K, H, cap, _ptr(recv_x),
-                                    _ptr(cnt), _ptr(ws), nbytes.value, ctypes.byref(h),
-                                    ctypes.byref(ex)))
-        return recv_x, cnt, Handle(h.value, ws, T, K, True), self._event(done), None
+        C.check(C.moedx_ll_dispatch(self.ctx, _ptr(x), _ptr(topk_idx), T, K, H, cap,
+                                    None if return_recv_hook else _ptr(recv_x), _ptr(cnt),
+                                    _ptr(ws), nbytes.value, ctypes.byref(h), ctypes.byref(ex)))
+        handle = Handle(h.value, ws, T, K, True)
+        hook = None
+        if return_recv_hook:
+            def hook():
+                rex = C.make_exec(_stream(), None, None, C.MOEDX_ASYNC)
+                C.check(C.moedx_ll_dispatch_recv(self.ctx, handle.ptr, _ptr(x), _ptr(topk_idx), H,
+                                                 _ptr(recv_x), ctypes.byref(rex)))
+        return recv_x, cnt, handle, self._event(done), hook
 
     def low_latency_combine(self, x: torch.Tensor, topk_idx: torch.Tensor,
                             topk_weights: torch.Tensor, handle: Handle, previous_event=None,
                             async_finish: bool = False, return_recv_hook: bool = False,
                             out: Optional[torch.Tensor] = None, no_sync: bool = False):
-        """Returns (combined [T, H] bf16, event, None)."""
-        assert not return_recv_hook, "no deferred receive phase exists on one GPU"
+        """Returns (combined [T, H] bf16, event, hook).  With return_recv_hook
+        the reduction runs when hook() is called (on the current stream) and
+        event is None; otherwise hook is None."""
         x = x.contiguous()
         H = x.shape[-1]
         T = handle.T
         combined = out if out is not None else torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+        ti, tw = topk_idx.contiguous(), topk_weights.contiguous()
+
+        def run(ex):
+            C.check(C.moedx_ll_combine(self.ctx, _ptr(x), _ptr(ti), _ptr(tw), handle.ptr, H,
+                                       _ptr(combined), ctypes.byref(ex)))
+
+        if return_recv_hook:
+            prev = previous_event.event if previous_event is not None else None
+
+            def hook():
+                run(C.make_exec(_stream(), prev, None, C.MOEDX_ASYNC))
+            return combined, EventOverlap(None), hook
         ex, done = self._exec(previous_event, async_finish, False, no_sync)
-        C.check(C.moedx_ll_combine(self.ctx, _ptr(x), _ptr(topk_idx.contiguous()),
-                                   _ptr(topk_weights.contiguous()), handle.ptr, H, _ptr(combined),
-                                   ctypes.byref(ex)))
+        run(ex)
         return combined, self._event(done), None

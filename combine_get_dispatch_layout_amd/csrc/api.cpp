@@ -735,9 +735,10 @@ int moedx_ll_dispatch(moedx_ctx* ctx, const uint16_t* x, const int64_t* topk_idx
     if ((int64_t)ctx->E * cap > INT32_MAX)
         return fail(MOEDX_EINVAL, "num_experts * num_max_dispatch_tokens_per_rank exceeds 2^31 - 1");
     if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
-    if (!recv_count || !workspace || (T > 0 && (!x || !topk_idx || !recv_x)))
+    // recv_x == NULL defers the rows to moedx_ll_dispatch_recv (x is then unused)
+    if (!recv_count || !workspace || (T > 0 && (!topk_idx || (recv_x && !x))))
         return fail(MOEDX_EINVAL, "NULL device pointer");
-    if (T > 0 && (!aligned16(x) || !aligned16(recv_x)))
+    if (T > 0 && recv_x && (!aligned16(x) || !aligned16(recv_x)))
         return fail(MOEDX_EINVAL, "x and recv_x must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(MOEDX_EINVAL, "workspace is not 256-byte aligned");
@@ -772,6 +773,28 @@ int moedx_ll_dispatch(moedx_ctx* ctx, const uint16_t* x, const int64_t* topk_idx
     }
     *out = h;
     return MOEDX_OK;
+}
+
+int moedx_ll_dispatch_recv(moedx_ctx* ctx, const moedx_handle* h, const uint16_t* x,
+                           const int64_t* topk_idx, int H, uint16_t* recv_x,
+                           const moedx_exec* exec) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!h || h->kind != kLowLatency) return fail(MOEDX_EINVAL, "a low-latency handle is required");
+    if (h->E != ctx->E) return fail(MOEDX_ESTATE, "handle was made on a ctx with a different E");
+    if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
+    if (h->T > 0 && (!x || !topk_idx || !recv_x)) return fail(MOEDX_EINVAL, "NULL device pointer");
+    if (h->T > 0 && (!aligned16(x) || !aligned16(recv_x)))
+        return fail(MOEDX_EINVAL, "x and recv_x must be 16-byte aligned");
+    Exec ex;
+    if (int rc = exec_begin(ctx, exec, &ex)) return rc;
+    if (h->T == 0) {
+        HIP_OR_FAIL(ex.no_kernel());
+    } else {
+        HIP_OR_FAIL(launch_ll_recv(x, topk_idx, h->ll_slot_of, h->T, h->K, H, h->E, h->cap, recv_x,
+                                   ex.launch()));
+        ctx->stats.ll_dispatch_launches += 1;
+    }
+    return exec_end(ex);
 }
 
 int moedx_ll_combine(moedx_ctx* ctx, const uint16_t* y, const int64_t* topk_idx,

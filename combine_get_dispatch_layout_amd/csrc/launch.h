@@ -148,6 +148,10 @@ hipError_t launch_ll_dispatch(const void* x, const int64_t* topk_idx, int T, int
                               int cap, void* recv_x, int32_t* recv_count, int32_t* src_idx,
                               int32_t* slot_of, const Launch& L);
 
+// The deferred receive (rows only) of a dispatch launched with recv_x NULL.
+hipError_t launch_ll_recv(const void* x, const int64_t* topk_idx, const int32_t* slot_of, int T,
+                          int K, int H, int E, int cap, void* recv_x, const Launch& L);
+
 hipError_t launch_ll_combine(const void* y, const int64_t* topk_idx, const float* topk_weights,
                              const int32_t* slot_of, int T, int K, int H, int E, int cap, void* out,
                              const Launch& L);

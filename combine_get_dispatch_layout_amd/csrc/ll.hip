@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void ll_dispatch_kernel(
     const int c1 = (int)((int64_t)H8 * (slice + 1) / slices);
     const u32x4* src = x + (int64_t)t * H8;
     u32x4 first = {0u, 0u, 0u, 0u};
-    if (c0 + tid < c1) first = __builtin_nontemporal_load(src + c0 + tid);
+    if (recv_x != nullptr && c0 + tid < c1) first = __builtin_nontemporal_load(src + c0 + tid);
 
     // Lane k holds the token's k-th expert (-1 when empty or out of range).
     int64_t ek = -1;
@@ -140,9 +140,42 @@ __global__ __launch_bounds__(kThreads) void ll_dispatch_kernel(
     // slot row of lane k, as a row index of recv_x [E * cap, H]
     const int row_l = slot >= 0 ? (int)ek * cap + slot : 0;
 
-    // Rows: this slice's chunk range of x[t] to every chosen expert's slot.
+    // Rows: this slice's chunk range of x[t] to every chosen expert's slot
+    // (none when the receive is deferred to ll_recv_kernel).
+    if (recv_x == nullptr) return;
     for (int c = c0 + tid; c < c1; c += kThreads) {
         const u32x4 v = c == c0 + tid ? first : __builtin_nontemporal_load(src + c);
+        uint64_t m = dests;
+        while (m) {
+            const int k = __builtin_ctzll(m);
+            m &= m - 1;
+            const int64_t row = __builtin_amdgcn_readlane(row_l, k);
+            __builtin_nontemporal_store(v, recv_x + row * H8 + c);
+        }
+    }
+}
+
+// The deferred receive of a low-latency dispatch: grid = T * slices; the
+// token's rows go to the slots the dispatch recorded in slot_of.
+__global__ __launch_bounds__(kThreads) void ll_recv_kernel(
+    const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx,
+    const int32_t* __restrict__ slot_of, int K, int H8, int E, int cap, int slices,
+    u32x4* __restrict__ recv_x) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x / slices;
+    const int slice = blockIdx.x - t * slices;
+    int row_l = -1;
+    if (lane < K) {
+        const int64_t e = topk_idx[(int64_t)t * K + lane];
+        const int s = slot_of[(int64_t)t * K + lane];
+        if (e >= 0 && e < E && s >= 0 && s < cap) row_l = (int)e * cap + s;
+    }
+    const uint64_t dests = __ballot(row_l >= 0);
+    const int c0 = (int)((int64_t)H8 * slice / slices);
+    const int c1 = (int)((int64_t)H8 * (slice + 1) / slices);
+    const u32x4* src = x + (int64_t)t * H8;
+    for (int c = c0 + (int)threadIdx.x; c < c1; c += kThreads) {
+        const u32x4 v = __builtin_nontemporal_load(src + c);
         uint64_t m = dests;
         while (m) {
             const int k = __builtin_ctzll(m);
@@ -240,6 +273,15 @@ hipError_t launch_ll_dispatch(const void* x, const int64_t* topk_idx, int T, int
     return launch_kernel(ll_dispatch_kernel, dim3(T * slices + 1), dim3(kThreads), L,
                          static_cast<const u32x4*>(x), topk_idx, T, K, H8, E, cap, slices,
                          static_cast<u32x4*>(recv_x), recv_count, src_idx, slot_of);
+}
+
+hipError_t launch_ll_recv(const void* x, const int64_t* topk_idx, const int32_t* slot_of, int T,
+                          int K, int H, int E, int cap, void* recv_x, const Launch& L) {
+    const int H8 = H / 8;
+    const int slices = ll_slices(T, H8, MOEDX_LL_COMBINE_TARGET_WG);
+    return launch_kernel(ll_recv_kernel, dim3(T * slices), dim3(kThreads), L,
+                         static_cast<const u32x4*>(x), topk_idx, slot_of, K, H8, E, cap, slices,
+                         static_cast<u32x4*>(recv_x));
 }
 
 hipError_t launch_ll_combine(const void* y, const int64_t* topk_idx, const float* topk_weights,

@@ -317,6 +317,10 @@ MOEDX_API int moedx_ll_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  *   src_idx[e][s] = L_e[s] and slot_of[t][k] = position of t in L_{topk_idx[t,k]}
  *   (-1 for an empty slot).  Runs as a single kernel launch; there is no
  *   deferred receive hook (no network receive exists on one GPU).
+ * recv_x == NULL defers the receive (return_recv_hook=True of the low-latency
+ *   example: the rows arrive only when the hook runs): counts and the handle
+ *   are written, rows are not, and x is not read; moedx_ll_dispatch_recv then
+ *   copies the rows.
  * Errors: MOEDX_ECAPACITY when T > cap or the workspace is too small;
  * MOEDX_EINVAL when E * cap exceeds 2^31 - 1 rows, H % 8 != 0, a pointer is
  * NULL or misaligned (x, recv_x 16-byte; workspace 256-byte). */
@@ -325,6 +329,16 @@ MOEDX_API int moedx_ll_dispatch(moedx_ctx *ctx, const uint16_t *x, const int64_t
                                 uint16_t *recv_x, int32_t *recv_count, void *workspace,
                                 size_t workspace_bytes, moedx_handle **out,
                                 const moedx_exec *exec);
+
+/* The deferred receive of a moedx_ll_dispatch called with recv_x == NULL (the
+ * hook of [GCU]'s low-latency example, "How DeepEP Enables Hook-Based
+ * Overlapping Without SM Occupation"): recv_x[e][slot_of[t][k]] = x[t] for
+ * every filled slot.  x, topk_idx and H as given to that dispatch; one kernel
+ * launch.  Errors: MOEDX_EINVAL for a handle that is not low-latency, H % 8
+ * != 0, NULL or misaligned pointers (16-byte). */
+MOEDX_API int moedx_ll_dispatch_recv(moedx_ctx *ctx, const moedx_handle *h, const uint16_t *x,
+                                     const int64_t *topk_idx, int H, uint16_t *recv_x,
+                                     const moedx_exec *exec);
 
 /* out[t] (bf16 [T, H]) = bf16_rne( fmaf chain over k = 0..K-1, from +0.0f, of
  * topk_weights[t,k] * y[e_k][slot_of[t,k]] ), y bf16 [E, cap, H]; empty slots

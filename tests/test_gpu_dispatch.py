@@ -176,3 +176,50 @@ def test_cached_dispatch_rejects_topk(oracle):
                               w.hidden, 0, None, None, ctypes.c_void_p(recv.data_ptr()), None,
                               None, None, None)
     assert rc == _capi.MOEDX_ESTATE
+
+
+@pytest.mark.parametrize("w,tokens", [(wl.TINY, None), (wl.PREFILL, 1000)],
+                         ids=["tiny", "prefill-1000"])
+def test_training_pairings(oracle, w, tokens):
+    """The four functions of the normal-kernel example: dispatch_forward,
+    combine_forward, and their backward pairings -- combine_backward is a cached
+    dispatch of the output gradient, dispatch_backward a combine of the row
+    gradients that also reduces the gradient of recv_topk_weights."""
+    dev = device()
+    inp = wl.make_inputs(w, tokens=tokens)
+    T, H, K = inp.x.shape[0], w.hidden, w.topk
+    E, R, C = w.experts, w.ranks, _channels(w)
+    ref = oracle_first_dispatch(oracle, inp, E, R, C, with_rows=False)
+    N = ref.prefix.num_recv
+    buf = make_buffer(E, R, C, T)
+    print(f"[pairings] {w.name} T={T}", flush=True)
+    # dispatch_forward
+    recv_x, rti, rtw, _, h, _ = buf.dispatch(inp.x.to(dev), topk_idx=inp.topk_idx.to(dev),
+                                             topk_weights=inp.topk_weights.to(dev))
+    rx_ref, rti_ref, rtw_ref = oracle.pack_bf16(bf16_bits(inp.x), inp.topk_idx.numpy(),
+                                                inp.topk_weights.numpy(), E, ref.prefix)
+    assert_equal("recv_x", np_(recv_x), rx_ref)
+    assert_equal("recv_topk_idx", np_(rti), rti_ref)
+    assert_equal("recv_topk_weights", np_(rtw).view(np.uint32), rtw_ref.view(np.uint32))
+    g = torch.Generator().manual_seed(9)
+    # combine_forward of expert outputs y (unweighted reduction of the rows)
+    y = torch.randn(N, H, generator=g).to(torch.bfloat16)
+    comb, cw, _ = buf.combine(y.to(dev), h)
+    want, _ = oracle.combine(bf16_bits(y), inp.topk_idx.numpy(), E, ref.prefix)
+    assert cw is None
+    assert_bf16_within_1ulp("combine_forward", np_(comb), want)
+    # combine_backward: the output gradient goes to every row like x did
+    grad_out = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    grad_rows, g_rti, g_rtw, _, _, _ = buf.dispatch(grad_out.to(dev), handle=h)
+    assert g_rti is None and g_rtw is None
+    want_rows, _, _ = oracle.pack_bf16(bf16_bits(grad_out), inp.topk_idx.numpy(), None, E,
+                                       ref.prefix, with_topk=False)
+    assert_equal("combine_backward", np_(grad_rows), want_rows)
+    # dispatch_backward: row gradients and the gradient of recv_topk_weights
+    grad_recv = torch.randn(N, H, generator=g).to(torch.bfloat16)
+    grad_rtw = torch.randn(N, K, generator=g)
+    gx, gw, _ = buf.combine(grad_recv.to(dev), h, topk_weights=grad_rtw.to(dev))
+    want_x, want_w = oracle.combine(bf16_bits(grad_recv), inp.topk_idx.numpy(), E, ref.prefix,
+                                    recv_topk_weights=grad_rtw.numpy())
+    assert_bf16_within_1ulp("dispatch_backward x", np_(gx), want_x)
+    assert_equal("dispatch_backward weights", np_(gw).view(np.uint32), want_w.view(np.uint32))
