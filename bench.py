@@ -74,6 +74,8 @@ def measured_traffic(op):
     None once the kernel source differs from the one profiled."""
     import hashlib
 
+    if op not in TRAFFIC_SOURCES:
+        return None
     path = os.path.join(ROOT, "combine_get_dispatch_layout_amd", "csrc", TRAFFIC_SOURCES[op])
     digest = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
     summary = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -351,6 +353,37 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
                         f"oracle pack_bf16 on {ts} tokens of the same workload")
     rows["cached_dispatch"] = entry(w, "cached_dispatch", ms, nbytes,
                                     {"recv_rows": N, "dtype": "bf16"}, cpu)
+
+    # -- what handle reuse saves: a first dispatch in exact mode on the same
+    # workload = layout + scan, the host wait for N and the per-expert counts,
+    # then the pack (rows, recv_topk_*, handle rows); a fresh handle each time
+    log_fn(f"[bench] row first_dispatch_exact: {w.name}")
+    nb_exact = ctypes.c_size_t()
+    C.check(C.moedx_handle_workspace_bytes(buf.ctx, T, K, 0, ctypes.byref(nb_exact)))
+    gw = inp.topk_weights.to(dev)
+    blocking = C.make_exec(stream.cuda_stream, None, None, 0)
+    for s in sets:
+        s["ws_exact"] = torch.empty(nb_exact.value, dtype=torch.uint8, device=dev)
+        s["rti"] = torch.empty(T * min(K, w.ranks), K, dtype=torch.int64, device=dev)
+        s["rtw"] = torch.empty(T * min(K, w.ranks), K, dtype=torch.float32, device=dev)
+
+    def first_exact(s):
+        def f():
+            h = ctypes.c_void_p()
+            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, P(s["ws_exact"]),
+                                             nb_exact.value, 0, ctypes.byref(h),
+                                             ctypes.byref(blocking)))
+            C.check(C.moedx_dispatch(buf.ctx, h, P(s["x"]), T, H, C.MOEDX_QUANT_NONE, P(idx),
+                                     P(gw), P(s["recv"]), None, P(s["rti"]), P(s["rtw"]), exr))
+            C.moedx_handle_destroy(h)  # the host record only; the workspace stays alive
+        return f
+
+    ms_first = timed([first_exact(s) for s in sets])
+    rows["first_dispatch_exact"] = entry(
+        w, "first_dispatch_exact", ms_first,
+        2 * T * H + 2 * N * H + 12 * T * K + 12 * N * K + 4 * T * w.ranks + 4 * N,
+        {"recv_rows": N, "note": "layout + host wait for N + pack; cached_dispatch above "
+                                 "is what handle reuse leaves"})
     for s in sets:
         C.moedx_handle_destroy(s["h"])
     del sets, buf
