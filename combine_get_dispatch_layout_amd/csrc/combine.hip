@@ -27,7 +27,7 @@
 #include "rows.h"
 
 #ifndef MOEDX_COMBINE_CPL
-#define MOEDX_COMBINE_CPL 2  // 16-byte chunks per lane; a wave covers 64 * CPL chunks
+#define MOEDX_COMBINE_CPL 1  // 16-byte chunks per lane; a wave covers 64 * CPL chunks
 #endif
 #ifndef MOEDX_COMBINE_VISIT_BATCH
 #define MOEDX_COMBINE_VISIT_BATCH 4  // visited rows whose loads are issued together
