@@ -167,3 +167,17 @@ def test_fp8_inf_and_nan_blocks(oracle):
     x[5, 400] = 0x7F80
     x[5, 401] = 0xFF80         # inf and -inf: inf / inf is NaN
     run_case(oracle, _rand(T, 16, 2, seed=14), H, 16, 4, 2, x_u16=x, fp8=True)
+
+
+@pytest.mark.parametrize("H", [1000, 2056, 7176])
+def test_ragged_hidden(oracle, H):
+    """Row widths that leave a short last slice in the pack and the combine
+    (H / 8 = 125, 257, 897 chunks of 16 bytes)."""
+    run_case(oracle, _rand(150, 32, 4, p_empty=0.1, seed=H), H, 32, 8, 3)
+
+
+@pytest.mark.parametrize("H", [1152, 2176])
+def test_fp8_ragged_blocks(oracle, H):
+    """FP8 rows whose 1x128 blocks do not split evenly over the waves of a row
+    (9 and 17 blocks)."""
+    run_case(oracle, _rand(90, 32, 4, seed=H), H, 32, 8, 3, fp8=True)
