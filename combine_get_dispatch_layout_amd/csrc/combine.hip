@@ -139,7 +139,7 @@ __device__ __forceinline__ Visits item_visits(const ItemLoads& a, int base, int6
 }
 
 // One wave per (token, slice of 64 * CPL chunks of its row).
-__global__ __launch_bounds__(256) void combine_kernel(
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(
     const u32x4* __restrict__ y, int T, int H8, int K, RowMap rm,
     const int8_t* __restrict__ slot_bucket, const float* __restrict__ gate_weights,
     const float* __restrict__ recv_topk_weights, u32x4* __restrict__ out,
@@ -244,7 +244,7 @@ hipError_t launch_combine(const void* y, int T, int H, int K, const RowMap& rm,
     const int64_t blocks = row_blocks(T, slices);
     const u32x4* ys = static_cast<const u32x4*>(y);
     u32x4* os = static_cast<u32x4*>(out);
-    return launch_kernel(combine_kernel, dim3((int)blocks), dim3(256), L, ys, T, H8, K, rm,
+    return launch_kernel(combine_kernel, dim3((int)blocks), dim3(kRowThreads), L, ys, T, H8, K, rm,
                          slot_bucket, gate_weights, recv_topk_weights, os, combined_topk_weights,
                          slices);
 }

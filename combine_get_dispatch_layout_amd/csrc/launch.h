@@ -29,7 +29,11 @@ __host__ __device__ inline int num_groups(int T) { return (T + kGroup - 1) / kGr
 // waves per workgroup; wave index = token * waves_per_token + slice, in
 // workgroup order.  (Keeping each 64-token group on one XCD was measured
 // slower: it spreads the rows in flight over more of HBM.)
-constexpr int kRowWavesPerBlock = 4;
+#ifndef MOEDX_ROW_WAVES_PER_BLOCK
+#define MOEDX_ROW_WAVES_PER_BLOCK 4
+#endif
+constexpr int kRowWavesPerBlock = MOEDX_ROW_WAVES_PER_BLOCK;
+constexpr int kRowThreads = kRowWavesPerBlock * 64;
 
 inline int64_t row_blocks(int T, int waves_per_token) {
     return ((int64_t)T * waves_per_token + kRowWavesPerBlock - 1) / kRowWavesPerBlock;

@@ -77,7 +77,7 @@ __device__ __forceinline__ void write_handle_rows(const HandleRows& hr, const To
 
 // CPL = 16-byte chunks each lane moves per pass over its part of the row.
 template <int CPL>
-__global__ __launch_bounds__(256) void pack_bf16_kernel(
+__global__ __launch_bounds__(kRowThreads) void pack_bf16_kernel(
     const u32x4* __restrict__ x, int T, int H8, int split, RowMap rm, HandleRows hr,
     u32x4* __restrict__ recv_x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_weights, int K, int E, int P, BucketDiv bucket,
@@ -191,7 +191,7 @@ __device__ __forceinline__ float pow2_ceil(float t) {
 // s of a block depends on kMode (moedx.h).  tensor_s / tensor_rs: the caller's
 // scale and its correctly rounded reciprocal (kTensor only).
 template <int CPL, int kMode>
-__global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__ x, int T, int H8,
+__global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(const u32x4* __restrict__ x, int T, int H8,
                                                        int split, RowMap rm, HandleRows hr,
                                                        u32x2* __restrict__ recv_x8,
                                                        void* __restrict__ recv_scales,
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const u32x4* __restrict__
 // of token t go unchanged to every receive row of t.  One wave per (token,
 // part of the code row); part 0 also moves the scale row.
 template <int CPL>
-__global__ __launch_bounds__(256) void pack_bytes_kernel(const u32x4* __restrict__ codes,
+__global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(const u32x4* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales, int T,
                                                          int C16, int SB, int split, RowMap rm,
                                                          HandleRows hr, u32x4* __restrict__ recv,
@@ -422,7 +422,7 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
                             float* recv_topk_weights, const Launch& L) {
     const int H8 = H / 8;
     const int split = pack_split(H8, kWaveChunks);
-    const dim3 grid(pack_blocks(T, split)), block(256);
+    const dim3 grid(pack_blocks(T, split)), block(kRowThreads);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x4* rx = static_cast<u32x4*>(recv_x);
 #define MOEDX_PACK(N)                                                                         \
@@ -445,7 +445,7 @@ hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const 
                            const Launch& L) {
     const int H8 = H / 8;
     const int split = pack_split(H8 / 16, kWaveBlocks);
-    const dim3 grid(pack_blocks(T, split)), block(256);
+    const dim3 grid(pack_blocks(T, split)), block(kRowThreads);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x2* rx = static_cast<u32x2*>(recv_x8);
     const int per_part = ((H8 / 16 + split - 1) / split) * 16;  // at most 16 * kWaveBlocks
@@ -470,7 +470,7 @@ hipError_t launch_pack_bytes(const void* codes, const void* scales, int T, int H
                              void* recv_scales, const Launch& L) {
     const int C16 = H / 16;
     const int split = pack_split(C16, kWaveChunks);
-    const dim3 grid(pack_blocks(T, split)), block(256);
+    const dim3 grid(pack_blocks(T, split)), block(kRowThreads);
     const u32x4* cs = static_cast<const u32x4*>(codes);
     u32x4* rc = static_cast<u32x4*>(recv_codes);
     const uint8_t* ss = static_cast<const uint8_t*>(scales);
