@@ -144,7 +144,11 @@ MOEDX_API const char *moedx_last_error(void);
  * number of contiguous token ranges the layout reports per bucket (the
  * channel unit of channel_prefix_matrix); max_tokens bounds T for every call
  * and sizes the ctx's scratch.  Allocates the ctx stream (default priority),
- * a small device scratch and a pinned host buffer; flags must be 0. */
+ * a small device scratch and a pinned host buffer; flags must be 0.
+ * The layout launches of one ctx (moedx_get_dispatch_layout,
+ * moedx_dispatch_prepare) share the scratch's completion counter: they must
+ * not run concurrently (issue them on one stream, or order them with events);
+ * other calls may overlap freely when their buffers do. */
 MOEDX_API int moedx_create(moedx_ctx **out, int device, int num_experts, int num_ranks,
                            int num_channels, int max_tokens, uint32_t flags);
 MOEDX_API int moedx_destroy(moedx_ctx *ctx);
