@@ -181,3 +181,11 @@ def test_fp8_ragged_blocks(oracle, H):
     """FP8 rows whose 1x128 blocks do not split evenly over the waves of a row
     (9 and 17 blocks)."""
     run_case(oracle, _rand(90, 32, 4, seed=H), H, 32, 8, 3, fp8=True)
+
+
+def test_large_batch_global_scan_paths(oracle):
+    """200000 tokens, 16 buckets, 200 channels: the group prefixes (3125 groups
+    x 16 buckets) and the channel partials (201 x 16) exceed the finishing
+    workgroup's LDS staging, so both come from global memory, over several
+    scan passes."""
+    run_case(oracle, _rand(200_000, 64, 4, p_empty=0.05, seed=77), 64, 64, 16, 200)
