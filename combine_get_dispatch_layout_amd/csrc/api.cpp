@@ -533,7 +533,8 @@ int moedx_handle_tensor(const moedx_handle* h, int which, const void** dev, int6
     if (h->kind == kNormal) {
         switch (which) {
             case MOEDX_T_RANK_PREFIX_MATRIX: p = h->rank_prefix_matrix; s0 = h->R; break;
-            case MOEDX_T_CHANNEL_PREFIX_MATRIX: p = h->channel_prefix_matrix; s0 = h->R; s1 = h->C; break;
+            case MOEDX_T_CHANNEL_PREFIX_MATRIX:
+                p = h->channel_prefix_matrix; s0 = h->R; s1 = h->C; break;
             case MOEDX_T_RECV_CHANNEL_PREFIX_MATRIX:
                 p = h->recv_channel_prefix_matrix; s0 = h->R; s1 = h->C; break;
             case MOEDX_T_RECV_SRC_IDX:
@@ -549,7 +550,8 @@ int moedx_handle_tensor(const moedx_handle* h, int which, const void** dev, int6
         switch (which) {
             case MOEDX_T_LL_SRC_IDX: p = h->ll_src_idx; s0 = h->E; s1 = h->cap; break;
             case MOEDX_T_LL_SLOT_OF: p = h->ll_slot_of; s0 = h->T; s1 = h->K; break;
-            default: return fail(MOEDX_EINVAL, "tensor %d is not part of a low-latency handle", which);
+            default:
+                return fail(MOEDX_EINVAL, "tensor %d is not part of a low-latency handle", which);
         }
     }
     *dev = p;
@@ -650,7 +652,8 @@ int moedx_dispatch_fp8(moedx_ctx* ctx, const moedx_handle* h, const void* x, int
     if (T > 0 && (!aligned16(x) || !aligned16(recv_x)))
         return fail(MOEDX_EINVAL, "x and recv_x must be 16-byte aligned");
     if (T > 0 && !tensor && !recv_scales) return fail(MOEDX_EINVAL, "recv_scales is NULL");
-    if (tensor && recv_scales) return fail(MOEDX_EINVAL, "a per-tensor scale writes no recv_scales");
+    if (tensor && recv_scales)
+        return fail(MOEDX_EINVAL, "a per-tensor scale writes no recv_scales");
     if ((T > 0 && !tensor && !aligned4(recv_scales)) ||
         (fp8->x_scales && mode != MOEDX_FP8_SCALE_UE8M0 && !aligned4(fp8->x_scales)))
         return fail(MOEDX_EINVAL, "fp32 scales must be 4-byte aligned");
@@ -733,7 +736,8 @@ int moedx_ll_dispatch(moedx_ctx* ctx, const uint16_t* x, const int64_t* topk_idx
     if (T > cap)
         return fail(MOEDX_ECAPACITY, "T=%d exceeds num_max_dispatch_tokens_per_rank=%d", T, cap);
     if ((int64_t)ctx->E * cap > INT32_MAX)
-        return fail(MOEDX_EINVAL, "num_experts * num_max_dispatch_tokens_per_rank exceeds 2^31 - 1");
+        return fail(MOEDX_EINVAL,
+                    "num_experts * num_max_dispatch_tokens_per_rank exceeds 2^31 - 1");
     if (H < 8 || H % 8 != 0) return fail(MOEDX_EINVAL, "H=%d must be a positive multiple of 8", H);
     // recv_x == NULL defers the rows to moedx_ll_dispatch_recv (x is then unused)
     if (!recv_count || !workspace || (T > 0 && (!topk_idx || (recv_x && !x))))

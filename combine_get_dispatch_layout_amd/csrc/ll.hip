@@ -241,7 +241,8 @@ __global__ __launch_bounds__(kThreads) void ll_combine_kernel(
         }
         u32x4 o;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = bf16_bits(acc[2 * j]) | (bf16_bits(acc[2 * j + 1]) << 16);
+        for (int j = 0; j < 4; ++j)
+            o[j] = bf16_bits(acc[2 * j]) | (bf16_bits(acc[2 * j + 1]) << 16);
         __builtin_nontemporal_store(o, out + (int64_t)t * H8 + c);
     }
 }
@@ -265,7 +266,8 @@ hipError_t launch_ll_dispatch(const void* x, const int64_t* topk_idx, int T, int
                               int cap, void* recv_x, int32_t* recv_count, int32_t* src_idx,
                               int32_t* slot_of, const Launch& L) {
     if (T == 0) {  // no token: every count is zero
-        return launch_kernel(zero_i32_kernel, dim3((E + kThreads - 1) / kThreads), dim3(kThreads), L,
+        return launch_kernel(zero_i32_kernel, dim3((E + kThreads - 1) / kThreads), dim3(kThreads),
+                             L,
                              recv_count, E);
     }
     const int H8 = H / 8;

@@ -7,13 +7,15 @@
 // handle ("What the Handle Contains" on the handle-reuse page) with send_head
 // and recv_src_idx; a cached dispatch only moves rows.
 //
-// Design (HBM-bound, no MFMA): one wavefront per token (or per 1/SPLIT of a
-// token's row).  The wave finds the token's rows itself (rows.h: one ballot per
-// destination bucket), reads its part of the row once with 16-byte loads, all
-// of a lane's chunks in flight before the first store, then writes it to each
-// destination row with 16-byte stores; destination rows are wave-uniform
-// scalars.  Positions are a function of the routing only, so the launch shape
-// never changes a result.
+// Design (HBM-bound, no MFMA): one wavefront per part of a token's row (at
+// most 64 chunks of 16 bytes for bf16, 8 blocks of 1x128 for FP8), so a
+// 7168-wide row is spread over 14 (bf16) or 7 (FP8) waves.  The wave finds the
+// token's rows itself (rows.h: one ballot per destination bucket), reads its
+// part of the row once with 16-byte loads, all of a lane's chunks in flight
+// before the first store, then writes it to each destination row with
+// non-temporal 16-byte stores; destination rows are wave-uniform scalars.
+// Positions are a function of the routing only, so the launch shape never
+// changes a result.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -191,11 +193,9 @@ __device__ __forceinline__ float pow2_ceil(float t) {
 // s of a block depends on kMode (moedx.h).  tensor_s / tensor_rs: the caller's
 // scale and its correctly rounded reciprocal (kTensor only).
 template <int CPL, int kMode>
-__global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(const u32x4* __restrict__ x, int T, int H8,
-                                                       int split, RowMap rm, HandleRows hr,
-                                                       u32x2* __restrict__ recv_x8,
-                                                       void* __restrict__ recv_scales,
-                                                       float tensor_s, float tensor_rs) {
+__global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(
+    const u32x4* __restrict__ x, int T, int H8, int split, RowMap rm, HandleRows hr,
+    u32x2* __restrict__ recv_x8, void* __restrict__ recv_scales, float tensor_s, float tensor_rs) {
     const int lane = threadIdx.x & 63;
     int t, part;
     wave_work(split, &t, &part);
@@ -344,11 +344,10 @@ __global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(const u32x4* __re
 // of token t go unchanged to every receive row of t.  One wave per (token,
 // part of the code row); part 0 also moves the scale row.
 template <int CPL>
-__global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(const u32x4* __restrict__ codes,
-                                                         const uint8_t* __restrict__ scales, int T,
-                                                         int C16, int SB, int split, RowMap rm,
-                                                         HandleRows hr, u32x4* __restrict__ recv,
-                                                         uint8_t* __restrict__ recv_scales) {
+__global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(
+    const u32x4* __restrict__ codes, const uint8_t* __restrict__ scales, int T, int C16, int SB,
+    int split, RowMap rm, HandleRows hr, u32x4* __restrict__ recv,
+    uint8_t* __restrict__ recv_scales) {
     const int lane = threadIdx.x & 63;
     int t, part;
     wave_work(split, &t, &part);
@@ -425,9 +424,10 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
     const dim3 grid(pack_blocks(T, split)), block(kRowThreads);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x4* rx = static_cast<u32x4*>(recv_x);
-#define MOEDX_PACK(N)                                                                         \
-    return launch_kernel(pack_bf16_kernel<N>, grid, block, L, xs, T, H8, split, rm, hr, rx, topk_idx, \
-                         topk_weights, K, E, P, bucket, recv_topk_idx, recv_topk_weights)
+#define MOEDX_PACK(N)                                                                     \
+    return launch_kernel(pack_bf16_kernel<N>, grid, block, L, xs, T, H8, split, rm, hr, rx, \
+                         topk_idx, topk_weights, K, E, P, bucket, recv_topk_idx,            \
+                         recv_topk_weights)
     switch (pick_cpl((H8 + split - 1) / split)) {
         case 1: MOEDX_PACK(1);
         case 2: MOEDX_PACK(2);

@@ -19,7 +19,7 @@ struct TokenRows {
     int row;        // lane r: row(t, r), or -1 when t does not go to bucket r
     int pos;        // lane r: position of t inside bucket r (send_head), or -1
     uint64_t mask;  // buckets of t (wave-uniform)
-    uint64_t dest;  // buckets whose row is valid (wave-uniform; equals mask for a consistent handle)
+    uint64_t dest;  // buckets whose row is valid (wave-uniform; mask, for a consistent handle)
 };
 
 __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
