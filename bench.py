@@ -87,6 +87,16 @@ def measured_traffic(op):
     return rec["traffic_bytes_per_launch"]
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, w, budget_s):
     """The CPU oracle (single thread, as it stands) on the same inputs."""
     import numpy as np
@@ -120,6 +130,8 @@ def row_bytes(kind, T, H, K, E, N=0, V=0, R=0):
                      one per-tensor scale none
     pack_fp8_prequant: read codes (TH) and fp32 scales (4T*H/128); write them
                      to N rows
+    combine        : read N rows (2NH), send_head (4TR), topk ids and gate
+                     weights (12TK); write T rows (2TH)
     cached_dispatch: read x (2TH); write N rows (2NH)
     get_layout     : read topk_idx (8TK); write is_token_in_rank (TR) and the
                      R + E counts
@@ -133,6 +145,7 @@ def row_bytes(kind, T, H, K, E, N=0, V=0, R=0):
         "pack_fp8_ue8m0": 2 * T * H + N * H + N * (H // 128),
         "pack_fp8_tensor": 2 * T * H + N * H,
         "pack_fp8_prequant": T * H + 4 * T * (H // 128) + N * H + 4 * N * (H // 128),
+        "combine": 2 * N * H + 2 * T * H + 4 * T * R + 12 * T * K,
         "cached_dispatch": 2 * T * H + 2 * N * H,
         "get_layout": 8 * T * K + T * R + 4 * (R + E),
         "ll_dispatch": 2 * T * H + 8 * T * K + 2 * V * H + 4 * V + 4 * T * K + 4 * E,
@@ -321,6 +334,23 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
                             f"oracle on {ts} tokens of the same workload")
         rows[name] = entry(w, name, ms, row_bytes(name, T, H, K, E, N=N),
                            {"recv_rows": N}, cpu)
+    # combine of bf16 expert outputs for the skewed routing (the dequantised rows
+    # in a real layer; the values do not change the work)
+    log_fn(f"[bench] row combine_fp8_skewed: {w.name}")
+    gw4 = inp.topk_weights.to(dev)
+    cap4 = T * min(K, w.ranks)
+    for s in sets:
+        s["y"] = torch.empty(cap4, H, dtype=torch.bfloat16, device=dev)
+        s["out"] = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+
+    def comb4(s):
+        return lambda: C.check(C.moedx_combine(buf.ctx, s["h"], P(s["y"]), H, P(gw4), None,
+                                               P(s["out"]), None, exr))
+
+    ms = timed([comb4(s) for s in sets])
+    rows["combine_fp8_skewed"] = entry(w, "combine_fp8_skewed", ms,
+                                       row_bytes("combine", T, H, K, E, N=N, R=w.ranks),
+                                       {"recv_rows": N, "dtype": "bf16"})
     for s in sets:
         C.moedx_handle_destroy(s["h"])
     del sets, buf, u8, pq
@@ -353,6 +383,28 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
                         f"oracle pack_bf16 on {ts} tokens of the same workload")
     rows["cached_dispatch"] = entry(w, "cached_dispatch", ms, nbytes,
                                     {"recv_rows": N, "dtype": "bf16"}, cpu)
+
+    # -- the reuse repetition: cached pack, then the gate-weighted combine
+    log_fn(f"[bench] rows combine_reuse / reuse_rep: {w.name}")
+    gw5 = inp.topk_weights.to(dev)
+    for s in sets:
+        s["out"] = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+
+    def comb5(s):
+        return lambda: C.check(C.moedx_combine(buf.ctx, s["h"], P(s["recv"]), H, P(gw5), None,
+                                               P(s["out"]), None, exr))
+
+    def rep5(s):
+        p_, c_ = cached(s), comb5(s)
+        return lambda: (p_(), c_())
+
+    ms_c = timed([comb5(s) for s in sets])
+    b_c = row_bytes("combine", T, H, K, E, N=N, R=w.ranks)
+    rows["combine_reuse"] = entry(w, "combine_reuse", ms_c, b_c, {"recv_rows": N, "dtype": "bf16"})
+    ms_r = timed([rep5(s) for s in sets])
+    rows["reuse_rep"] = entry(w, "reuse_rep", ms_r, nbytes + b_c,
+                              {"recv_rows": N, "note": "cached dispatch + weighted combine, "
+                                                      "back to back (one repetition)"})
 
     # -- what handle reuse saves: a first dispatch in exact mode on the same
     # workload = layout + scan, the host wait for N and the per-expert counts,
@@ -539,18 +591,18 @@ def main():
     def flush():
         torch.sum(flush_buf, dim=(0,), out=sink)
 
-    def prepare(s_):
+    def prepare(s_, e=exr):
         h = ctypes.c_void_p()
         C.check(C.moedx_dispatch_prepare(ctx, p_idx, T, K, P(s_["ws"]), nbytes.value, cap,
-                                         ctypes.byref(h), exr))
+                                         ctypes.byref(h), e))
         return h
 
-    def pack(h, s_):
+    def pack(h, s_, e=exr):
         C.check(C.moedx_dispatch(ctx, h, P(s_["x"]), T, H, C.MOEDX_QUANT_NONE, p_idx, p_gw,
-                                 P(s_["recv"]), None, P(s_["rti"]), P(s_["rtw"]), exr))
+                                 P(s_["recv"]), None, P(s_["rti"]), P(s_["rtw"]), e))
 
-    def combine(h, s_):
-        C.check(C.moedx_combine(ctx, h, P(s_["recv"]), H, p_gw, None, P(s_["out"]), None, exr))
+    def combine(h, s_, e=exr):
+        C.check(C.moedx_combine(ctx, h, P(s_["recv"]), H, p_gw, None, P(s_["out"]), None, e))
 
     def record():
         ev = ctypes.c_void_p()
@@ -583,6 +635,30 @@ def main():
         b = record()
         torch.cuda.synchronize()
         return elapsed_ms(a, b) / n
+
+    def op_kernel_us(op, n):
+        """Per-launch kernel durations (events stamped at each kernel's own start
+        and end) of n back-to-back launches over rotating sets: p10 / median / p90."""
+        evs = []
+        for _ in range(n):
+            a_, b_ = ctypes.c_void_p(), ctypes.c_void_p()
+            C.check(C.moedx_event_create(ctypes.byref(a_)))
+            C.check(C.moedx_event_create(ctypes.byref(b_)))
+            evs.append((a_.value, b_.value))
+        flush()
+        for i, (ka, kb) in enumerate(evs):
+            j = i % NSETS
+            e = ctypes.byref(C.make_exec(stream.cuda_stream, None, None, C.MOEDX_ASYNC, ka, kb))
+            if op == "layout":
+                C.moedx_handle_destroy(prepare(sets[j], e))
+            elif op == "pack":
+                pack(handles[j], sets[j], e)
+            else:
+                combine(handles[j], sets[j], e)
+        torch.cuda.synchronize()
+        d = sorted(elapsed_ms(ka, kb) * 1e3 for ka, kb in evs)
+        q = lambda f: d[min(len(d) - 1, int(round(f * (len(d) - 1))))]  # noqa: E731
+        return {"p10": round(q(0.1), 2), "median": round(q(0.5), 2), "p90": round(q(0.9), 2)}
 
     def pipelined_ms(n):
         """n whole steps back to back (layout, pack, combine each), rotating sets."""
@@ -621,6 +697,30 @@ def main():
     t_comb = op_avg_ms("combine", args.steps)
     ms_pipe = pipelined_ms(args.steps)
     wall = time.perf_counter() - wall0
+    dist = {op: op_kernel_us(op, args.steps) for op in ("layout", "pack", "combine")}
+
+    # Exact mode through the API on the host clock: the host waits for N after
+    # the layout (no capacity bound), then the pack and the combine run.
+    nb_exact = ctypes.c_size_t()
+    C.check(C.moedx_handle_workspace_bytes(ctx, T, K, 0, ctypes.byref(nb_exact)))
+    ws_exact = torch.empty(nb_exact.value, dtype=torch.uint8, device=dev)
+    blocking = C.make_exec(stream.cuda_stream, None, None, 0)
+
+    def exact_step(s_):
+        h_ = ctypes.c_void_p()
+        C.check(C.moedx_dispatch_prepare(ctx, p_idx, T, K, P(ws_exact), nb_exact.value, 0,
+                                         ctypes.byref(h_), ctypes.byref(blocking)))
+        pack(h_, s_)
+        combine(h_, s_, ctypes.byref(blocking))
+        C.moedx_handle_destroy(h_)
+
+    wall_exact = []
+    for i in range(max(args.warmup, 1) + args.steps):
+        t0 = time.perf_counter()
+        exact_step(sets[i % NSETS])
+        if i >= max(args.warmup, 1):
+            wall_exact.append((time.perf_counter() - t0) * 1e6)
+    wall_exact.sort()
     ms = t_lay + t_pack + t_comb
     gbs = step_bytes / (ms * 1e-3) / 1e9
     for h in handles:
@@ -655,7 +755,7 @@ def main():
         t_cpu, reps, n_cpu = cpu_baseline(inp, w, args.cpu_budget_s)
         assert n_cpu == N
         cpu = {"value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle", "tokens_per_s": round(T / t_cpu, 1),
+               "kind": "oracle", "tokens_per_s": round(T / t_cpu, 1), "cpu_model": cpu_model(),
                "sample": f"median of {reps} full {T}x{H} steps (layout+prefix+pack+weighted "
                          f"combine), single-threaded C oracle"}
 
@@ -688,9 +788,16 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernels_us": {"layout": round(t_lay * 1e3, 2), "pack": round(t_pack * 1e3, 2),
                        "combine": round(t_comb * 1e3, 2)},
+        "kernels_us_per_launch": dist,
         "kernel_GBps": {"pack": round(bytes_["pack"] / (t_pack * 1e-3) / 1e9, 1),
                         "combine": round(bytes_["combine"] / (t_comb * 1e-3) / 1e9, 1)},
         "pipelined_ms_per_step": round(ms_pipe, 5),
+        "exact_mode_api_wall_us": {
+            "median": round(statistics.median(wall_exact), 1),
+            "p10": round(wall_exact[int(0.1 * (len(wall_exact) - 1))], 1),
+            "p90": round(wall_exact[int(round(0.9 * (len(wall_exact) - 1)))], 1),
+            "note": "host clock; layout, host wait for N and the per-expert counts, pack, "
+                    "combine, host wait"},
         "pipelined_GBps_cache_assisted": round(step_bytes / (ms_pipe * 1e-3) / 1e9, 1),
         "copy_ceiling_GBps": round(copy_gbs, 1),
         "algorithmic_bytes": bytes_,

@@ -17,9 +17,10 @@
 // (rows.h); lanes 0..K-1 hold the slots, and for each bucket of the token one
 // ballot names its slots: the first is the visit, and the bucket's weight is
 // the sum over them in ascending order, so every visited row, its weight and
-// its address are wave-uniform.  Up to 4 visits' loads are issued before the
-// first FMA.  The visit order is fixed, so the result does not depend on the
-// launch shape.
+// its address are wave-uniform.  Visits go in batches of 4, then 2, then 1,
+// each batch's loads issued before its first FMA, so no row is read twice.
+// The visit order is fixed, so the result does not depend on the launch
+// shape.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,9 +29,6 @@
 
 #ifndef MOEDX_COMBINE_CPL
 #define MOEDX_COMBINE_CPL 1  // 16-byte chunks per lane; a wave covers 64 * CPL chunks
-#endif
-#ifndef MOEDX_COMBINE_VISIT_BATCH
-#define MOEDX_COMBINE_VISIT_BATCH 4  // visited rows whose loads are issued together
 #endif
 #ifndef MOEDX_COMBINE_NT_LOAD
 #define MOEDX_COMBINE_NT_LOAD 1
@@ -46,7 +44,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCPL = MOEDX_COMBINE_CPL;
-constexpr int kVB = MOEDX_COMBINE_VISIT_BATCH;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -138,6 +135,37 @@ __device__ __forceinline__ Visits item_visits(const ItemLoads& a, int base, int6
     return v;
 }
 
+// The next NB visits of *m (in order): their rows' loads are all issued,
+// then the FMAs run in visit order; the visits are taken off *m.
+template <int NB, int CPL>
+__device__ __forceinline__ void visit_batch(const u32x4* __restrict__ y, int H8, const int* cs,
+                                            const Visits& vs, uint64_t* m, float (*acc)[8]) {
+    const u32x4* src[NB];
+    float wt[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int k = __builtin_ctzll(*m);
+        *m &= *m - 1;
+        src[b] = y + (int64_t)__builtin_amdgcn_readlane(vs.row, k) * H8;
+        wt[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vs.w), k));
+    }
+    u32x4 v[NB][CPL];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) v[b][i] = load_row(src[b] + cs[i]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of its FMAs
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[i][2 * j] = __builtin_fmaf(wt[b], bf16_lo(v[b][i][j]), acc[i][2 * j]);
+                acc[i][2 * j + 1] = __builtin_fmaf(wt[b], bf16_hi(v[b][i][j]), acc[i][2 * j + 1]);
+            }
+}
+
 // One wave per (token, slice of 64 * CPL chunks of its row).
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     const u32x4* __restrict__ y, int T, int H8, int K, RowMap rm,
@@ -170,47 +198,12 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+    // Batches of 4 visits, then one of 2 and one of 1 as needed: every load of
+    // a batch is issued before its first FMA and no row is read twice.
     uint64_t m = vs.lanes;
-    int k_last = m ? __builtin_ctzll(m) : 0;
-    while (m) {
-        // kVB visited rows per batch: every load is issued before the first
-        // FMA (a batch past the last visit re-reads that visit's row and
-        // adds nothing).
-        const u32x4* src[kVB];
-        float wt[kVB];
-        bool use[kVB];
-#pragma unroll
-        for (int b = 0; b < kVB; ++b) {
-            use[b] = m != 0;
-            if (use[b]) {
-                k_last = __builtin_ctzll(m);
-                m &= m - 1;
-            }
-            src[b] = y + (int64_t)__builtin_amdgcn_readlane(vs.row, k_last) * H8;
-            wt[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vs.w), k_last));
-        }
-        u32x4 v[kVB][CPL];
-#pragma unroll
-        for (int b = 0; b < kVB; ++b)
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) v[b][i] = load_row(src[b] + cs[i]);
-        __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of its FMAs
-        // Branch-free: an unused slot of the batch computes and discards its
-        // FMA, so no control flow separates the loads from one another.
-#pragma unroll
-        for (int b = 0; b < kVB; ++b) {
-#pragma unroll
-            for (int i = 0; i < CPL; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float lo = __builtin_fmaf(wt[b], bf16_lo(v[b][i][j]), acc[i][2 * j]);
-                    const float hi =
-                        __builtin_fmaf(wt[b], bf16_hi(v[b][i][j]), acc[i][2 * j + 1]);
-                    acc[i][2 * j] = use[b] ? lo : acc[i][2 * j];
-                    acc[i][2 * j + 1] = use[b] ? hi : acc[i][2 * j + 1];
-                }
-        }
-    }
+    while (__popcll(m) >= 4) visit_batch<4, CPL>(y, H8, cs, vs, &m, acc);
+    if (__popcll(m) >= 2) visit_batch<2, CPL>(y, H8, cs, vs, &m, acc);
+    if (m) visit_batch<1, CPL>(y, H8, cs, vs, &m, acc);
     u32x4* dst = out + (int64_t)t * H8;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
