@@ -64,20 +64,31 @@ def algorithmic_bytes(T, H, K, E, R, C, N):
 TRAFFIC_SOURCES = {"layout": "layout.hip", "get_layout": "layout.hip", "pack": "pack.hip",
                    "pack_fp8": "pack.hip", "pack_fp8_ue8m0": "pack.hip",
                    "pack_fp8_tensor": "pack.hip", "pack_fp8_prequant": "pack.hip",
-                   "cached_dispatch": "pack.hip",
-                   "combine": "combine.hip", "ll_dispatch": "ll.hip", "ll_combine": "ll.hip"}
+                   "cached_dispatch": "pack.hip", "combine": "combine.hip",
+                   "combine_fp8_skewed": "combine.hip", "combine_reuse": "combine.hip",
+                   "ll_dispatch": "ll.hip", "ll_combine": "ll.hip"}
+# headers every kernel source includes: a change there changes the kernels too
+SHARED_HEADERS = ("launch.h", "rows.h")
+
+
+def source_digest(src):
+    """First 16 hex digits of the sha256 over a kernel source and the shared headers."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in (src,) + SHARED_HEADERS:
+        with open(os.path.join(ROOT, "combine_get_dispatch_layout_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(op):
     """HBM bytes per launch of `op` from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size), or
     None once the kernel source differs from the one profiled."""
-    import hashlib
-
     if op not in TRAFFIC_SOURCES:
         return None
-    path = os.path.join(ROOT, "combine_get_dispatch_layout_amd", "csrc", TRAFFIC_SOURCES[op])
-    digest = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    digest = source_digest(TRAFFIC_SOURCES[op])
     summary = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(summary):
         return None
