@@ -53,9 +53,12 @@ class EventOverlap:
     def __exit__(self, *exc):
         self.current_stream_wait()
 
+    # Held by the class: at interpreter exit module globals may already be gone.
+    _destroy = staticmethod(C.moedx_event_destroy)
+
     def __del__(self):
         if getattr(self, "event", None) is not None:
-            C.moedx_event_destroy(self.event)
+            self._destroy(self.event)
             self.event = None
 
 
@@ -116,9 +119,11 @@ class Handle:
             "num_recv": self.tensor(C.MOEDX_T_NUM_RECV, torch.int32),
         }
 
+    _destroy = staticmethod(C.moedx_handle_destroy)
+
     def __del__(self):
         if getattr(self, "ptr", None):
-            C.moedx_handle_destroy(self.ptr)
+            self._destroy(self.ptr)
             self.ptr = None
 
 
@@ -136,9 +141,11 @@ class Buffer:
                                num_channels, max_tokens, 0))
         self.ctx = ctx.value
 
+    _destroy = staticmethod(C.moedx_destroy)
+
     def __del__(self):
         if getattr(self, "ctx", None):
-            C.moedx_destroy(self.ctx)
+            self._destroy(self.ctx)
             self.ctx = None
 
     # -- plumbing ---------------------------------------------------------------
