@@ -108,6 +108,32 @@ def cpu_model():
     return "unknown"
 
 
+def kernel_us_distribution(C, stream, launch, n, flush):
+    """Per-launch kernel durations of n back-to-back launches: HIP events
+    stamped at each kernel's own start and end.  launch(i, exec_ptr) enqueues
+    launch i (one kernel) with that exec.  Returns p10 / median / p90 in us."""
+    evs = []
+    for _ in range(n):
+        a_, b_ = ctypes.c_void_p(), ctypes.c_void_p()
+        C.check(C.moedx_event_create(ctypes.byref(a_)))
+        C.check(C.moedx_event_create(ctypes.byref(b_)))
+        evs.append((a_.value, b_.value))
+    flush()
+    for i, (ka, kb) in enumerate(evs):
+        launch(i, ctypes.byref(C.make_exec(stream.cuda_stream, None, None, C.MOEDX_ASYNC, ka, kb)))
+    stream.synchronize()
+    d = []
+    for ka, kb in evs:
+        ms = ctypes.c_float()
+        C.check(C.moedx_event_elapsed_ms(ka, kb, ctypes.byref(ms)))
+        C.moedx_event_destroy(ka)
+        C.moedx_event_destroy(kb)
+        d.append(ms.value * 1e3)
+    d.sort()
+    q = lambda f: d[min(len(d) - 1, int(round(f * (len(d) - 1))))]  # noqa: E731
+    return {"p10": round(q(0.1), 2), "median": round(q(0.5), 2), "p90": round(q(0.9), 2)}
+
+
 def cpu_baseline(inp, w, budget_s):
     """The CPU oracle (single thread, as it stands) on the same inputs."""
     import numpy as np
@@ -221,6 +247,19 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
         rot_ms(fns, max(warmup, 1))
         return rot_ms(fns, steps)
 
+    # The exec the single-kernel row closures launch with: exr, or one whose
+    # events are stamped at the kernel's own start and end.
+    cur = [exr]
+
+    def per_launch(fns):
+        def launch(i, e):
+            cur[0] = e
+            fns[i % len(fns)]()
+        try:
+            return kernel_us_distribution(C, stream, launch, steps, flush)
+        finally:
+            cur[0] = exr
+
     def u16(t):
         return t.view(torch.int16).numpy().view(np.uint16)
 
@@ -283,9 +322,11 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
     def fp8_pack(s):
         return lambda: C.check(C.moedx_dispatch(
             buf.ctx, s["h"], P(s["x"]), T, H, C.MOEDX_QUANT_FP8_E4M3_1X128, None, None,
-            P(s["recv"]), P(s["scales"]), None, None, exr))
+            P(s["recv"]), P(s["scales"]), None, None, cur[0]))
 
-    ms = timed([fp8_pack(s) for s in sets])
+    fns = [fp8_pack(s) for s in sets]
+    ms = timed(fns)
+    dist = per_launch(fns)
     nbytes = row_bytes("pack_fp8", T, H, K, E, N=N)
     cpu = None
     if o is not None:
@@ -297,12 +338,13 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
         secs, reps = _median_time(lambda: o.pack_fp8(xs, pre), cpu_budget_s / 4)
         cpu = cpu_entry(row_bytes("pack_fp8", ts, H, K, E, N=pre.num_recv), secs, reps,
                         f"oracle pack_fp8 on {ts} tokens of the same workload")
-    rows["pack_fp8"] = entry(w, "pack_fp8", ms, nbytes, {"recv_rows": N, "dtype": "bf16->e4m3"}, cpu)
+    rows["pack_fp8"] = entry(w, "pack_fp8", ms, nbytes, {"recv_rows": N, "dtype": "bf16->e4m3",
+                                                          "per_launch_us": dist}, cpu)
 
     # the other scale modes and the pre-quantised pass-through, same workload
     def fp8_opt(s, opts, x_ptr, scales_ptr):
         return lambda: C.check(C.moedx_dispatch_fp8(buf.ctx, s["h"], x_ptr, T, H, ctypes.byref(opts),
-                                                    P(s["recv"]), scales_ptr, exr))
+                                                    P(s["recv"]), scales_ptr, cur[0]))
 
     ue8m0 = C.moedx_fp8(C.MOEDX_FP8_SCALE_UE8M0, 0, 0.0, None)
     tensor = C.moedx_fp8(C.MOEDX_FP8_SCALE_TENSOR, 0, 0.0123, None)
@@ -322,6 +364,7 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
     for name, fns, omode in variants:
         log_fn(f"[bench] row {name}: {w.name}")
         ms = timed(fns)
+        dist = per_launch(fns)
         cpu = None
         if o is not None:
             ts = 512
@@ -344,7 +387,7 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
             cpu = cpu_entry(row_bytes(name, ts, H, K, E, N=pre.num_recv), secs, reps,
                             f"oracle on {ts} tokens of the same workload")
         rows[name] = entry(w, name, ms, row_bytes(name, T, H, K, E, N=N),
-                           {"recv_rows": N}, cpu)
+                           {"recv_rows": N, "per_launch_us": dist}, cpu)
     # combine of bf16 expert outputs for the skewed routing (the dequantised rows
     # in a real layer; the values do not change the work)
     log_fn(f"[bench] row combine_fp8_skewed: {w.name}")
@@ -356,12 +399,14 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
 
     def comb4(s):
         return lambda: C.check(C.moedx_combine(buf.ctx, s["h"], P(s["y"]), H, P(gw4), None,
-                                               P(s["out"]), None, exr))
+                                               P(s["out"]), None, cur[0]))
 
-    ms = timed([comb4(s) for s in sets])
+    fns = [comb4(s) for s in sets]
+    ms = timed(fns)
     rows["combine_fp8_skewed"] = entry(w, "combine_fp8_skewed", ms,
                                        row_bytes("combine", T, H, K, E, N=N, R=w.ranks),
-                                       {"recv_rows": N, "dtype": "bf16"})
+                                       {"recv_rows": N, "dtype": "bf16",
+                                        "per_launch_us": per_launch(fns)})
     for s in sets:
         C.moedx_handle_destroy(s["h"])
     del sets, buf, u8, pq
@@ -375,11 +420,13 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
     def cached(s):
         return lambda: C.check(C.moedx_dispatch(
             buf.ctx, s["h"], P(s["x"]), T, H, C.MOEDX_QUANT_NONE, None, None,
-            P(s["recv"]), None, None, None, exr))
+            P(s["recv"]), None, None, None, cur[0]))
 
     for s in sets:  # the first dispatch on each handle writes its rows
         cached(s)()
-    ms = timed([cached(s) for s in sets])
+    fns = [cached(s) for s in sets]
+    ms = timed(fns)
+    dist = per_launch(fns)
     nbytes = row_bytes("cached_dispatch", T, H, K, E, N=N)
     cpu = None
     if o is not None:
@@ -393,7 +440,7 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
         cpu = cpu_entry(row_bytes("cached_dispatch", ts, H, K, E, N=pre.num_recv), secs, reps,
                         f"oracle pack_bf16 on {ts} tokens of the same workload")
     rows["cached_dispatch"] = entry(w, "cached_dispatch", ms, nbytes,
-                                    {"recv_rows": N, "dtype": "bf16"}, cpu)
+                                    {"recv_rows": N, "dtype": "bf16", "per_launch_us": dist}, cpu)
 
     # -- the reuse repetition: cached pack, then the gate-weighted combine
     log_fn(f"[bench] rows combine_reuse / reuse_rep: {w.name}")
@@ -403,15 +450,17 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
 
     def comb5(s):
         return lambda: C.check(C.moedx_combine(buf.ctx, s["h"], P(s["recv"]), H, P(gw5), None,
-                                               P(s["out"]), None, exr))
+                                               P(s["out"]), None, cur[0]))
 
     def rep5(s):
         p_, c_ = cached(s), comb5(s)
         return lambda: (p_(), c_())
 
-    ms_c = timed([comb5(s) for s in sets])
+    fns = [comb5(s) for s in sets]
+    ms_c = timed(fns)
     b_c = row_bytes("combine", T, H, K, E, N=N, R=w.ranks)
-    rows["combine_reuse"] = entry(w, "combine_reuse", ms_c, b_c, {"recv_rows": N, "dtype": "bf16"})
+    rows["combine_reuse"] = entry(w, "combine_reuse", ms_c, b_c,
+                                  {"recv_rows": N, "dtype": "bf16", "per_launch_us": per_launch(fns)})
     ms_r = timed([rep5(s) for s in sets])
     rows["reuse_rep"] = entry(w, "reuse_rep", ms_r, nbytes + b_c,
                               {"recv_rows": N, "note": "cached dispatch + weighted combine, "
@@ -466,9 +515,11 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
 
     def get_layout(s):
         return lambda: C.check(C.moedx_get_dispatch_layout(
-            buf.ctx, P(s["idx"]), T, K, P(s["ntpr"]), P(s["ntpe"]), P(s["itir"]), exr))
+            buf.ctx, P(s["idx"]), T, K, P(s["ntpr"]), P(s["ntpe"]), P(s["itir"]), cur[0]))
 
-    ms = timed([get_layout(s) for s in lsets])
+    fns = [get_layout(s) for s in lsets]
+    ms = timed(fns)
+    dist = per_launch(fns)
     cpu = None
     if o is not None:
         ids = inp.topk_idx.numpy()
@@ -476,7 +527,7 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
         cpu = cpu_entry(row_bytes("get_layout", T, H, K, E, R=R), secs, reps,
                         f"oracle layout on the full {T}-token workload")
     rows["get_layout"] = entry(w, "get_layout", ms, row_bytes("get_layout", T, H, K, E, R=R),
-                               {"bound_note": "latency (under 0.3 MB)"}, cpu)
+                               {"bound_note": "latency (under 0.3 MB)", "per_launch_us": dist}, cpu)
     del lsets, buf
 
     # -- low-latency dispatch and combine on the 128-token decode workload -------
@@ -500,7 +551,7 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
         def f():
             h = ctypes.c_void_p()
             C.check(C.moedx_ll_dispatch(buf.ctx, P(s["x"]), P(ids), T, K, H, cap, P(s["recv"]),
-                                        P(s["cnt"]), P(s["ws"]), nb.value, ctypes.byref(h), exr))
+                                        P(s["cnt"]), P(s["ws"]), nb.value, ctypes.byref(h), cur[0]))
             if s["h"] is not None:
                 C.moedx_handle_destroy(s["h"])
             s["h"] = h
@@ -508,10 +559,13 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
 
     def ll_combine(s):
         return lambda: C.check(C.moedx_ll_combine(buf.ctx, P(s["recv"]), P(ids), P(wts), s["h"], H,
-                                                  P(s["out"]), exr))
+                                                  P(s["out"]), cur[0]))
 
-    ms_d = timed([ll_dispatch(s) for s in llsets])
-    ms_c = timed([ll_combine(s) for s in llsets])
+    fns_d, fns_c = [ll_dispatch(s) for s in llsets], [ll_combine(s) for s in llsets]
+    ms_d = timed(fns_d)
+    dist_d = per_launch(fns_d)
+    ms_c = timed(fns_c)
+    dist_c = per_launch(fns_c)
     V = int((inp.topk_idx >= 0).sum())
     cpu_d = cpu_c = None
     if o is not None:
@@ -530,9 +584,9 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
                           f"oracle ll_combine on the full {T}-token workload")
     note = {"bound_note": "latency: a few MB per launch", "slots_filled": V}
     rows["ll_dispatch"] = entry(w, "ll_dispatch", ms_d, row_bytes("ll_dispatch", T, H, K, E, V=V),
-                                note, cpu_d)
+                                dict(note, per_launch_us=dist_d), cpu_d)
     rows["ll_combine"] = entry(w, "ll_combine", ms_c, row_bytes("ll_combine", T, H, K, E, V=V),
-                               note, cpu_c)
+                               dict(note, per_launch_us=dist_c), cpu_c)
     for s in llsets:
         if s["h"] is not None:
             C.moedx_handle_destroy(s["h"])
@@ -648,28 +702,17 @@ def main():
         return elapsed_ms(a, b) / n
 
     def op_kernel_us(op, n):
-        """Per-launch kernel durations (events stamped at each kernel's own start
-        and end) of n back-to-back launches over rotating sets: p10 / median / p90."""
-        evs = []
-        for _ in range(n):
-            a_, b_ = ctypes.c_void_p(), ctypes.c_void_p()
-            C.check(C.moedx_event_create(ctypes.byref(a_)))
-            C.check(C.moedx_event_create(ctypes.byref(b_)))
-            evs.append((a_.value, b_.value))
-        flush()
-        for i, (ka, kb) in enumerate(evs):
+        """Per-launch kernel durations of n back-to-back launches over rotating
+        sets: p10 / median / p90."""
+        def launch(i, e):
             j = i % NSETS
-            e = ctypes.byref(C.make_exec(stream.cuda_stream, None, None, C.MOEDX_ASYNC, ka, kb))
             if op == "layout":
                 C.moedx_handle_destroy(prepare(sets[j], e))
             elif op == "pack":
                 pack(handles[j], sets[j], e)
             else:
                 combine(handles[j], sets[j], e)
-        torch.cuda.synchronize()
-        d = sorted(elapsed_ms(ka, kb) * 1e3 for ka, kb in evs)
-        q = lambda f: d[min(len(d) - 1, int(round(f * (len(d) - 1))))]  # noqa: E731
-        return {"p10": round(q(0.1), 2), "median": round(q(0.5), 2), "p90": round(q(0.9), 2)}
+        return kernel_us_distribution(C, stream, launch, n, flush)
 
     def pipelined_ms(n):
         """n whole steps back to back (layout, pack, combine each), rotating sets."""
