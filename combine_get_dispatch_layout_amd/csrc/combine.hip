@@ -171,12 +171,11 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     const u32x4* __restrict__ y, int T, int H8, int K, RowMap rm,
     const int8_t* __restrict__ slot_bucket, const float* __restrict__ gate_weights,
     const float* __restrict__ recv_topk_weights, u32x4* __restrict__ out,
-    float* __restrict__ combined_topk_weights, int slices) {
+    float* __restrict__ combined_topk_weights, RowSplit rs) {
     constexpr int CPL = kCPL;
     const int lane = threadIdx.x & 63;
-    const int w = row_wave();
-    const int t = w / slices;
-    const int part = w - t * slices;
+    int t, part;
+    row_part(rs, &t, &part);
     if (t >= T) return;
     const int base = lane < rm.R ? rm.rank_prefix_matrix[lane] - rm.num_tokens_per_rank[lane] : 0;
     const ItemLoads ld = item_loads(rm, slot_bucket, gate_weights, K, t, lane);
@@ -239,7 +238,7 @@ hipError_t launch_combine(const void* y, int T, int H, int K, const RowMap& rm,
     u32x4* os = static_cast<u32x4*>(out);
     return launch_kernel(combine_kernel, dim3((int)blocks), dim3(kRowThreads), L, ys, T, H8, K, rm,
                          slot_bucket, gate_weights, recv_topk_weights, os, combined_topk_weights,
-                         slices);
+                         make_row_split(H8, slices));
 }
 
 }  // namespace moedx

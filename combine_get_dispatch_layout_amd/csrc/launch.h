@@ -10,6 +10,8 @@
 #include <tuple>
 #include <utility>
 
+#include "fastdiv.h"
+
 namespace moedx {
 
 #ifndef MOEDX_LAYOUT_TILE
@@ -42,6 +44,25 @@ inline int64_t row_blocks(int T, int waves_per_token) {
 // This wave's index (wave-uniform).
 __device__ __forceinline__ int row_wave() {
     return __builtin_amdgcn_readfirstlane(blockIdx.x * kRowWavesPerBlock + (threadIdx.x >> 6));
+}
+
+// How a token's row is cut over waves: `split` waves per token; part p covers
+// units [p * per, min((p + 1) * per, units)) with per = ceil(units / split).
+struct RowSplit {
+    FastDiv div;  // wave index / split
+    int split;
+    int per;
+};
+
+inline RowSplit make_row_split(int units, int split) {
+    return RowSplit{make_fastdiv((uint32_t)split), split, (units + split - 1) / split};
+}
+
+// The wave's token and part (wave-uniform).
+__device__ __forceinline__ void row_part(const RowSplit& rs, int* t, int* part) {
+    const int w = row_wave();
+    *t = (int)rs.div.div((uint32_t)w);
+    *part = w - *t * rs.split;
 }
 
 // Where a launch goes and, optionally, events stamped with the kernel's own

@@ -63,13 +63,6 @@ __device__ __forceinline__ void store_row(V v, V* p) {
 #endif
 }
 
-// The wave's token and part of the row; t is wave-uniform.
-__device__ __forceinline__ void wave_work(int split, int* t, int* part) {
-    const int w = row_wave();
-    *t = w / split;
-    *part = w - *t * split;
-}
-
 __device__ __forceinline__ void write_handle_rows(const HandleRows& hr, const TokenRows& d, int t,
                                                   int R, int lane) {
     if (hr.send_head == nullptr) return;
@@ -80,19 +73,19 @@ __device__ __forceinline__ void write_handle_rows(const HandleRows& hr, const To
 // CPL = 16-byte chunks each lane moves per pass over its part of the row.
 template <int CPL>
 __global__ __launch_bounds__(kRowThreads) void pack_bf16_kernel(
-    const u32x4* __restrict__ x, int T, int H8, int split, RowMap rm, HandleRows hr,
+    const u32x4* __restrict__ x, int T, int H8, RowSplit rs, RowMap rm, HandleRows hr,
     u32x4* __restrict__ recv_x, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_weights, int K, int E, int P, BucketDiv bucket,
     int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_topk_weights) {
     const int lane = threadIdx.x & 63;
     int t, part;
-    wave_work(split, &t, &part);
+    row_part(rs, &t, &part);
     if (t >= T) return;
     const TokenRows d = token_rows(rm, t, lane);
     if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     const u32x4* src = x + (int64_t)t * H8;
-    const int c_begin = (int)((int64_t)part * H8 / split);
-    const int c_end = (int)((int64_t)(part + 1) * H8 / split);
+    const int c_begin = part * rs.per;
+    const int c_end = min(c_begin + rs.per, H8);
 
     for (int base = c_begin; base < c_end; base += CPL * 64) {
         u32x4 v[CPL];
@@ -194,18 +187,18 @@ __device__ __forceinline__ float pow2_ceil(float t) {
 // scale and its correctly rounded reciprocal (kTensor only).
 template <int CPL, int kMode>
 __global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(
-    const u32x4* __restrict__ x, int T, int H8, int split, RowMap rm, HandleRows hr,
+    const u32x4* __restrict__ x, int T, int H8, RowSplit rs, RowMap rm, HandleRows hr,
     u32x2* __restrict__ recv_x8, void* __restrict__ recv_scales, float tensor_s, float tensor_rs) {
     const int lane = threadIdx.x & 63;
     int t, part;
-    wave_work(split, &t, &part);
+    row_part(rs, &t, &part);
     if (t >= T) return;
     const TokenRows d = token_rows(rm, t, lane);
     if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     const u32x4* src = x + (int64_t)t * H8;
-    const int G = H8 >> 4;  // blocks per row; parts hold whole blocks
-    const int c_begin = (int)((int64_t)part * G / split) * 16;
-    const int c_end = (int)((int64_t)(part + 1) * G / split) * 16;
+    const int G = H8 >> 4;  // blocks per row; parts hold whole blocks (rs counts blocks)
+    const int c_begin = part * rs.per * 16;
+    const int c_end = min(part * rs.per + rs.per, G) * 16;
 
     for (int base = c_begin; base < c_end; base += CPL * 64) {
         u32x4 v[CPL];
@@ -346,17 +339,17 @@ __global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(
 template <int CPL>
 __global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(
     const u32x4* __restrict__ codes, const uint8_t* __restrict__ scales, int T, int C16, int SB,
-    int split, RowMap rm, HandleRows hr, u32x4* __restrict__ recv,
+    RowSplit rs, RowMap rm, HandleRows hr, u32x4* __restrict__ recv,
     uint8_t* __restrict__ recv_scales) {
     const int lane = threadIdx.x & 63;
     int t, part;
-    wave_work(split, &t, &part);
+    row_part(rs, &t, &part);
     if (t >= T) return;
     const TokenRows d = token_rows(rm, t, lane);
     if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     const u32x4* src = codes + (int64_t)t * C16;
-    const int c_begin = (int)((int64_t)part * C16 / split);
-    const int c_end = (int)((int64_t)(part + 1) * C16 / split);
+    const int c_begin = part * rs.per;
+    const int c_end = min(c_begin + rs.per, C16);
     for (int base = c_begin; base < c_end; base += CPL * 64) {
         u32x4 v[CPL];
 #pragma unroll
@@ -403,7 +396,8 @@ int pick_cpl(int chunks) {
 }
 
 // Waves per token row: enough that no wave moves more than kWaveChunks chunks
-// (kWaveBlocks whole 1x128 blocks for FP8), parts of near-equal size.  Short
+// (kWaveBlocks whole 1x128 blocks for FP8); each part holds ceil(units /
+// split) units, the last one what remains (RowSplit).  Short
 // parts keep many small waves in flight (measured best for bf16 rows); the
 // FP8 pack, which also computes, does best with 128 chunks per wave.
 int pack_split(int units, int units_per_wave) {
@@ -421,14 +415,15 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
                             float* recv_topk_weights, const Launch& L) {
     const int H8 = H / 8;
     const int split = pack_split(H8, kWaveChunks);
+    const RowSplit rs = make_row_split(H8, split);
     const dim3 grid(pack_blocks(T, split)), block(kRowThreads);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x4* rx = static_cast<u32x4*>(recv_x);
-#define MOEDX_PACK(N)                                                                     \
-    return launch_kernel(pack_bf16_kernel<N>, grid, block, L, xs, T, H8, split, rm, hr, rx, \
-                         topk_idx, topk_weights, K, E, P, bucket, recv_topk_idx,            \
+#define MOEDX_PACK(N)                                                                  \
+    return launch_kernel(pack_bf16_kernel<N>, grid, block, L, xs, T, H8, rs, rm, hr, rx, \
+                         topk_idx, topk_weights, K, E, P, bucket, recv_topk_idx,         \
                          recv_topk_weights)
-    switch (pick_cpl((H8 + split - 1) / split)) {
+    switch (pick_cpl(rs.per)) {
         case 1: MOEDX_PACK(1);
         case 2: MOEDX_PACK(2);
         case 4: MOEDX_PACK(4);
@@ -445,16 +440,16 @@ hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const 
                            const Launch& L) {
     const int H8 = H / 8;
     const int split = pack_split(H8 / 16, kWaveBlocks);
+    const RowSplit rs = make_row_split(H8 / 16, split);  // in 1x128 blocks
     const dim3 grid(pack_blocks(T, split)), block(kRowThreads);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x2* rx = static_cast<u32x2*>(recv_x8);
-    const int per_part = ((H8 / 16 + split - 1) / split) * 16;  // at most 16 * kWaveBlocks
     const float trs = mode == kTensor ? 1.0f / tensor_scale : 0.0f;
-    const bool two = pick_cpl(per_part) > 1;
-#define MOEDX_PACK8(M)                                                                          \
-    return two ? launch_kernel(pack_fp8_kernel<2, M>, grid, block, L, xs, T, H8, split, rm, hr, \
-                               rx, recv_scales, tensor_scale, trs)                              \
-               : launch_kernel(pack_fp8_kernel<1, M>, grid, block, L, xs, T, H8, split, rm, hr, \
+    const bool two = pick_cpl(rs.per * 16) > 1;  // at most 16 * kWaveBlocks chunks
+#define MOEDX_PACK8(M)                                                                       \
+    return two ? launch_kernel(pack_fp8_kernel<2, M>, grid, block, L, xs, T, H8, rs, rm, hr, \
+                               rx, recv_scales, tensor_scale, trs)                           \
+               : launch_kernel(pack_fp8_kernel<1, M>, grid, block, L, xs, T, H8, rs, rm, hr, \
                                rx, recv_scales, tensor_scale, trs)
     switch (mode) {
         case kAmax: MOEDX_PACK8(kAmax);
@@ -470,15 +465,16 @@ hipError_t launch_pack_bytes(const void* codes, const void* scales, int T, int H
                              void* recv_scales, const Launch& L) {
     const int C16 = H / 16;
     const int split = pack_split(C16, kWaveChunks);
+    const RowSplit parts = make_row_split(C16, split);
     const dim3 grid(pack_blocks(T, split)), block(kRowThreads);
     const u32x4* cs = static_cast<const u32x4*>(codes);
     u32x4* rc = static_cast<u32x4*>(recv_codes);
     const uint8_t* ss = static_cast<const uint8_t*>(scales);
     uint8_t* rs = static_cast<uint8_t*>(recv_scales);
-    if (pick_cpl((C16 + split - 1) / split) > 1)
+    if (pick_cpl(parts.per) > 1)
         return launch_kernel(pack_bytes_kernel<2>, grid, block, L, cs, ss, T, C16, scale_bytes,
-                             split, rm, hr, rc, rs);
-    return launch_kernel(pack_bytes_kernel<1>, grid, block, L, cs, ss, T, C16, scale_bytes, split,
+                             parts, rm, hr, rc, rs);
+    return launch_kernel(pack_bytes_kernel<1>, grid, block, L, cs, ss, T, C16, scale_bytes, parts,
                          rm, hr, rc, rs);
 }
 
