@@ -77,7 +77,7 @@ TRAFFIC_SOURCES = {"layout": "layout.hip", "get_layout": "layout.hip", "pack": "
                    "combine_fp8_skewed": "combine.hip", "combine_reuse": "combine.hip",
                    "ll_dispatch": "ll.hip", "ll_combine": "ll.hip"}
 # headers every kernel source includes: a change there changes the kernels too
-SHARED_HEADERS = ("launch.h", "rows.h")
+SHARED_HEADERS = ("launch.h", "rows.h", "fastdiv.h")
 
 
 def source_digest(src):
