@@ -846,7 +846,8 @@ def main():
                    "ranks": R, "channels": Ch, "routing": w.routing, "recv_rows": N,
                    "mode": "capacity (no host sync)",
                    "timing": "sum over layout, pack, combine of each op's mean over back-to-back "
-                             "launches on 3 rotating buffer sets (HBM-cold), HIP events"},
+                             f"launches rotating over {NSETS} buffer sets, so that every input "
+                             "is read from HBM (not the Infinity Cache); HIP events"},
         "tokens_per_s": round(T / (ms * 1e-3), 1),
         "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
