@@ -10,11 +10,12 @@ recv_topk_idx / recv_topk_weights and the handle's send_head / recv_src_idx) +
 gate-weighted combine of the identity expert's rows, in capacity mode (no host
 synchronisation inside the step); each is one kernel launch.
 
-Timing: each op is launched back to back `--steps` times over three rotating
-buffer sets between two HIP events on its stream, so that no launch reads data
-a recent launch touched (the 256 MB Infinity Cache otherwise serves a good part
-of a just-written receive buffer); a step's time is the sum of the three
-per-op means.  The value is algorithmic bytes / step time (GB/s); tokens/s and
+Timing: each op is launched back to back `--steps` times between two HIP
+events on its stream, rotating over enough buffer sets that every launch reads
+its input from HBM: more than twice the 256 MB Infinity Cache is read between
+two reads of one set (the cache otherwise serves a good part of a just-written
+receive buffer, and keeps up to four copies of x while the pack's streaming
+stores pass); a step's time is the sum of the three per-op means.  The value is algorithmic bytes / step time (GB/s); tokens/s and
 the fraction of the 8 TB/s HBM peak are reported beside it, with whole steps
 back to back (cache-assisted, labelled as such) and the CPU oracle timed on the
 same workload as a baseline.
