@@ -120,14 +120,15 @@ size_t carve_normal(moedx_handle* h, char* base, int T, int K, int E, int R, int
     d->token_mask = cv.take<uint64_t>((size_t)T);
     d->slot_bucket = cv.take<int8_t>((size_t)T * K);
     d->num_tokens_per_rank = cv.take<int32_t>(R);
-    d->num_tokens_per_expert = cv.take<int32_t>(E);
+    // N, then the per-expert counts: exact mode reads both back with one copy
+    d->num_recv = cv.take<int32_t>(1 + (size_t)E);
+    d->num_tokens_per_expert = d->num_recv + 1;
     d->rank_prefix_matrix = cv.take<int32_t>(R);
     d->channel_prefix_matrix = cv.take<int32_t>((size_t)R * C);
     d->recv_channel_prefix_matrix = cv.take<int32_t>((size_t)R * C);
     d->group_prefix = cv.take<int32_t>((size_t)std::max(ng, 1) * R);
     d->send_head = cv.take<int32_t>((size_t)T * R);
     d->recv_src_idx = cv.take<int32_t>((size_t)std::max<int64_t>(rows, 1));
-    d->num_recv = cv.take<int32_t>(1);
     d->group_cnt = cv.take<int32_t>((size_t)std::max(ng, 1) * R);
     d->chan_part = cv.take<int32_t>((size_t)(C + 1) * R);
     d->tile_expert = cv.take<int32_t>((size_t)std::max(nt, 1) * E);
@@ -488,10 +489,8 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
     if (rc == MOEDX_OK) ctx->stats.layout_launches += 1;
     if (rc == MOEDX_OK && capacity_rows == 0) {
         // Exact mode: the host waits for N and the per-expert counts.
-        e = hipMemcpyAsync(ctx->pinned, h->num_recv, 4, hipMemcpyDeviceToHost, ex.run);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(ctx->pinned + 1, h->num_tokens_per_expert, (size_t)h->E * 4,
-                               hipMemcpyDeviceToHost, ex.run);
+        e = hipMemcpyAsync(ctx->pinned, h->num_recv, (size_t)(1 + h->E) * 4,
+                           hipMemcpyDeviceToHost, ex.run);
         if (e == hipSuccess) e = hipStreamSynchronize(ex.run);
         if (e != hipSuccess) {
             rc = hip_fail(e, "exact-mode count readback");
