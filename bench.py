@@ -608,6 +608,96 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
     return rows
 
 
+def batch_sweep(token_counts, steps, log_fn):
+    """The step (layout + pack + combine, capacity mode) of the prefill workload's
+    routing and hidden size at other batch sizes, every input read from HBM;
+    one JSON line per batch size."""
+    import torch
+
+    from combine_get_dispatch_layout_amd import Buffer
+    from combine_get_dispatch_layout_amd import _capi as C
+    from combine_get_dispatch_layout_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    ex = C.make_exec(stream.cuda_stream, None, None, C.MOEDX_ASYNC)
+    exr = ctypes.byref(ex)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    w = wl.PREFILL
+    H, K, E, R, Ch = w.hidden, w.topk, w.experts, w.ranks, w.channels
+    for T in token_counts:
+        log_fn(f"[bench] batch sweep: {T} tokens")
+        inp = wl.make_inputs(w, tokens=T)
+        buf = Buffer(E, R, num_channels=Ch, max_tokens=T)
+        cap = T * min(K, R)
+        nb = ctypes.c_size_t()
+        C.check(C.moedx_handle_workspace_bytes(buf.ctx, T, K, cap, ctypes.byref(nb)))
+        nsets = input_copies(2 * T * H)
+        idx, gw = inp.topk_idx.to(dev), inp.topk_weights.to(dev)
+        sets = []
+        for _ in range(nsets):
+            s = {"x": inp.x.to(dev), "ws": torch.empty(nb.value, dtype=torch.uint8, device=dev),
+                 "recv": torch.empty(cap, H, dtype=torch.bfloat16, device=dev),
+                 "rti": torch.empty(cap, K, dtype=torch.int64, device=dev),
+                 "rtw": torch.empty(cap, K, dtype=torch.float32, device=dev),
+                 "out": torch.empty(T, H, dtype=torch.bfloat16, device=dev)}
+            h = ctypes.c_void_p()
+            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, P(s["ws"]), nb.value, cap,
+                                             ctypes.byref(h), exr))
+            s["h"] = h
+            sets.append(s)
+
+        def op(name, i):
+            s = sets[i % nsets]
+            if name == "layout":
+                h = ctypes.c_void_p()
+                C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, P(s["ws"]), nb.value, cap,
+                                                 ctypes.byref(h), exr))
+                C.moedx_handle_destroy(h)
+            elif name == "pack":
+                C.check(C.moedx_dispatch(buf.ctx, s["h"], P(s["x"]), T, H, C.MOEDX_QUANT_NONE,
+                                         P(idx), P(gw), P(s["recv"]), None, P(s["rti"]),
+                                         P(s["rtw"]), exr))
+            else:
+                C.check(C.moedx_combine(buf.ctx, s["h"], P(s["recv"]), H, P(gw), None,
+                                        P(s["out"]), None, exr))
+
+        for i in range(nsets):
+            op("pack", i)
+        torch.cuda.synchronize()
+        dev_n = ctypes.c_void_p()
+        shape = (ctypes.c_int64 * 2)()
+        C.check(C.moedx_handle_tensor(sets[0]["h"], C.MOEDX_T_NUM_RECV, ctypes.byref(dev_n), shape))
+        off = dev_n.value - sets[0]["ws"].data_ptr()
+        N = int(sets[0]["ws"][off:off + 4].view(torch.int32).item())
+        us = {}
+        for name in ("layout", "pack", "combine"):
+            for _ in range(2):  # the first pass warms up
+                torch.sum(flush_buf, dim=(0,), out=sink)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for i in range(steps):
+                    op(name, i)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us[name] = round(a.elapsed_time(b) * 1e3 / steps, 2)
+        byts = algorithmic_bytes(T, H, K, E, R, Ch, N)
+        step_us = sum(us.values())
+        gbs = sum(byts.values()) / (step_us * 1e-6) / 1e9
+        print(json.dumps({"tokens": T, "hidden": H, "recv_rows": N, "buffer_sets": nsets,
+                          "kernels_us": us, "step_us": round(step_us, 2), "GBps": round(gbs, 1),
+                          "roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "pack_frac": round(byts["pack"] / (us["pack"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "combine_frac": round(byts["combine"] / (us["combine"] * 1e-6) / 1e9
+                                                / HBM_PEAK_GBS, 4)}), flush=True)
+        for s in sets:
+            C.moedx_handle_destroy(s["h"])
+        del sets, buf
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -618,12 +708,18 @@ def main():
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the further steps (FP8 pack, cached dispatch, standalone "
                          "layout, low-latency pair) on their own workloads")
+    ap.add_argument("--batch-sweep", type=str, default=None, metavar="T1,T2,...",
+                    help="instead of the step line, one line per batch size: the same step "
+                         "with the prefill routing and hidden size at these token counts")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the exchange (logical ranks are buckets "
               "in one HBM); runs on more than one GPU are not part of this build.",
               file=sys.stderr)
         sys.exit(2)
+    if args.batch_sweep:
+        batch_sweep([int(v) for v in args.batch_sweep.split(",")], args.steps, log)
+        return
 
     import torch
 
