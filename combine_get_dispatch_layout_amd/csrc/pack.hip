@@ -44,6 +44,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaveChunks = MOEDX_PACK_WAVE_CHUNKS;
 constexpr int kWaveBlocks = MOEDX_PACK_FP8_WAVE_BLOCKS;
+// Every kernel below moves its part of a row in one pass of CPL chunks per
+// lane; the launchers' CPL choices cover these part sizes.
+static_assert(kWaveChunks >= 1 && kWaveChunks <= 128, "bf16 / byte parts: at most 2 chunks per lane");
+static_assert(kWaveBlocks >= 1 && kWaveBlocks <= 8, "FP8 parts: at most 2 chunks per lane");
 
 template <typename V>
 __device__ __forceinline__ V load_row(const V* p) {
@@ -81,19 +85,20 @@ __global__ __launch_bounds__(kRowThreads) void pack_bf16_kernel(
     int t, part;
     row_part(rs, &t, &part);
     if (t >= T) return;
-    const TokenRows d = token_rows(rm, t, lane);
-    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     const u32x4* src = x + (int64_t)t * H8;
     const int c_begin = part * rs.per;
     const int c_end = min(c_begin + rs.per, H8);
-
-    for (int base = c_begin; base < c_end; base += CPL * 64) {
-        u32x4 v[CPL];
+    // One pass (CPL * 64 >= rs.per): the row loads go out before the row lookup.
+    u32x4 v[CPL];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = base + i * 64 + lane;
-            if (c < c_end) v[i] = load_row(src + c);
-        }
+    for (int i = 0; i < CPL; ++i) {
+        const int c = c_begin + i * 64 + lane;
+        if (c < c_end) v[i] = load_row(src + c);
+    }
+    const TokenRows d = token_rows(rm, t, lane);
+    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
+    {
+        const int base = c_begin;
         uint64_t m = d.dest;
         while (m) {
             const int r = __builtin_ctzll(m);
@@ -193,20 +198,21 @@ __global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(
     int t, part;
     row_part(rs, &t, &part);
     if (t >= T) return;
-    const TokenRows d = token_rows(rm, t, lane);
-    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     const u32x4* src = x + (int64_t)t * H8;
     const int G = H8 >> 4;  // blocks per row; parts hold whole blocks (rs counts blocks)
     const int c_begin = part * rs.per * 16;
     const int c_end = min(part * rs.per + rs.per, G) * 16;
-
-    for (int base = c_begin; base < c_end; base += CPL * 64) {
-        u32x4 v[CPL];
+    // One pass (CPL * 64 >= 16 * rs.per): the row loads go out before the row lookup.
+    u32x4 v[CPL];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = base + i * 64 + lane;
-            v[i] = c < c_end ? load_row(src + c) : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int i = 0; i < CPL; ++i) {
+        const int c = c_begin + i * 64 + lane;
+        v[i] = c < c_end ? load_row(src + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const TokenRows d = token_rows(rm, t, lane);
+    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
+    {
+        const int base = c_begin;
         u32x2 code[CPL];
         float scale[CPL];
 #pragma unroll
@@ -345,18 +351,20 @@ __global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(
     int t, part;
     row_part(rs, &t, &part);
     if (t >= T) return;
-    const TokenRows d = token_rows(rm, t, lane);
-    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     const u32x4* src = codes + (int64_t)t * C16;
     const int c_begin = part * rs.per;
     const int c_end = min(c_begin + rs.per, C16);
-    for (int base = c_begin; base < c_end; base += CPL * 64) {
-        u32x4 v[CPL];
+    // One pass (CPL * 64 >= rs.per): the row loads go out before the row lookup.
+    u32x4 v[CPL];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = base + i * 64 + lane;
-            if (c < c_end) v[i] = load_row(src + c);
-        }
+    for (int i = 0; i < CPL; ++i) {
+        const int c = c_begin + i * 64 + lane;
+        if (c < c_end) v[i] = load_row(src + c);
+    }
+    const TokenRows d = token_rows(rm, t, lane);
+    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
+    {
+        const int base = c_begin;
         uint64_t m = d.dest;
         while (m) {
             const int r = __builtin_ctzll(m);
