@@ -346,7 +346,7 @@ template <int CPL>
 __global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(
     const u32x4* __restrict__ codes, const uint8_t* __restrict__ scales, int T, int C16, int SB,
     RowSplit rs, RowMap rm, HandleRows hr, u32x4* __restrict__ recv,
-    uint8_t* __restrict__ recv_scales) {
+    uint8_t* __restrict__ recv_scales, bool words) {
     const int lane = threadIdx.x & 63;
     int t, part;
     row_part(rs, &t, &part);
@@ -378,15 +378,32 @@ __global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(
         }
     }
     if (part == 0 && scales != nullptr) {
-        for (int b0 = 0; b0 < SB; b0 += 64) {
-            const int b = b0 + lane;
-            const uint8_t sv = b < SB ? scales[(int64_t)t * SB + b] : 0;
-            uint64_t m = d.dest;
-            while (m) {
-                const int r = __builtin_ctzll(m);
-                m &= m - 1;
-                const int64_t row = __builtin_amdgcn_readlane(d.row, r);
-                if (b < SB) recv_scales[row * SB + b] = sv;
+        if (words) {  // SB % 4 == 0 and both scale arrays 4-byte aligned: 4 bytes per lane
+            const int SW = SB >> 2;
+            const uint32_t* s32 = reinterpret_cast<const uint32_t*>(scales);
+            uint32_t* r32 = reinterpret_cast<uint32_t*>(recv_scales);
+            for (int b0 = 0; b0 < SW; b0 += 64) {
+                const int b = b0 + lane;
+                const uint32_t sv = b < SW ? s32[(int64_t)t * SW + b] : 0u;
+                uint64_t m = d.dest;
+                while (m) {
+                    const int r = __builtin_ctzll(m);
+                    m &= m - 1;
+                    const int64_t row = __builtin_amdgcn_readlane(d.row, r);
+                    if (b < SW) r32[row * SW + b] = sv;
+                }
+            }
+        } else {
+            for (int b0 = 0; b0 < SB; b0 += 64) {
+                const int b = b0 + lane;
+                const uint8_t sv = b < SB ? scales[(int64_t)t * SB + b] : 0;
+                uint64_t m = d.dest;
+                while (m) {
+                    const int r = __builtin_ctzll(m);
+                    m &= m - 1;
+                    const int64_t row = __builtin_amdgcn_readlane(d.row, r);
+                    if (b < SB) recv_scales[row * SB + b] = sv;
+                }
             }
         }
     }
@@ -479,11 +496,13 @@ hipError_t launch_pack_bytes(const void* codes, const void* scales, int T, int H
     u32x4* rc = static_cast<u32x4*>(recv_codes);
     const uint8_t* ss = static_cast<const uint8_t*>(scales);
     uint8_t* rs = static_cast<uint8_t*>(recv_scales);
+    const bool words = (scale_bytes & 3) == 0 && (reinterpret_cast<uintptr_t>(ss) & 3u) == 0 &&
+                       (reinterpret_cast<uintptr_t>(rs) & 3u) == 0;
     if (pick_cpl(parts.per) > 1)
         return launch_kernel(pack_bytes_kernel<2>, grid, block, L, cs, ss, T, C16, scale_bytes,
-                             parts, rm, hr, rc, rs);
+                             parts, rm, hr, rc, rs, words);
     return launch_kernel(pack_bytes_kernel<1>, grid, block, L, cs, ss, T, C16, scale_bytes, parts,
-                         rm, hr, rc, rs);
+                         rm, hr, rc, rs, words);
 }
 
 }  // namespace moedx

@@ -146,6 +146,38 @@ def test_prequantized_pass_through(oracle, fmt):
         assert_equal("scales", got, oracle.pack_rows_bytes(sc, ref.prefix))
 
 
+@pytest.mark.parametrize("case", ["5_blocks", "unaligned"])
+def test_prequantized_scale_rows_copied_bytewise(oracle, case):
+    """UE8M0 scale rows whose length is not a multiple of 4 bytes (H = 640: 5
+    blocks), or whose array starts off a 4-byte boundary, take the byte-wise
+    copy; the result is the same pass-through."""
+    dev = device()
+    T, E, R, C, K = 300, 32, 4, 3, 4
+    H = 640 if case == "5_blocks" else 1024
+    rng = np.random.default_rng(43)
+    idx = wl.random_routing(rng, T, E, K, p_empty=0.1)
+    codes = rng.integers(0, 256, (T, H), dtype=np.uint8)
+    G = H // 128
+    sc = rng.integers(0, 256, (T, G), dtype=np.uint8)
+    inp = wl.Inputs(torch.zeros(T, H, dtype=torch.bfloat16), torch.from_numpy(idx),
+                    torch.full((T, K), 0.25))
+    ref = oracle_first_dispatch(oracle, inp, E, R, C, with_rows=False)
+    buf = make_buffer(E, R, C, T)
+    if case == "unaligned":  # a view one byte into a larger allocation
+        big = torch.zeros(T * G + 1, dtype=torch.uint8, device=dev)
+        big[1:] = torch.from_numpy(sc.reshape(-1)).to(dev)
+        sc_dev = big[1:].view(T, G)
+        assert sc_dev.data_ptr() % 4 != 0
+    else:
+        sc_dev = torch.from_numpy(sc).to(dev)
+    print(f"[prequant bytes {case}]", flush=True)
+    (rc, rs), *_ = buf.dispatch((torch.from_numpy(codes).to(dev), sc_dev),
+                                topk_idx=inp.topk_idx.to(dev), use_ue8m0=True)
+    N = ref.prefix.num_recv
+    assert_equal("codes", np_(rc)[:N], oracle.pack_rows_bytes(codes, ref.prefix))
+    assert_equal("scales", np_(rs)[:N].reshape(N, -1), oracle.pack_rows_bytes(sc, ref.prefix))
+
+
 def test_prequantized_equals_quantising_dispatch(oracle):
     """Quantise on the GPU, then dispatch the (codes, scales) pair: the same rows."""
     dev = device()
