@@ -32,7 +32,7 @@
 #define MOEDX_PACK_NT_LOAD 0  // streaming (non-temporal) loads of x
 #endif
 #ifndef MOEDX_PACK_NT_STORE
-#define MOEDX_PACK_NT_STORE 1  // streaming (non-temporal) stores of receive rows
+#define MOEDX_PACK_NT_STORE 1  // streaming, write-through stores of receive rows
 #endif
 
 namespace moedx {
@@ -58,10 +58,15 @@ __device__ __forceinline__ V load_row(const V* p) {
 #endif
 }
 
-template <typename V>
-__device__ __forceinline__ void store_row(V v, V* p) {
+// 16-byte receive-row stores: streaming (nt) and written through to memory at
+// system scope (sc0 sc1), which measured about 1 us faster than plain
+// non-temporal stores on the 4096 x 7168 bf16 pack and about 2 us on the
+// 16384 x 4096 cached dispatch (FP8: no difference).  No builtin sets sc0 /
+// sc1 on a store, so this is one vector store in inline assembly; it returns
+// nothing, so no wait counter is involved.
+__device__ __forceinline__ void store_row(u32x4 v, u32x4* p) {
 #if MOEDX_PACK_NT_STORE
-    __builtin_nontemporal_store(v, p);
+    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt" : : "v"(p), "v"(v) : "memory");
 #else
     *p = v;
 #endif
