@@ -13,7 +13,8 @@
 // token's rows itself (rows.h: one ballot per destination bucket), reads its
 // part of the row once with 16-byte loads, all of a lane's chunks in flight
 // before the first store, then writes it to each destination row with
-// non-temporal 16-byte stores; destination rows are wave-uniform scalars.
+// streaming write-through 16-byte stores; destination rows are wave-uniform
+// scalars.
 // Positions are a function of the routing only, so the launch shape never
 // changes a result.
 #include <hip/hip_runtime.h>
