@@ -32,6 +32,40 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+# Releases that must wait until no stream capture is running.  Destroying a
+# context synchronises its stream and frees device and pinned memory, and an
+# event destroy is not a capturable call either; any of them during a capture
+# invalidates the graph being recorded.  A finalizer can run at any point (the
+# garbage collector may collect an old Buffer in the middle of someone else's
+# capture), so while the current stream is capturing the release is queued and
+# done by the next call that runs outside a capture.
+_deferred: list = []
+
+
+def _capturing() -> bool:
+    try:
+        return torch.cuda.is_available() and torch.cuda.is_current_stream_capturing()
+    except Exception:  # interpreter shutdown: torch may already be gone
+        return False
+
+
+def _flush_deferred(_deferred=_deferred, _capturing=_capturing) -> None:
+    while _deferred and not _capturing():
+        fn, ptr = _deferred.pop()
+        fn(ptr)
+
+
+# Finalizers reach these through default arguments and class attributes: at
+# interpreter exit the module's globals may already be gone.
+def _release(fn, ptr, _deferred=_deferred, _capturing=_capturing,
+             _flush=_flush_deferred) -> None:
+    if _capturing():
+        _deferred.append((fn, ptr))
+        return
+    fn(ptr)
+    _flush()
+
+
 class EventOverlap:
     """Owns one library event.  ``event is None`` means "already complete"
     (what a call with async_finish=False hands back, for tuple arity)."""
@@ -55,10 +89,11 @@ class EventOverlap:
 
     # Held by the class: at interpreter exit module globals may already be gone.
     _destroy = staticmethod(C.moedx_event_destroy)
+    _release = staticmethod(_release)
 
     def __del__(self):
         if getattr(self, "event", None) is not None:
-            self._destroy(self.event)
+            self._release(self._destroy, self.event)
             self.event = None
 
 
@@ -136,20 +171,24 @@ class Buffer:
         self.device = torch.cuda.current_device() if device is None else device
         self.num_experts, self.num_ranks, self.num_channels = num_experts, num_ranks, num_channels
         self.max_tokens = max_tokens
+        _flush_deferred()
         ctx = ctypes.c_void_p()
         C.check(C.moedx_create(ctypes.byref(ctx), self.device, num_experts, num_ranks,
                                num_channels, max_tokens, 0))
         self.ctx = ctx.value
 
     _destroy = staticmethod(C.moedx_destroy)
+    _release = staticmethod(_release)
 
     def __del__(self):
         if getattr(self, "ctx", None):
-            self._destroy(self.ctx)
+            self._release(self._destroy, self.ctx)
             self.ctx = None
 
     # -- plumbing ---------------------------------------------------------------
     def _exec(self, previous_event, async_finish, allocate_on_comm_stream, no_sync=False):
+        if _deferred:
+            _flush_deferred()
         done = ctypes.c_void_p() if async_finish else None
         flags = (C.MOEDX_ON_CTX_STREAM if allocate_on_comm_stream else 0) | (
             C.MOEDX_ASYNC if no_sync else 0)

@@ -70,3 +70,20 @@ def test_null_arguments_are_rejected(capi):
     assert capi.moedx_destroy(None) == capi.MOEDX_OK
     assert capi.moedx_handle_destroy(None) == capi.MOEDX_OK
     assert capi.moedx_event_destroy(None) == capi.MOEDX_OK
+
+
+def test_releases_wait_for_the_end_of_a_capture():
+    """Finalizer releases queue while a stream capture runs and happen at the
+    next release or call outside a capture, most recent first."""
+    from combine_get_dispatch_layout_amd import buffer as bm
+
+    done = []
+    assert not bm._deferred
+    bm._release(done.append, 1, _capturing=lambda: True)
+    bm._release(done.append, 2, _capturing=lambda: True)
+    assert done == [] and len(bm._deferred) == 2
+    bm._flush_deferred(_capturing=lambda: True)  # still capturing: nothing happens
+    assert done == []
+    bm._release(done.append, 3, _capturing=lambda: False,
+                _flush=lambda: bm._flush_deferred(_capturing=lambda: False))
+    assert done == [3, 2, 1] and not bm._deferred

@@ -147,3 +147,51 @@ def test_two_contexts_on_concurrent_streams(oracle):
         for inp, (h, recv, rti, rtw, out) in zip(inps, outs):
             print(f"[streams] rep {rep}", flush=True)
             _check(oracle, inp, h, recv, rti, rtw, out)
+
+
+def test_release_inside_capture_is_deferred(oracle):
+    """A context and an event released while a stream is capturing (here by
+    the garbage collector, as happens when an old Buffer is collected during
+    someone else's capture) are destroyed after the capture ends; the graph
+    recorded meanwhile stays valid and replays correctly."""
+    import gc
+
+    from combine_get_dispatch_layout_amd import buffer as bm
+
+    dev = device()
+    T, H = 300, 512
+    cap = T * min(K, R)
+    buf = make_buffer(E, R, C, T)
+    doomed = make_buffer(E, R, C, T)
+    first = _inputs(21, T, H)
+    x_s, idx_s, w_s = first.x.to(dev), first.topk_idx.to(dev), first.topk_weights.to(dev)
+    _, _, _, _, _, ev = doomed.dispatch(x_s, topk_idx=idx_s, topk_weights=w_s,
+                                        num_worst_tokens=cap, async_finish=True)
+    ev.synchronize()
+    buf.dispatch(x_s, topk_idx=idx_s, topk_weights=w_s, num_worst_tokens=cap, no_sync=True)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            recv, rti, rtw, _, h, _ = buf.dispatch(x_s, topk_idx=idx_s, topk_weights=w_s,
+                                                   num_worst_tokens=cap, no_sync=True)
+            del doomed, ev
+            gc.collect()
+            assert len(bm._deferred) >= 2, "ctx and event release not deferred"
+            out, _, _ = buf.combine(recv, h, gate_weights=w_s, no_sync=True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        inp = _inputs(22 + rep, T, H)
+        x_s.copy_(inp.x.to(dev))
+        idx_s.copy_(inp.topk_idx.to(dev))
+        w_s.copy_(inp.topk_weights.to(dev))
+        print(f"[graph] release-in-capture replay {rep}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        _check(oracle, inp, h, recv, rti, rtw, out)
+        # the next call outside a capture performs the queued releases
+        buf.get_dispatch_layout(idx_s, E)
+        assert not bm._deferred
