@@ -8,17 +8,24 @@
 // on the row data: rank_prefix_matrix, channel_prefix_matrix and
 // recv_channel_prefix_matrix, all on the device (no host prefix sum).
 //
-// Each workgroup takes a tile of 256 tokens, one per lane.  Bucket membership
-// of a wave's 64 tokens (a "group") is one 64-bit ballot per bucket, so group
-// counts, and the counts from a group's start to any channel boundary inside
-// it, are popcounts of registers the wave already holds; expert counts go
-// through an LDS histogram.  The last workgroup to finish (an atomic ticket;
-// no workgroup ever waits on another) turns the group counts into exclusive
-// per-bucket prefixes with wave shuffles, and derives the bucket totals and
-// offsets, the expert totals and the channel prefixes.  A receive position is
-// then base[r] + group_prefix[g][r] + a popcount inside the group, which the
+// Phase 1 (layout_tile): a workgroup takes a tile of 256 tokens, one per lane.
+// Bucket membership of a wave's 64 tokens (a "group") is one 64-bit ballot per
+// bucket, so group counts, and the counts from a group's start to any channel
+// boundary inside it, are popcounts of registers the wave already holds;
+// expert counts go through an LDS histogram.  The partials are published with
+// a release fence and an atomic ticket; no workgroup ever waits on another.
+// Phase 2 (layout_finish), run by the workgroup that takes the last ticket:
+// the group counts become exclusive per-bucket prefixes, and the bucket totals
+// and offsets, expert totals and channel prefixes follow.  A receive position
+// is then base[r] + group_prefix[g][r] + a popcount inside the group, which the
 // pack and combine kernels evaluate for themselves.  Every value is a pure
 // function of the routing; no atomic decides an order.
+//
+// The launch is one chain of dependent steps (the topk loads, the partials'
+// stores and fence, the ticket, the finishing workgroup's loads) run by
+// workgroups that each have a SIMD to themselves, so its time is latency:
+// loads are issued together before their first use, and the finishing step at
+// the usual sizes is straight-line code.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,57 +35,146 @@ namespace moedx {
 
 namespace {
 
-constexpr int kWaves = kTile / 64;
-constexpr int kPerThread = 16;  // groups per finishing thread per pass
-constexpr int kBatch = 16;      // loads issued together for the expert totals
+constexpr int kLayoutWaves = kTile / 64;
+
 constexpr int kLdsGroups = 8192;  // LDS slots for group prefixes (32 KB)
 constexpr int kLdsChan = 2048;    // LDS slots for channel-boundary partials (8 KB)
 
+// LDS of the layout workgroup.  gp and chan stage the group prefixes and the
+// channel-boundary partials for the general finishing step when they fit.
+struct LayoutShared {
+    int32_t hist[kMaxExperts];
+    int32_t gp[kLdsGroups];
+    int32_t chan[kLdsChan];
+    int32_t total[kMaxRanks];
+    int32_t base[kMaxRanks];
+    int32_t fgp[kGroup * kMaxRanks];  // group prefixes of the fast finishing step
+    unsigned int ticket;
+};
+
+// A raw buffer over n 32-bit words.  A buffer load checks its offset against
+// the buffer's size in hardware and returns 0 past the end without touching
+// memory, so a batch of such loads needs no branch and all of it can be in
+// flight at once.  (The resource's last word is the
+// gfx9-family raw-buffer format.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t word_buffer(const int32_t* p, int n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p), (short)0, n * 4,
+                                             0x00020000);
+}
+// Word i of a word_buffer; kNoWord (or any index past the end) reads 0.
+constexpr unsigned int kNoWord = 0x20000000u;  // 2 GiB in: past every buffer here
+__device__ __forceinline__ int32_t load_word(__amdgpu_buffer_rsrc_t r, unsigned int i) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)(i * 4u), 0, 0);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// inside each row of 16 lanes, then the last lane of row 0 (row 2) is added to
+// row 1 (row 3) and the last lane of row 1 to rows 2 and 3.
+__device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
 // Channel c starts at token b_c = min(c * per, T), c = 0..C (b_C = T).
-__device__ __forceinline__ int64_t boundary(int c, int per, int T) {
+__device__ __forceinline__ int64_t layout_boundary(int c, int per, int T) {
     const int64_t b = (int64_t)c * per;
     return b < T ? b : T;
 }
 
-__global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
-    __shared__ int32_t hist[kMaxExperts];
-    __shared__ int32_t s_gp[kLdsGroups];   // group prefixes, when ng * R fits
-    __shared__ int32_t s_chan[kLdsChan];   // channel-boundary partials, when (C+1) * R fits
-    __shared__ int32_t s_total[kMaxRanks];
-    __shared__ int32_t s_base[kMaxRanks];
-    __shared__ unsigned int s_ticket;
+// What a tile's thread keeps of its token for the per-token outputs: the
+// bucket mask and the bucket of every slot, four per word (0xFF: empty slot).
+struct TileToken {
+    uint64_t mask;
+    uint32_t sb[kMaxTopk / 4];
+};
+
+// Per-token outputs of token t (t < T): is_token_in_rank, the token mask and
+// the slot buckets.
+__device__ __forceinline__ void layout_token_outputs(const LayoutArgs& a, int t,
+                                                     const TileToken& tk) {
+    const int R = a.R, K = a.K;
+    const uint64_t mask = tk.mask;
+    uint8_t* out = a.is_token_in_rank + (int64_t)t * R;
+    if ((R & 3) == 0) {
+        for (int r = 0; r < R; r += 4)
+            *reinterpret_cast<uint32_t*>(out + r) =
+                (uint32_t)((mask >> r) & 1u) | ((uint32_t)((mask >> (r + 1)) & 1u) << 8) |
+                ((uint32_t)((mask >> (r + 2)) & 1u) << 16) |
+                ((uint32_t)((mask >> (r + 3)) & 1u) << 24);
+    } else {
+        for (int r = 0; r < R; ++r) out[r] = (uint8_t)((mask >> r) & 1u);
+    }
+    if (a.token_mask) a.token_mask[t] = mask;
+    if (a.slot_bucket) {
+        int8_t* sbo = a.slot_bucket + (int64_t)t * K;
+        if ((K & 3) == 0) {  // t * K is a multiple of 4: whole words
+#pragma unroll
+            for (int w = 0; w < kMaxTopk / 4; ++w)
+                if (4 * w < K) reinterpret_cast<uint32_t*>(sbo)[w] = tk.sb[w];
+        } else {
+#pragma unroll
+            for (int k = 0; k < kMaxTopk; ++k)
+                if (k < K) sbo[k] = (int8_t)(tk.sb[k >> 2] >> (8 * (k & 3)));
+        }
+    }
+}
+
+// Phase 1 for tile `tile` of `ntiles`.  Returns true in the workgroup that took
+// the last ticket (workgroup-uniform), which must then run layout_finish and,
+// after it, layout_token_outputs for its own tokens (*tk; the other workgroups
+// have written theirs when this returns).
+__device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int ntiles,
+                                            LayoutShared& s, TileToken* tk) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int T = a.T, K = a.K, E = a.E, R = a.R;
     const bool with_channels = a.channel_prefix_matrix != nullptr;
 
-    // ---- phase 1: this tile's tokens ----------------------------------------
     // The small partials the finishing workgroup reads are stored first and
     // published (fence + ticket) before the large per-token outputs, so the
     // fence only waits for them.
-    const int t = blockIdx.x * kTile + tid;
+    const int t = tile * kTile + tid;
     uint64_t mask = 0;
-    int64_t ids[kMaxTopk];
+    tk->mask = 0;
+#pragma unroll
+    for (int w = 0; w < kMaxTopk / 4; ++w) tk->sb[w] = 0xffffffffu;
     if (T > 0) {
-        for (int e = tid; e < E; e += kTile) hist[e] = 0;
+        for (int e = tid; e < E; e += kTile) s.hist[e] = 0;
         __syncthreads();
         if (t < T) {
+            // Every slot load is issued before the first is used (one memory
+            // round trip); slots past K re-read slot K - 1 and are ignored.
             const int64_t* row = a.topk_idx + (int64_t)t * K;
+            int64_t ids[kMaxTopk];
+            if (K <= kMaxTopk / 2) {
 #pragma unroll
-            for (int k = 0; k < kMaxTopk; ++k) ids[k] = (k < K) ? row[k] : -1;
+                for (int k = 0; k < kMaxTopk / 2; ++k) ids[k] = row[k < K ? k : K - 1];
+#pragma unroll
+                for (int k = kMaxTopk / 2; k < kMaxTopk; ++k) ids[k] = -1;
+            } else {
+#pragma unroll
+                for (int k = 0; k < kMaxTopk; ++k) ids[k] = row[k < K ? k : K - 1];
+            }
 #pragma unroll
             for (int k = 0; k < kMaxTopk; ++k) {
-                if (k >= K) break;
                 const int64_t e = ids[k];
-                if (e >= 0 && e < E) {  // ids outside [0, E) are treated as empty slots
-                    mask |= 1ull << a.bucket.of((int)e);
-                    atomicAdd(&hist[(int)e], 1);
+                if (k < K && e >= 0 && e < E) {  // ids outside [0, E) are empty slots
+                    const int b = a.bucket.of((int)e);
+                    mask |= 1ull << b;
+                    tk->sb[k >> 2] ^= (uint32_t)(0xff ^ b) << (8 * (k & 3));
+                    atomicAdd(&s.hist[(int)e], 1);
                 }
             }
+            tk->mask = mask;
         }
         // Group (one wave = 64 tokens) counts of every bucket; lane r keeps bucket r.
-        const int g = blockIdx.x * kWaves + wave;
+        const int g = tile * kLayoutWaves + wave;
         const int g_begin = g * kGroup;
         if (g_begin < T) {
             int32_t my_cnt = 0;
@@ -91,7 +187,7 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
             if (with_channels) {
                 int c = (int)((g_begin + a.per - 1) / a.per);
                 for (; c <= a.C; ++c) {
-                    const int64_t b = boundary(c, a.per, T);
+                    const int64_t b = layout_boundary(c, a.per, T);
                     if (b >= T || b >= g_begin + kGroup) break;
                     const int off = (int)(b - g_begin);
                     const uint64_t below = off == 0 ? 0ull : (~0ull >> (64 - off));
@@ -105,53 +201,188 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
             }
         }
         __syncthreads();
-        for (int e = tid; e < E; e += kTile) a.tile_expert[(int64_t)blockIdx.x * E + e] = hist[e];
+        for (int e = tid; e < E; e += kTile) a.tile_expert[(int64_t)tile * E + e] = s.hist[e];
     }
-
-    // ---- phase 2: publish the partials; the last workgroup finishes the job ----
     // Release at device scope: the partials are visible to every XCD's L2
     // before the ticket moves.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
-    if (tid == 0) s_ticket = atomicAdd(a.ticket, 1u);
+    if (tid == 0) s.ticket = atomicAdd(a.ticket, 1u);
+    __syncthreads();
+    const bool last = s.ticket == (unsigned int)(ntiles - 1);
+    // The per-token outputs (not read by the finishing step, which the last
+    // workgroup runs before writing its own, so that its acquire does not wait
+    // for these stores).
+    if (!last && t < T) layout_token_outputs(a, t, *tk);
+    return last;
+}
 
-    // The per-token outputs (not read by the finishing step).
-    if (t < T) {
-        uint8_t* out = a.is_token_in_rank + (int64_t)t * R;
-        if ((R & 3) == 0) {
-            for (int r = 0; r < R; r += 4)
-                *reinterpret_cast<uint32_t*>(out + r) =
-                    (uint32_t)((mask >> r) & 1u) | ((uint32_t)((mask >> (r + 1)) & 1u) << 8) |
-                    ((uint32_t)((mask >> (r + 2)) & 1u) << 16) |
-                    ((uint32_t)((mask >> (r + 3)) & 1u) << 24);
-        } else {
-            for (int r = 0; r < R; ++r) out[r] = (uint8_t)((mask >> r) & 1u);
-        }
-        if (a.token_mask) a.token_mask[t] = mask;
-        if (a.slot_bucket) {
+// Sizes the fast finishing step covers: every group of a bucket in one wave
+// (T <= 4096), at most 16 tiles of expert partials per expert, and at most two
+// channel boundaries (of one bucket each) per thread.
+__device__ __forceinline__ bool layout_fast_finish_fits(const LayoutArgs& a, int ntiles) {
+    const int nb = a.channel_prefix_matrix != nullptr ? (a.C + 1) * a.R : 0;
+    return a.T > 0 && num_groups(a.T) <= 64 && ntiles <= 16 && nb <= 2 * kTile;
+}
+
+// Phase 2 for the sizes layout_fast_finish_fits admits: every load is issued
+// before the first is used (one memory round trip), and the scan is branch-free:
+// wave w takes buckets w, w + 4, ..., lane g holding group g, and one wave
+// prefix sum per bucket gives every group prefix and the bucket total.
+__device__ __forceinline__ void layout_finish_fast(const LayoutArgs& a, int ntiles,
+                                                   LayoutShared& s) {
+    constexpr int kBuckets = kMaxRanks / kLayoutWaves;  // buckets per wave, at most
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = a.T, E = a.E, R = a.R;
+    const int ng = num_groups(T);
+    const int nb = a.channel_prefix_matrix != nullptr ? (a.C + 1) * R : 0;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+    // Indices first, then every load.
+    const bool g_lane = lane < ng;
+    const __amdgpu_buffer_rsrc_t gc = word_buffer(a.group_cnt, ng * R);
+    const __amdgpu_buffer_rsrc_t te = word_buffer(a.tile_expert, ntiles * E);
+    const __amdgpu_buffer_rsrc_t cp = word_buffer(a.chan_part, nb);
+    const unsigned int gbase = g_lane ? (unsigned int)(lane * R + wave) : kNoWord;
+    const unsigned int ebase = tid < E ? (unsigned int)tid : kNoWord;
+    int32_t cnt[kBuckets], ev[16], cv[2];
 #pragma unroll
-            for (int k = 0; k < kMaxTopk; ++k) {
-                if (k >= K) break;
-                const int64_t e = ids[k];
-                a.slot_bucket[(int64_t)t * K + k] =
-                    (e >= 0 && e < E) ? (int8_t)a.bucket.of((int)e) : (int8_t)-1;
-            }
-        }
+    for (int i = 0; i < kBuckets; ++i)  // bucket wave + 4i; past R: past the buffer's end
+        cnt[i] = load_word(gc, wave + 4 * i < R ? gbase + (unsigned int)(4 * i) : kNoWord);
+#pragma unroll
+    for (int u = 0; u < 16; ++u)  // tiles past ntiles lie past the buffer's end
+        ev[u] = load_word(te, ebase + (unsigned int)(u * E));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) cv[q] = load_word(cp, (unsigned int)(tid + q * kTile));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Group prefixes and bucket totals.
+#pragma unroll
+    for (int i = 0; i < kBuckets; ++i) {
+        const int r = wave + 4 * i;
+        if (r >= R) break;  // wave-uniform
+        const int32_t incl = wave_inclusive_sum(cnt[i]);
+        const int32_t excl = incl - cnt[i];
+        s.fgp[lane * R + r] = excl;
+        if (g_lane && a.group_prefix) a.group_prefix[(int64_t)lane * R + r] = excl;
+        if (lane == 63) s.total[r] = incl;
+    }
+    // Expert totals (E <= 256 here in one pass; more experts in further passes).
+    int32_t esum = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) esum += ev[u];
+    if (tid < E) a.num_tokens_per_expert[tid] = esum;
+    for (int e = tid + kTile; e < E; e += kTile) {
+        int32_t v = 0;
+        for (int j = 0; j < ntiles; ++j) v += a.tile_expert[(int64_t)j * E + e];
+        a.num_tokens_per_expert[e] = v;
     }
     __syncthreads();
-    if (s_ticket != gridDim.x - 1) return;
+    // Bucket offsets: one wave prefix sum over the bucket totals.
+    if (wave == 0) {
+        const int32_t tot = lane < R ? s.total[lane] : 0;
+        const int32_t incl = wave_inclusive_sum(tot);
+        if (lane < R) {
+            a.num_tokens_per_rank[lane] = tot;
+            if (a.rank_prefix_matrix) a.rank_prefix_matrix[lane] = incl;
+            if (a.num_recv && lane == R - 1) *a.num_recv = incl;
+        }
+    }
+    // Channel prefixes: excl(b, r) = group prefix of b's group + count from the
+    // group start to b (the bucket total for b = T).
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i = tid + q * kTile;
+        if (i < nb) {
+            const int c = i / R, r = i - (i / R) * R;
+            const int64_t b = layout_boundary(c, a.per, T);
+            const int32_t val = b >= T ? s.total[r] : s.fgp[(int)(b / kGroup) * R + r] + cv[q];
+            if (c < a.C) a.recv_channel_prefix_matrix[r * a.C + c] = val;
+            if (c > 0) a.channel_prefix_matrix[r * a.C + c - 1] = val;
+        }
+    }
+    if (tid == 0) atomicExch(a.ticket, 0u);
+}
+
+// Phase 2, in the workgroup that took the last ticket of `ntiles` tiles.
+__device__ __forceinline__ void layout_finish(const LayoutArgs& a, int ntiles, LayoutShared& s) {
+    if (layout_fast_finish_fits(a, ntiles)) {
+        layout_finish_fast(a, ntiles, s);
+        return;
+    }
+    constexpr int kPerThread = 16;  // groups per finishing thread per pass
+    constexpr int kBatch = 16;      // loads issued together for the expert totals
+    const int tid = threadIdx.x;
+    const int T = a.T, E = a.E, R = a.R;
+    const bool with_channels = a.channel_prefix_matrix != nullptr;
     // Acquire: drop stale lines before reading the other workgroups' partials.
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     const int ng = num_groups(T);
-    const int nt = T > 0 ? (int)gridDim.x : 0;
+    const int nt = T > 0 ? ntiles : 0;
 
-    // Expert totals: issue these loads first; they overlap the group scan.
+    // The first pass of every partial sum below loads its values before any
+    // is used, so that at the usual sizes (at most 16 tiles, 1024 groups and
+    // 256 channel boundaries) all of them take one memory round trip.  These
+    // are buffer loads (word_buffer): out-of-range indices read 0, so none
+    // waits behind a branch.  Every index is computed before the first load.
+    // Expert totals: thread i < E * per_e sums the partials of expert i % E
+    // from tiles i / E + u * per_e.
     const int per_e = E >= kTile ? 1 : kTile / E;
+    const bool e_thread = tid < E * per_e;
+    const int e0 = e_thread ? tid % E : 0, part0 = tid / E;
+    const unsigned int ebase = e_thread ? (unsigned int)(part0 * E + e0) : kNoWord;
+    // Channel-boundary partial counts (written in phase 1), staged in LDS.
+    const int nb = with_channels ? (a.C + 1) * R : 0;
+    const bool cp_in_lds = nb <= kLdsChan;
+    // Exclusive prefix over groups per bucket.  Bucket r owns L consecutive
+    // lanes of one wave (L a power of two, L * R <= 256); each lane takes G
+    // consecutive groups per pass and the L lanes combine their sums with a
+    // shuffle scan.  Prefixes also go to LDS when they fit, for the channel step.
+    int L = 64;
+    while (L * R > kTile) L >>= 1;
+    int G = (ng + L - 1) / L;
+    if (G > kPerThread) G = kPerThread;
+    if (G < 1) G = 1;
+    const bool gp_in_lds = ng * R <= kLdsGroups;
+    const bool scan_thread = tid < L * R;
+    const int sr = tid / L, sj = tid % L;
+    const unsigned int gbase = scan_thread ? (unsigned int)(sj * G * R + sr) : kNoWord;
+
+    const __amdgpu_buffer_rsrc_t te = word_buffer(a.tile_expert, nt * E);
+    int32_t ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)  // tiles past nt lie past the buffer's end
+        ev[u] = load_word(te, ebase + (unsigned int)(u * per_e * E));
+    int32_t cv = 0;
+    if (cp_in_lds && nb > 0) cv = load_word(word_buffer(a.chan_part, nb), (unsigned int)tid);
+    const __amdgpu_buffer_rsrc_t gc = word_buffer(a.group_cnt, ng * R);
+    int32_t gv[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u)  // groups past ng lie past the buffer's end
+        gv[u] = load_word(gc, gbase + (unsigned int)(u * R));
+    // Keep every use below the last of these loads: all of them are in flight
+    // before the first wait.
+    __builtin_amdgcn_sched_barrier(0);
+
     int32_t esum[kMaxExperts / kTile];  // one partial per expert this thread sums
 #pragma unroll
-    for (int q = 0; q < kMaxExperts / kTile; ++q) {
-        esum[q] = 0;
+    for (int q = 0; q < kMaxExperts / kTile; ++q) esum[q] = 0;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) esum[0] += ev[u];
+    if (e_thread)  // tiles past the first pass
+        for (int j = part0 + per_e * kBatch; j < nt; j += per_e * kBatch) {
+            int32_t v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int jj = j + u * per_e;
+                v[u] = jj < nt ? a.tile_expert[(int64_t)jj * E + e0] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) esum[0] += v[u];
+        }
+#pragma unroll
+    for (int q = 1; q < kMaxExperts / kTile; ++q) {  // E > 256 only
         const int i = tid + q * kTile;
         if (i >= E * per_e) continue;
         const int e = i % E, part = i / E;
@@ -166,25 +397,11 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
             for (int u = 0; u < kBatch; ++u) esum[q] += v[u];
         }
     }
+    if (cp_in_lds) {
+        if (tid < nb) s.chan[tid] = cv;
+        for (int i = tid + kTile; i < nb; i += kTile) s.chan[i] = a.chan_part[i];
+    }
 
-    // Channel-boundary partial counts (written in phase 1) staged in LDS.
-    const int nb = with_channels ? (a.C + 1) * R : 0;
-    const bool cp_in_lds = nb <= kLdsChan;
-    if (cp_in_lds)
-        for (int i = tid; i < nb; i += kTile) s_chan[i] = a.chan_part[i];
-
-    // Exclusive prefix over groups per bucket.  Bucket r owns L consecutive
-    // lanes of one wave (L a power of two, L * R <= 256); each lane takes G
-    // consecutive groups per pass and the L lanes combine their sums with a
-    // shuffle scan.  Prefixes also go to LDS when they fit, for the channel step.
-    int L = 64;
-    while (L * R > kTile) L >>= 1;
-    int G = (ng + L - 1) / L;
-    if (G > kPerThread) G = kPerThread;
-    if (G < 1) G = 1;
-    const bool gp_in_lds = ng * R <= kLdsGroups;
-    const bool scan_thread = tid < L * R;
-    const int sr = tid / L, sj = tid % L;
     int32_t carry = 0;
     if (scan_thread) {
         for (int pass = 0; pass < ng; pass += L * G) {
@@ -192,7 +409,8 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
             int32_t v[kPerThread];
 #pragma unroll
             for (int u = 0; u < kPerThread; ++u)
-                v[u] = (u < G && g0 + u < ng) ? a.group_cnt[(int64_t)(g0 + u) * R + sr] : 0;
+                v[u] = pass == 0 ? (u < G ? gv[u] : 0)
+                       : (u < G && g0 + u < ng) ? a.group_cnt[(int64_t)(g0 + u) * R + sr] : 0;
             int32_t mine = 0;
 #pragma unroll
             for (int u = 0; u < kPerThread; ++u) mine += v[u];
@@ -207,51 +425,51 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
                 const int gg = g0 + u;
                 if (u < G && gg < ng) {
                     if (a.group_prefix) a.group_prefix[(int64_t)gg * R + sr] = run;
-                    if (gp_in_lds) s_gp[gg * R + sr] = run;
+                    if (gp_in_lds) s.gp[gg * R + sr] = run;
                 }
                 run += v[u];
             }
             carry += __shfl(incl, L - 1, L);
         }
-        if (sj == 0) s_total[sr] = carry;
+        if (sj == 0) s.total[sr] = carry;
     }
     // Expert partials meet in LDS.
-    for (int e = tid; e < E; e += kTile) hist[e] = 0;
+    for (int e = tid; e < E; e += kTile) s.hist[e] = 0;
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < kMaxExperts / kTile; ++q) {
         const int i = tid + q * kTile;
         if (i < E * per_e) {
-            if (per_e == 1) hist[i] = esum[q];
-            else atomicAdd(&hist[i % E], esum[q]);
+            if (per_e == 1) s.hist[i] = esum[q];
+            else atomicAdd(&s.hist[i % E], esum[q]);
         }
     }
     if (tid == 0) {
         int32_t run = 0;
         for (int r = 0; r < R; ++r) {
-            s_base[r] = run;
-            run += s_total[r];
+            s.base[r] = run;
+            run += s.total[r];
         }
     }
     __syncthreads();
     if (tid < R) {
-        a.num_tokens_per_rank[tid] = s_total[tid];
-        if (a.rank_prefix_matrix) a.rank_prefix_matrix[tid] = s_base[tid] + s_total[tid];
-        if (a.num_recv && tid == R - 1) *a.num_recv = s_base[tid] + s_total[tid];
+        a.num_tokens_per_rank[tid] = s.total[tid];
+        if (a.rank_prefix_matrix) a.rank_prefix_matrix[tid] = s.base[tid] + s.total[tid];
+        if (a.num_recv && tid == R - 1) *a.num_recv = s.base[tid] + s.total[tid];
     }
-    for (int e = tid; e < E; e += kTile) a.num_tokens_per_expert[e] = hist[e];
+    for (int e = tid; e < E; e += kTile) a.num_tokens_per_expert[e] = s.hist[e];
     // Channel prefixes, one (boundary, bucket) pair per thread:
     // excl(b, r) = group_prefix[b / 64][r] + (count from the group start to b).
     for (int i = tid; i < nb; i += kTile) {
         const int c = i / R, r = i % R;
-        const int64_t b = boundary(c, a.per, T);
+        const int64_t b = layout_boundary(c, a.per, T);
         int32_t val;
         if (b >= T) {
-            val = s_total[r];
+            val = s.total[r];
         } else {
             const int g = (int)(b / kGroup);
-            const int32_t gp = gp_in_lds ? s_gp[g * R + r] : a.group_prefix[(int64_t)g * R + r];
-            val = gp + (cp_in_lds ? s_chan[i] : a.chan_part[i]);
+            const int32_t gp = gp_in_lds ? s.gp[g * R + r] : a.group_prefix[(int64_t)g * R + r];
+            val = gp + (cp_in_lds ? s.chan[i] : a.chan_part[i]);
         }
         if (c < a.C) a.recv_channel_prefix_matrix[r * a.C + c] = val;
         if (c > 0) a.channel_prefix_matrix[r * a.C + c - 1] = val;
@@ -259,6 +477,15 @@ __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
     if (tid == 0) atomicExch(a.ticket, 0u);
 }
 
+__global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
+    __shared__ LayoutShared s;
+    TileToken tk;
+    if (layout_tile(a, (int)blockIdx.x, (int)gridDim.x, s, &tk)) {
+        layout_finish(a, (int)gridDim.x, s);
+        const int t = (int)blockIdx.x * kTile + (int)threadIdx.x;
+        if (t < a.T) layout_token_outputs(a, t, tk);
+    }
+}
 
 }  // namespace
 
