@@ -398,6 +398,7 @@ int moedx_get_dispatch_layout(moedx_ctx* ctx, const int64_t* topk_idx, int T, in
     a.bucket = ctx->bucket;
     a.C = ctx->C;
     a.per = T > 0 ? (T + ctx->C - 1) / ctx->C : 1;
+    a.per_div = make_fastdiv((uint32_t)a.per);
     a.is_token_in_rank = is_token_in_rank;
     a.num_tokens_per_rank = num_tokens_per_rank;
     a.num_tokens_per_expert = num_tokens_per_expert;
@@ -469,6 +470,7 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
         a.bucket = ctx->bucket;
         a.C = h->C;
         a.per = T > 0 ? (T + h->C - 1) / h->C : 1;
+        a.per_div = make_fastdiv((uint32_t)a.per);
         a.is_token_in_rank = h->is_token_in_rank;
         a.token_mask = h->token_mask;
         a.slot_bucket = h->slot_bucket;

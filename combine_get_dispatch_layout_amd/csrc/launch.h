@@ -108,6 +108,7 @@ BucketDiv bucket_div(int E, int P);
 struct LayoutArgs {
     const int64_t* topk_idx;  // [T, K]
     int T, K, E, R, P, C, per;
+    FastDiv per_div;  // n / per
     BucketDiv bucket;
     uint8_t* is_token_in_rank;             // [T, R]
     uint64_t* token_mask;                  // [T] bucket bit mask (handle)

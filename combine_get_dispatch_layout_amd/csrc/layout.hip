@@ -124,6 +124,30 @@ __device__ __forceinline__ void layout_token_outputs(const LayoutArgs& a, int t,
     }
 }
 
+// The NS slots of one token (NS >= K, row = its topk_idx row): its bucket
+// mask, its slot buckets in *tk and its experts counted in the LDS histogram.
+// Slots past K re-read slot K - 1 and are ignored; ids outside [0, E) are
+// empty slots.
+template <int NS>
+__device__ __forceinline__ uint64_t tile_slots(const LayoutArgs& a, const int64_t* row,
+                                               LayoutShared& s, TileToken* tk) {
+    const int K = a.K, E = a.E;
+    int64_t ids[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) ids[k] = row[k < K ? k : K - 1];
+    uint64_t mask = 0;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const int64_t e = ids[k];
+        const bool valid = k < K && e >= 0 && e < E;
+        const int b = a.bucket.of(valid ? (int)e : 0);
+        mask |= valid ? (1ull << b) : 0ull;
+        tk->sb[k >> 2] ^= valid ? (uint32_t)(0xff ^ b) << (8 * (k & 3)) : 0u;
+        if (valid) atomicAdd(&s.hist[(int)e], 1);
+    }
+    return mask;
+}
+
 // Phase 1 for tile `tile` of `ntiles`.  Returns true in the workgroup that took
 // the last ticket (workgroup-uniform), which must then run layout_finish and,
 // after it, layout_token_outputs for its own tokens (*tk; the other workgroups
@@ -151,52 +175,48 @@ __device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int n
             // Every slot load is issued before the first is used (one memory
             // round trip); slots past K re-read slot K - 1 and are ignored.
             const int64_t* row = a.topk_idx + (int64_t)t * K;
-            int64_t ids[kMaxTopk];
-            if (K <= kMaxTopk / 2) {
-#pragma unroll
-                for (int k = 0; k < kMaxTopk / 2; ++k) ids[k] = row[k < K ? k : K - 1];
-#pragma unroll
-                for (int k = kMaxTopk / 2; k < kMaxTopk; ++k) ids[k] = -1;
-            } else {
-#pragma unroll
-                for (int k = 0; k < kMaxTopk; ++k) ids[k] = row[k < K ? k : K - 1];
-            }
-#pragma unroll
-            for (int k = 0; k < kMaxTopk; ++k) {
-                const int64_t e = ids[k];
-                if (k < K && e >= 0 && e < E) {  // ids outside [0, E) are empty slots
-                    const int b = a.bucket.of((int)e);
-                    mask |= 1ull << b;
-                    tk->sb[k >> 2] ^= (uint32_t)(0xff ^ b) << (8 * (k & 3));
-                    atomicAdd(&s.hist[(int)e], 1);
-                }
-            }
+            if (K <= kMaxTopk / 2)
+                mask = tile_slots<kMaxTopk / 2>(a, row, s, tk);
+            else
+                mask = tile_slots<kMaxTopk>(a, row, s, tk);
             tk->mask = mask;
         }
-        // Group (one wave = 64 tokens) counts of every bucket; lane r keeps bucket r.
+        // Bucket counts over the wave's 64 tokens (a group), eight buckets at
+        // a time: each token's bits for buckets j..j+7 are spread to one byte
+        // each (a count never exceeds 64, so bytes never carry) and one wave
+        // prefix sum per 32-bit half gives, at lane i, the counts over lanes
+        // 0..i of four buckets.  Lane 63 holds the group counts; the counts
+        // from the group start to a channel boundary at offset o are those of
+        // lane o - 1.  Lane r stores bucket r's values.
         const int g = tile * kLayoutWaves + wave;
         const int g_begin = g * kGroup;
-        if (g_begin < T) {
-            int32_t my_cnt = 0;
-            for (int r = 0; r < R; ++r) {
-                const int c = __popcll(__ballot((mask >> r) & 1u));
-                if (lane == r) my_cnt = c;
-            }
-            if (lane < R) a.group_cnt[(int64_t)g * R + lane] = my_cnt;
-            // Channel boundaries inside this group: count from the group start.
-            if (with_channels) {
-                int c = (int)((g_begin + a.per - 1) / a.per);
-                for (; c <= a.C; ++c) {
+        if (g_begin < T) {  // wave-uniform; every lane takes part in the sums
+            // First channel boundary at or after g_begin: ceil(g_begin / per).
+            const int c_first =
+                with_channels ? (int)a.per_div.div((uint32_t)(g_begin + a.per - 1)) : a.C + 1;
+            for (int j = 0; j < R; j += 8) {
+                const uint32_t bits = (uint32_t)(mask >> j) & 0xffu;
+                const uint32_t lo = ((bits & 0xfu) * 0x00204081u) & 0x01010101u;
+                const uint32_t hi = ((bits >> 4) * 0x00204081u) & 0x01010101u;
+                const uint32_t slo = (uint32_t)wave_inclusive_sum((int32_t)lo);
+                const uint32_t shi = (uint32_t)wave_inclusive_sum((int32_t)hi);
+                const int rr = lane - j;  // this lane's bucket within the eight
+                const bool mine = rr >= 0 && rr < 8 && lane < R;
+                const int sh = 8 * (rr & 3);
+                {
+                    const uint32_t w = rr < 4 ? __builtin_amdgcn_readlane(slo, 63)
+                                              : __builtin_amdgcn_readlane(shi, 63);
+                    if (mine) a.group_cnt[(int64_t)g * R + lane] = (int32_t)((w >> sh) & 0xffu);
+                }
+                for (int c = c_first; c <= a.C; ++c) {
                     const int64_t b = layout_boundary(c, a.per, T);
                     if (b >= T || b >= g_begin + kGroup) break;
                     const int off = (int)(b - g_begin);
-                    const uint64_t below = off == 0 ? 0ull : (~0ull >> (64 - off));
-                    int32_t part = 0;
-                    for (int r = 0; r < R; ++r) {
-                        const int n = __popcll(__ballot((mask >> r) & 1u) & below);
-                        if (lane == r) part = n;
-                    }
-                    if (lane < R) a.chan_part[(int64_t)c * R + lane] = part;
+                    uint32_t w = 0;
+                    if (off > 0)
+                        w = rr < 4 ? __builtin_amdgcn_readlane(slo, off - 1)
+                                   : __builtin_amdgcn_readlane(shi, off - 1);
+                    if (mine) a.chan_part[(int64_t)c * R + lane] = (int32_t)((w >> sh) & 0xffu);
                 }
             }
         }
