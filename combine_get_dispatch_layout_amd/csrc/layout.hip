@@ -48,7 +48,6 @@ struct LayoutShared {
     int32_t chan[kLdsChan];
     int32_t total[kMaxRanks];
     int32_t base[kMaxRanks];
-    int32_t fgp[kGroup * kMaxRanks];  // group prefixes of the fast finishing step
     unsigned int ticket;
 };
 
@@ -237,67 +236,98 @@ __device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int n
     return last;
 }
 
-// Sizes the fast finishing step covers: every group of a bucket in one wave
-// (T <= 4096), at most 16 tiles of expert partials per expert, and at most two
-// channel boundaries (of one bucket each) per thread.
+// The fast finishing step keeps every load of its partials in registers:
+// up to 4 buckets per wave (R <= 16) times 4 chunks of 64 groups (T <= 16384),
+// up to 32 tiles per expert thread, three channel boundaries per thread; and
+// its group prefixes in LDS (gp).
+constexpr int kFastChunks = 4;
+constexpr int kFastBuckets = 4;
+constexpr int kFastTiles = 32;
+constexpr int kFastBounds = 3;
+
+__device__ __forceinline__ int layout_per_expert(int E) { return E >= kTile ? 1 : kTile / E; }
+
 __device__ __forceinline__ bool layout_fast_finish_fits(const LayoutArgs& a, int ntiles) {
     const int nb = a.channel_prefix_matrix != nullptr ? (a.C + 1) * a.R : 0;
-    return a.T > 0 && num_groups(a.T) <= 64 && ntiles <= 16 && nb <= 2 * kTile;
+    const int ng = num_groups(a.T);
+    return a.T > 0 && ng <= kFastChunks * kGroup && a.R <= kFastBuckets * kLayoutWaves &&
+           ng * a.R <= kLdsGroups && ntiles <= kFastTiles * layout_per_expert(a.E) &&
+           nb <= kFastBounds * kTile;
 }
 
 // Phase 2 for the sizes layout_fast_finish_fits admits: every load is issued
 // before the first is used (one memory round trip), and the scan is branch-free:
-// wave w takes buckets w, w + 4, ..., lane g holding group g, and one wave
-// prefix sum per bucket gives every group prefix and the bucket total.
+// wave w takes buckets w, w + 4, ..., lane g of chunk c holding group 64c + g,
+// and one wave prefix sum per bucket and chunk (plus the running total of the
+// chunks before) gives every group prefix and the bucket total.
 __device__ __forceinline__ void layout_finish_fast(const LayoutArgs& a, int ntiles,
                                                    LayoutShared& s) {
-    constexpr int kBuckets = kMaxRanks / kLayoutWaves;  // buckets per wave, at most
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = a.T, E = a.E, R = a.R;
     const int ng = num_groups(T);
+    const int nch = (ng + kGroup - 1) / kGroup;
     const int nb = a.channel_prefix_matrix != nullptr ? (a.C + 1) * R : 0;
+    // Expert partials: thread i < E * per_e sums tiles i / E, i / E + per_e, ...
+    // of expert i % E (experts past 256 are summed after the fast part).
+    const int per_e = layout_per_expert(E);
+    const bool e_thread = tid < E * per_e;
+    const int e0 = tid % E;
+    for (int e = tid; e < E; e += kTile) s.hist[e] = 0;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     // Indices first, then every load.
-    const bool g_lane = lane < ng;
     const __amdgpu_buffer_rsrc_t gc = word_buffer(a.group_cnt, ng * R);
     const __amdgpu_buffer_rsrc_t te = word_buffer(a.tile_expert, ntiles * E);
     const __amdgpu_buffer_rsrc_t cp = word_buffer(a.chan_part, nb);
-    const unsigned int gbase = g_lane ? (unsigned int)(lane * R + wave) : kNoWord;
-    const unsigned int ebase = tid < E ? (unsigned int)tid : kNoWord;
-    int32_t cnt[kBuckets], ev[16], cv[2];
+    const unsigned int ebase = e_thread ? (unsigned int)((tid / E) * E + e0) : kNoWord;
+    int32_t cnt[kFastBuckets][kFastChunks], ev[kFastTiles], cv[kFastBounds];
 #pragma unroll
-    for (int i = 0; i < kBuckets; ++i)  // bucket wave + 4i; past R: past the buffer's end
-        cnt[i] = load_word(gc, wave + 4 * i < R ? gbase + (unsigned int)(4 * i) : kNoWord);
+    for (int i = 0; i < kFastBuckets; ++i)
 #pragma unroll
-    for (int u = 0; u < 16; ++u)  // tiles past ntiles lie past the buffer's end
-        ev[u] = load_word(te, ebase + (unsigned int)(u * E));
+        for (int c = 0; c < kFastChunks; ++c) {  // past R or ng: past the buffer's end
+            const int r = wave + kLayoutWaves * i, gg = c * kGroup + lane;
+            cnt[i][c] = load_word(gc, r < R && gg < ng ? (unsigned int)(gg * R + r) : kNoWord);
+        }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) cv[q] = load_word(cp, (unsigned int)(tid + q * kTile));
+    for (int u = 0; u < kFastTiles; ++u)  // tiles past ntiles lie past the buffer's end
+        ev[u] = load_word(te, ebase + (unsigned int)(u * per_e * E));
+#pragma unroll
+    for (int q = 0; q < kFastBounds; ++q) cv[q] = load_word(cp, (unsigned int)(tid + q * kTile));
     __builtin_amdgcn_sched_barrier(0);
 
     // Group prefixes and bucket totals.
 #pragma unroll
-    for (int i = 0; i < kBuckets; ++i) {
-        const int r = wave + 4 * i;
+    for (int i = 0; i < kFastBuckets; ++i) {
+        const int r = wave + kLayoutWaves * i;
         if (r >= R) break;  // wave-uniform
-        const int32_t incl = wave_inclusive_sum(cnt[i]);
-        const int32_t excl = incl - cnt[i];
-        s.fgp[lane * R + r] = excl;
-        if (g_lane && a.group_prefix) a.group_prefix[(int64_t)lane * R + r] = excl;
-        if (lane == 63) s.total[r] = incl;
+        int32_t carry = 0;
+#pragma unroll
+        for (int c = 0; c < kFastChunks; ++c) {
+            if (c >= nch) break;  // wave-uniform
+            const int32_t incl = wave_inclusive_sum(cnt[i][c]);
+            const int gg = c * kGroup + lane;
+            if (gg < ng) {
+                const int32_t excl = carry + incl - cnt[i][c];
+                s.gp[gg * R + r] = excl;
+                if (a.group_prefix) a.group_prefix[(int64_t)gg * R + r] = excl;
+            }
+            carry += __builtin_amdgcn_readlane(incl, 63);
+        }
+        if (lane == 0) s.total[r] = carry;
     }
-    // Expert totals (E <= 256 here in one pass; more experts in further passes).
+    // Expert totals: the partial sums of each expert meet in LDS.
     int32_t esum = 0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) esum += ev[u];
-    if (tid < E) a.num_tokens_per_expert[tid] = esum;
-    for (int e = tid + kTile; e < E; e += kTile) {
+    for (int u = 0; u < kFastTiles; ++u) esum += ev[u];
+    __syncthreads();  // hist cleared by every thread
+    if (e_thread) atomicAdd(&s.hist[e0], esum);
+    for (int e = tid + kTile; e < E; e += kTile) {  // E > 256
         int32_t v = 0;
         for (int j = 0; j < ntiles; ++j) v += a.tile_expert[(int64_t)j * E + e];
-        a.num_tokens_per_expert[e] = v;
+        s.hist[e] = v;
     }
     __syncthreads();
+    for (int e = tid; e < E; e += kTile) a.num_tokens_per_expert[e] = s.hist[e];
     // Bucket offsets: one wave prefix sum over the bucket totals.
     if (wave == 0) {
         const int32_t tot = lane < R ? s.total[lane] : 0;
@@ -311,12 +341,12 @@ __device__ __forceinline__ void layout_finish_fast(const LayoutArgs& a, int ntil
     // Channel prefixes: excl(b, r) = group prefix of b's group + count from the
     // group start to b (the bucket total for b = T).
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kFastBounds; ++q) {
         const int i = tid + q * kTile;
         if (i < nb) {
             const int c = i / R, r = i - (i / R) * R;
             const int64_t b = layout_boundary(c, a.per, T);
-            const int32_t val = b >= T ? s.total[r] : s.fgp[(int)(b / kGroup) * R + r] + cv[q];
+            const int32_t val = b >= T ? s.total[r] : s.gp[(int)(b / kGroup) * R + r] + cv[q];
             if (c < a.C) a.recv_channel_prefix_matrix[r * a.C + c] = val;
             if (c > 0) a.channel_prefix_matrix[r * a.C + c - 1] = val;
         }
