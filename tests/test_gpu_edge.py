@@ -189,3 +189,22 @@ def test_large_batch_global_scan_paths(oracle):
     workgroup's LDS staging, so both come from global memory, over several
     scan passes."""
     run_case(oracle, _rand(200_000, 64, 4, p_empty=0.05, seed=77), 64, 64, 16, 200)
+
+
+# The layout's straight-line finishing step covers up to 256 groups (T <= 16384),
+# 16 buckets, 32 tiles of expert partials per expert thread (256 / E threads per
+# expert when E < 256) and 3 channel boundaries per thread (768); every shape
+# below sits at one of those limits or one past it, so both finishing steps are
+# checked against the oracle on either side of each bound (H = 8 keeps the
+# rows small while every receive position is still compared).
+@pytest.mark.parametrize("T,E,K,R,C", [
+    (16384, 64, 6, 16, 47),   # 256 groups, 64 tiles over 4 threads per expert, 768 boundaries
+    (16384, 64, 6, 16, 48),   # 784 boundaries: general step
+    (16385, 64, 6, 16, 8),    # 257 groups: general step
+    (8192, 256, 8, 16, 5),    # 32 tiles with one thread per expert
+    (8193, 256, 8, 16, 5),    # 33 tiles: general step
+    (1000, 68, 4, 17, 6),     # 17 buckets: general step
+    (2000, 1024, 8, 16, 8),   # experts past the first 256 summed after the fast part
+], ids=lambda v: str(v))
+def test_layout_finishing_step_limits(oracle, T, E, K, R, C):
+    run_case(oracle, _rand(T, E, K, p_empty=0.02, seed=T + R + C), 8, E, R, C, capacity=(T % 2 == 0))
