@@ -148,9 +148,9 @@ __device__ __forceinline__ uint64_t tile_slots(const LayoutArgs& a, const int64_
 }
 
 // Phase 1 for tile `tile` of `ntiles`.  Returns true in the workgroup that took
-// the last ticket (workgroup-uniform), which must then run layout_finish and,
-// after it, layout_token_outputs for its own tokens (*tk; the other workgroups
-// have written theirs when this returns).
+// the last ticket (workgroup-uniform), which must then run layout_finish and
+// see that its own per-token outputs (*tk) are written; the other workgroups
+// have written theirs when this returns.
 __device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int ntiles,
                                             LayoutShared& s, TileToken* tk) {
     const int tid = threadIdx.x;
@@ -261,7 +261,7 @@ __device__ __forceinline__ bool layout_fast_finish_fits(const LayoutArgs& a, int
 // and one wave prefix sum per bucket and chunk (plus the running total of the
 // chunks before) gives every group prefix and the bucket total.
 __device__ __forceinline__ void layout_finish_fast(const LayoutArgs& a, int ntiles,
-                                                   LayoutShared& s) {
+                                                   LayoutShared& s, const TileToken& tk) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = a.T, E = a.E, R = a.R;
     const int ng = num_groups(T);
@@ -293,6 +293,11 @@ __device__ __forceinline__ void layout_finish_fast(const LayoutArgs& a, int ntil
         ev[u] = load_word(te, ebase + (unsigned int)(u * per_e * E));
 #pragma unroll
     for (int q = 0; q < kFastBounds; ++q) cv[q] = load_word(cp, (unsigned int)(tid + q * kTile));
+    // This workgroup's own per-token outputs, issued while the loads are in flight.
+    {
+        const int t = (int)blockIdx.x * kTile + tid;
+        if (t < T) layout_token_outputs(a, t, tk);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // Group prefixes and bucket totals.
@@ -355,10 +360,13 @@ __device__ __forceinline__ void layout_finish_fast(const LayoutArgs& a, int ntil
 }
 
 // Phase 2, in the workgroup that took the last ticket of `ntiles` tiles.
-__device__ __forceinline__ void layout_finish(const LayoutArgs& a, int ntiles, LayoutShared& s) {
+// Returns whether it has also written this workgroup's per-token outputs (tk;
+// the fast step issues them while its loads are in flight).
+__device__ __forceinline__ bool layout_finish(const LayoutArgs& a, int ntiles, LayoutShared& s,
+                                              const TileToken& tk) {
     if (layout_fast_finish_fits(a, ntiles)) {
-        layout_finish_fast(a, ntiles, s);
-        return;
+        layout_finish_fast(a, ntiles, s, tk);
+        return true;
     }
     constexpr int kPerThread = 16;  // groups per finishing thread per pass
     constexpr int kBatch = 16;      // loads issued together for the expert totals
@@ -525,15 +533,17 @@ __device__ __forceinline__ void layout_finish(const LayoutArgs& a, int ntiles, L
         if (c > 0) a.channel_prefix_matrix[r * a.C + c - 1] = val;
     }
     if (tid == 0) atomicExch(a.ticket, 0u);
+    return false;
 }
 
 __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
     __shared__ LayoutShared s;
     TileToken tk;
     if (layout_tile(a, (int)blockIdx.x, (int)gridDim.x, s, &tk)) {
-        layout_finish(a, (int)gridDim.x, s);
-        const int t = (int)blockIdx.x * kTile + (int)threadIdx.x;
-        if (t < a.T) layout_token_outputs(a, t, tk);
+        if (!layout_finish(a, (int)gridDim.x, s, tk)) {
+            const int t = (int)blockIdx.x * kTile + (int)threadIdx.x;
+            if (t < a.T) layout_token_outputs(a, t, tk);
+        }
     }
 }
 
