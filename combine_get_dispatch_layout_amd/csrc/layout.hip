@@ -229,9 +229,9 @@ __device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int n
     if (tid == 0) s.ticket = atomicAdd(a.ticket, 1u);
     __syncthreads();
     const bool last = s.ticket == (unsigned int)(ntiles - 1);
-    // The per-token outputs (not read by the finishing step, which the last
-    // workgroup runs before writing its own, so that its acquire does not wait
-    // for these stores).
+    // The per-token outputs (not read by the finishing step).  The last
+    // workgroup writes its own during or after its finish, so that its acquire
+    // fence does not wait for these stores.
     if (!last && t < T) layout_token_outputs(a, t, *tk);
     return last;
 }
