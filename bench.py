@@ -12,7 +12,7 @@ synchronisation inside the step); each is one kernel launch.
 
 Timing: each op is launched back to back `--steps` times between two HIP
 events on its stream, rotating over enough buffer sets that every launch reads
-its input from HBM: more than twice the 256 MB Infinity Cache is read between
+its input from HBM: at least twice the 256 MB Infinity Cache is read between
 two reads of one set (the cache otherwise serves a good part of a just-written
 receive buffer, and keeps up to four copies of x while the pack's streaming
 stores pass); a step's time is the sum of the three per-op means.  The value is algorithmic bytes / step time (GB/s); tokens/s and
@@ -43,7 +43,7 @@ INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (memory-side) cache
 
 
 def input_copies(nbytes):
-    """Copies of an op's input to rotate over so that more than twice the
+    """Copies of an op's input to rotate over so that at least twice the
     Infinity Cache is read between two reads of one copy: every launch then
     reads its input from HBM (with 3 copies of a 58.7 MB x the bf16 pack read
     x from the cache and looked 16% faster than it is)."""

@@ -1,0 +1,41 @@
+"""Host-side pieces of bench.py that need no GPU: the one-GPU guard, the input
+rotation that keeps every timed launch reading from HBM, and the traffic
+figures that are reported only for the kernel source they were measured on."""
+
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_rotation_reads_at_least_twice_the_infinity_cache_between_reuses():
+    for nbytes in (1 << 20, 58_720_256, 117_440_512, 233_000_000, 1 << 30):
+        n = bench.input_copies(nbytes)
+        assert n >= 3
+        # between two reads of one copy, the other n - 1 copies are read
+        assert (n - 1) * nbytes >= 2 * bench.INFINITY_CACHE_BYTES
+
+
+def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch):
+    summary = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))
+    for op, rec in summary["ops"].items():
+        assert rec["traffic_bytes_per_launch"] > 0
+        # the committed digests are those of the committed sources
+        assert rec["source_sha256_16"] == bench.source_digest(rec["source"]), op
+        assert bench.measured_traffic(op) == rec["traffic_bytes_per_launch"]
+    # a different source (here: another kernel file) gives no figure
+    monkeypatch.setitem(bench.TRAFFIC_SOURCES, "pack", "combine.hip")
+    assert bench.measured_traffic("pack") is None
+    assert bench.measured_traffic("no_such_op") is None
