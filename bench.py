@@ -141,7 +141,8 @@ def kernel_us_distribution(C, stream, launch, n, flush):
         d.append(ms.value * 1e3)
     d.sort()
     q = lambda f: d[min(len(d) - 1, int(round(f * (len(d) - 1))))]  # noqa: E731
-    return {"p10": round(q(0.1), 2), "median": round(q(0.5), 2), "p90": round(q(0.9), 2)}
+    return {"p10": round(q(0.1), 2), "median": round(q(0.5), 2), "p90": round(q(0.9), 2),
+            "mean": round(statistics.mean(d), 2)}
 
 
 def cpu_baseline(inp, w, budget_s):
@@ -609,9 +610,10 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
 
 
 def batch_sweep(token_counts, steps, log_fn):
-    """The step (layout + pack + combine, capacity mode) of the prefill workload's
-    routing and hidden size at other batch sizes, every input read from HBM;
-    one JSON line per batch size."""
+    """The step (dispatch = layout + first pack on a fresh handle, then the
+    combine; capacity mode) of the prefill workload's routing and hidden size at
+    other batch sizes, every input read from HBM; one JSON line per batch size
+    (the layout alone is timed beside it)."""
     import torch
 
     from combine_get_dispatch_layout_amd import Buffer
@@ -649,23 +651,26 @@ def batch_sweep(token_counts, steps, log_fn):
             s["h"] = h
             sets.append(s)
 
+        def first_pack(h, s):
+            C.check(C.moedx_dispatch(buf.ctx, h, P(s["x"]), T, H, C.MOEDX_QUANT_NONE,
+                                     P(idx), P(gw), P(s["recv"]), None, P(s["rti"]),
+                                     P(s["rtw"]), exr))
+
         def op(name, i):
             s = sets[i % nsets]
-            if name == "layout":
+            if name in ("layout", "dispatch"):
                 h = ctypes.c_void_p()
                 C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, P(s["ws"]), nb.value, cap,
                                                  ctypes.byref(h), exr))
+                if name == "dispatch":
+                    first_pack(h, s)
                 C.moedx_handle_destroy(h)
-            elif name == "pack":
-                C.check(C.moedx_dispatch(buf.ctx, s["h"], P(s["x"]), T, H, C.MOEDX_QUANT_NONE,
-                                         P(idx), P(gw), P(s["recv"]), None, P(s["rti"]),
-                                         P(s["rtw"]), exr))
             else:
                 C.check(C.moedx_combine(buf.ctx, s["h"], P(s["recv"]), H, P(gw), None,
                                         P(s["out"]), None, exr))
 
         for i in range(nsets):
-            op("pack", i)
+            first_pack(sets[i]["h"], sets[i])
         torch.cuda.synchronize()
         dev_n = ctypes.c_void_p()
         shape = (ctypes.c_int64 * 2)()
@@ -673,7 +678,7 @@ def batch_sweep(token_counts, steps, log_fn):
         off = dev_n.value - sets[0]["ws"].data_ptr()
         N = int(sets[0]["ws"][off:off + 4].view(torch.int32).item())
         us = {}
-        for name in ("layout", "pack", "combine"):
+        for name in ("dispatch", "combine", "layout"):
             for _ in range(2):  # the first pass warms up
                 torch.sum(flush_buf, dim=(0,), out=sink)
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -684,12 +689,14 @@ def batch_sweep(token_counts, steps, log_fn):
                 torch.cuda.synchronize()
                 us[name] = round(a.elapsed_time(b) * 1e3 / steps, 2)
         byts = algorithmic_bytes(T, H, K, E, R, Ch, N)
-        step_us = sum(us.values())
+        step_us = us["dispatch"] + us["combine"]
         gbs = sum(byts.values()) / (step_us * 1e-6) / 1e9
+        dispatch_bytes = byts["layout"] + byts["pack"]
         print(json.dumps({"tokens": T, "hidden": H, "recv_rows": N, "buffer_sets": nsets,
                           "kernels_us": us, "step_us": round(step_us, 2), "GBps": round(gbs, 1),
                           "roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
-                          "pack_frac": round(byts["pack"] / (us["pack"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "dispatch_frac": round(dispatch_bytes / (us["dispatch"] * 1e-6) / 1e9
+                                                 / HBM_PEAK_GBS, 4),
                           "combine_frac": round(byts["combine"] / (us["combine"] * 1e-6) / 1e9
                                                 / HBM_PEAK_GBS, 4)}), flush=True)
         for s in sets:
@@ -790,20 +797,28 @@ def main():
         C.moedx_event_destroy(b)
         return ms.value
 
+    # Each set's handle, finished by its first pack; the combine runs on these.
     handles = [prepare(s_) for s_ in sets]
     for h, s_ in zip(handles, sets):
         pack(h, s_)
 
+    def dispatch(s_, e=exr, e_pack=None):
+        """The step's dispatch on a fresh handle: the layout's partials, then the
+        first pack, which also finishes the handle's prefixes."""
+        h = prepare(s_, e)
+        pack(h, s_, e_pack if e_pack is not None else e)
+        C.moedx_handle_destroy(h)
+
     def op_avg_ms(op, n):
-        """Average duration of n back-to-back launches of one op over rotating sets."""
+        """Average duration of n back-to-back runs of one op over rotating sets."""
         flush()
         a = record()
         for i in range(n):
             j = i % NSETS
             if op == "layout":
                 C.moedx_handle_destroy(prepare(sets[j]))
-            elif op == "pack":
-                pack(handles[j], sets[j])
+            elif op == "dispatch":
+                dispatch(sets[j])
             else:
                 combine(handles[j], sets[j])
         b = record()
@@ -811,20 +826,21 @@ def main():
         return elapsed_ms(a, b) / n
 
     def op_kernel_us(op, n):
-        """Per-launch kernel durations of n back-to-back launches over rotating
-        sets: p10 / median / p90."""
+        """Kernel durations of one kernel per run over n back-to-back runs on
+        rotating sets: p10 / median / p90 / mean ("pack": the first pack of each
+        dispatch, its layout launch unstamped before it)."""
         def launch(i, e):
             j = i % NSETS
             if op == "layout":
                 C.moedx_handle_destroy(prepare(sets[j], e))
             elif op == "pack":
-                pack(handles[j], sets[j], e)
+                dispatch(sets[j], exr, e)
             else:
                 combine(handles[j], sets[j], e)
         return kernel_us_distribution(C, stream, launch, n, flush)
 
     def pipelined_ms(n):
-        """n whole steps back to back (layout, pack, combine each), rotating sets."""
+        """n whole steps back to back (layout, first pack, combine each), rotating sets."""
         flush()
         a = record()
         for i in range(n):
@@ -838,7 +854,7 @@ def main():
         return elapsed_ms(a, b) / n
 
     log(f"[bench] warmup {args.warmup}")
-    for op in ("layout", "pack", "combine"):
+    for op in ("layout", "dispatch", "combine"):
         op_avg_ms(op, max(args.warmup, 1))
     pipelined_ms(max(args.warmup, 1))
     torch.cuda.synchronize()
@@ -855,12 +871,13 @@ def main():
     log(f"[bench] timing: {args.steps} launches per op (HBM-cold rotation), {args.steps} pipelined steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_lay = op_avg_ms("layout", args.steps)
-    t_pack = op_avg_ms("pack", args.steps)
+    t_disp = op_avg_ms("dispatch", args.steps)
     t_comb = op_avg_ms("combine", args.steps)
+    t_lay = op_avg_ms("layout", args.steps)
     ms_pipe = pipelined_ms(args.steps)
     wall = time.perf_counter() - wall0
     dist = {op: op_kernel_us(op, args.steps) for op in ("layout", "pack", "combine")}
+    t_pack = dist["pack"]["mean"] * 1e-3  # ms: the first pack alone, kernel-stamped
 
     # Exact mode through the API on the host clock: the host waits for N after
     # the layout (no capacity bound), then the pack and the combine run.
@@ -884,7 +901,7 @@ def main():
         if i >= max(args.warmup, 1):
             wall_exact.append((time.perf_counter() - t0) * 1e6)
     wall_exact.sort()
-    ms = t_lay + t_pack + t_comb
+    ms = t_disp + t_comb
     gbs = step_bytes / (ms * 1e-3) / 1e9
     for h in handles:
         C.moedx_handle_destroy(h)
@@ -906,7 +923,8 @@ def main():
     copy_gbs = 2 * nb / (copy_ms * 1e-3) / 1e9
     del src_c, dst_c
 
-    kern = {"pack": (t_pack, bytes_["pack"]), "combine": (t_comb, bytes_["combine"])}
+    t_comb_k = dist["combine"]["mean"] * 1e-3
+    kern = {"pack": (t_pack, bytes_["pack"]), "combine": (t_comb_k, bytes_["combine"])}
     dom = max(kern, key=lambda k: kern[k][0])
     dom_ms, dom_bytes = kern[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
@@ -942,19 +960,22 @@ def main():
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": E, "topk": K,
                    "ranks": R, "channels": Ch, "routing": w.routing, "recv_rows": N,
                    "mode": "capacity (no host sync)",
-                   "timing": "sum over layout, pack, combine of each op's mean over back-to-back "
-                             f"launches rotating over {NSETS} buffer sets, so that every input "
-                             "is read from HBM (not the Infinity Cache); HIP events"},
+                   "timing": "dispatch (layout partials + first pack on a fresh handle) plus "
+                             "combine, each the mean over back-to-back runs rotating over "
+                             f"{NSETS} buffer sets, so that every input is read from HBM (not "
+                             "the Infinity Cache); HIP events"},
         "tokens_per_s": round(T / (ms * 1e-3), 1),
         "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
-        "kernels_us": {"layout": round(t_lay * 1e3, 2), "pack": round(t_pack * 1e3, 2),
-                       "combine": round(t_comb * 1e3, 2)},
+        "ops_us": {"dispatch": round(t_disp * 1e3, 2), "combine": round(t_comb * 1e3, 2),
+                   "layout_alone": round(t_lay * 1e3, 2)},
+        "kernels_us": {"layout": dist["layout"]["mean"], "pack": dist["pack"]["mean"],
+                       "combine": dist["combine"]["mean"]},
         "kernels_us_per_launch": dist,
         "kernel_GBps": {"pack": round(bytes_["pack"] / (t_pack * 1e-3) / 1e9, 1),
-                        "combine": round(bytes_["combine"] / (t_comb * 1e-3) / 1e9, 1)},
+                        "combine": round(bytes_["combine"] / (t_comb_k * 1e-3) / 1e9, 1)},
         "pipelined_ms_per_step": round(ms_pipe, 5),
         "exact_mode_api_wall_us": {
             "median": round(statistics.median(wall_exact), 1),

@@ -234,7 +234,8 @@ class Buffer:
                 previous_event=None, async_finish=False, allocate_on_comm_stream=False,
                 no_sync=False):
         """Layout + scan into a new handle (exact mode, or capacity mode with
-        ``num_worst_tokens`` receive rows)."""
+        ``num_worst_tokens`` receive rows; a capacity-mode handle's prefixes,
+        totals and N are written by its first dispatch or combine)."""
         topk_idx = topk_idx.contiguous()
         T, K = topk_idx.shape
         nbytes = ctypes.c_size_t()

@@ -50,6 +50,10 @@ struct moedx_handle {
     int64_t n_host;    // exact mode only
     std::vector<int32_t> per_expert_host;
     mutable bool rows_written;  // send_head / recv_src_idx filled by a dispatch
+    // Capacity mode: prepared with the layout's partials only; the first
+    // dispatch or combine finishes the prefixes (or launches the finishing
+    // step first).
+    mutable bool prefixes_pending;
     // device arrays inside the caller's workspace
     uint8_t* is_token_in_rank;
     uint64_t* token_mask;
@@ -229,6 +233,48 @@ static int check_waves(int T, int H) {
     const int64_t slices = (int64_t)(H / 8 + 63) / 64;
     if ((int64_t)T * slices > ((int64_t)1 << 30))
         return fail(MOEDX_EINVAL, "T=%d x H=%d exceeds the supported row count", T, H);
+    return MOEDX_OK;
+}
+
+// The layout kernel's arguments for a handle: every handle array is written.
+static LayoutArgs handle_layout_args(const moedx_ctx* ctx, const moedx_handle* h,
+                                     const int64_t* topk_idx) {
+    LayoutArgs a{};
+    a.topk_idx = topk_idx;
+    a.T = h->T;
+    a.K = h->K;
+    a.E = h->E;
+    a.R = h->R;
+    a.P = h->P;
+    a.bucket = ctx->bucket;
+    a.C = h->C;
+    a.per = h->T > 0 ? (h->T + h->C - 1) / h->C : 1;
+    a.per_div = make_fastdiv((uint32_t)a.per);
+    a.is_token_in_rank = h->is_token_in_rank;
+    a.token_mask = h->token_mask;
+    a.slot_bucket = h->slot_bucket;
+    a.num_tokens_per_rank = h->num_tokens_per_rank;
+    a.num_tokens_per_expert = h->num_tokens_per_expert;
+    a.rank_prefix_matrix = h->rank_prefix_matrix;
+    a.num_recv = h->num_recv;
+    a.group_prefix = h->group_prefix;
+    a.channel_prefix_matrix = h->channel_prefix_matrix;
+    a.recv_channel_prefix_matrix = h->recv_channel_prefix_matrix;
+    a.group_cnt = h->group_cnt;
+    a.chan_part = h->chan_part;
+    a.tile_expert = h->tile_expert;
+    a.ticket = ctx->ticket;
+    return a;
+}
+
+// A handle prepared with the layout's partials only gets its prefixes from the
+// finishing step, launched here on the op's stream ahead of the op's kernel.
+static int finish_pending(moedx_ctx* ctx, const moedx_handle* h, hipStream_t run) {
+    if (!h->prefixes_pending) return MOEDX_OK;
+    HIP_OR_FAIL(launch_layout_finish(handle_layout_args(ctx, h, nullptr),
+                                     Launch{run, nullptr, nullptr}));
+    ctx->stats.layout_launches += 1;
+    h->prefixes_pending = false;
     return MOEDX_OK;
 }
 
@@ -460,32 +506,12 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
     int rc = exec_begin(ctx, exec, &ex);
     hipError_t e = hipSuccess;
     if (rc == MOEDX_OK) {
-        LayoutArgs a{};
-        a.topk_idx = topk_idx;
-        a.T = T;
-        a.K = K;
-        a.E = h->E;
-        a.R = h->R;
-        a.P = h->P;
-        a.bucket = ctx->bucket;
-        a.C = h->C;
-        a.per = T > 0 ? (T + h->C - 1) / h->C : 1;
-        a.per_div = make_fastdiv((uint32_t)a.per);
-        a.is_token_in_rank = h->is_token_in_rank;
-        a.token_mask = h->token_mask;
-        a.slot_bucket = h->slot_bucket;
-        a.num_tokens_per_rank = h->num_tokens_per_rank;
-        a.num_tokens_per_expert = h->num_tokens_per_expert;
-        a.rank_prefix_matrix = h->rank_prefix_matrix;
-        a.num_recv = h->num_recv;
-        a.group_prefix = h->group_prefix;
-        a.channel_prefix_matrix = h->channel_prefix_matrix;
-        a.recv_channel_prefix_matrix = h->recv_channel_prefix_matrix;
-        a.group_cnt = h->group_cnt;
-        a.chan_part = h->chan_part;
-        a.tile_expert = h->tile_expert;
-        a.ticket = ctx->ticket;
-        e = launch_layout(a, ex.launch());
+        // Capacity mode: the partials only; the first dispatch (or combine)
+        // on the handle finishes the prefixes.
+        const LayoutArgs a = handle_layout_args(ctx, h, topk_idx);
+        const bool partials = capacity_rows > 0 && T > 0;
+        e = partials ? launch_layout_partials(a, ex.launch()) : launch_layout(a, ex.launch());
+        h->prefixes_pending = partials;
         if (e != hipSuccess) rc = hip_fail(e, "layout launch");
     }
     if (rc == MOEDX_OK) ctx->stats.layout_launches += 1;
@@ -607,6 +633,18 @@ int moedx_dispatch(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, 
     // The first dispatch on a handle also writes send_head and recv_src_idx.
     const HandleRows hr = h->rows_written ? HandleRows{nullptr, nullptr}
                                           : HandleRows{h->send_head, h->recv_src_idx};
+    if (T > 0 && quant == MOEDX_QUANT_NONE && h->prefixes_pending &&
+        pack_first_fits(T, h->R, h->E, h->C)) {
+        // One launch finishes the handle and packs the rows.
+        HIP_OR_FAIL(launch_pack_bf16_first(handle_layout_args(ctx, h, topk_idx), x, H,
+                                           h->capacity, hr, recv_x, topk_weights, recv_topk_idx,
+                                           recv_topk_weights, ex.launch()));
+        ctx->stats.pack_launches += 1;
+        h->prefixes_pending = false;
+        h->rows_written = true;
+        return exec_end(ex);
+    }
+    if (int rc = finish_pending(ctx, h, ex.run)) return rc;
     if (T == 0) {
         HIP_OR_FAIL(ex.no_kernel());
     } else if (quant == MOEDX_QUANT_NONE) {
@@ -664,6 +702,7 @@ int moedx_dispatch_fp8(moedx_ctx* ctx, const moedx_handle* h, const void* x, int
                     h->R, h->T, h->capacity > 0 ? h->capacity : h->n_host};
     const HandleRows hr = h->rows_written ? HandleRows{nullptr, nullptr}
                                           : HandleRows{h->send_head, h->recv_src_idx};
+    if (int rc = finish_pending(ctx, h, ex.run)) return rc;
     if (T == 0) {
         HIP_OR_FAIL(ex.no_kernel());
     } else if (fp8->prequantized) {
@@ -701,6 +740,7 @@ int moedx_combine(moedx_ctx* ctx, const moedx_handle* h, const uint16_t* y, int 
     if (int rc = exec_begin(ctx, exec, &ex)) return rc;
     const RowMap rm{h->token_mask, h->group_prefix, h->rank_prefix_matrix, h->num_tokens_per_rank,
                     h->R, h->T, h->capacity > 0 ? h->capacity : h->n_host};
+    if (int rc = finish_pending(ctx, h, ex.run)) return rc;
     if (h->T == 0) {
         HIP_OR_FAIL(ex.no_kernel());
     } else {

@@ -128,6 +128,15 @@ struct LayoutArgs {
 
 hipError_t launch_layout(const LayoutArgs& a, const Launch& L);
 
+// The partials and per-token outputs of the layout only (handle arrays
+// group_cnt, chan_part, tile_expert, is_token_in_rank, token_mask,
+// slot_bucket); the prefixes, totals and N are left to a finishing step.
+hipError_t launch_layout_partials(const LayoutArgs& a, const Launch& L);
+
+// The finishing step alone (one workgroup) over partials a previous
+// launch_layout_partials wrote.
+hipError_t launch_layout_finish(const LayoutArgs& a, const Launch& L);
+
 // ---- receive rows ------------------------------------------------------------
 
 // row(t, r) = base[r] + group_prefix[t / 64][r] + (tokens of t's 64-token group
@@ -147,6 +156,16 @@ struct HandleRows {
     int32_t* send_head;     // [T, R]
     int32_t* recv_src_idx;  // [rows]
 };
+
+// First dispatch (bf16) on a handle prepared with launch_layout_partials, in
+// one launch that also finishes the handle's prefixes; for T <= 4096, R a
+// multiple of 4 up to 16 and (C + 1) * R <= 768 (pack_first_fits).  `la`
+// carries every handle array.
+bool pack_first_fits(int T, int R, int E, int C);
+hipError_t launch_pack_bf16_first(const LayoutArgs& la, const void* x, int H, int64_t rows,
+                                  const HandleRows& hr, void* recv_x, const float* topk_weights,
+                                  int64_t* recv_topk_idx, float* recv_topk_weights,
+                                  const Launch& L);
 
 hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
                             void* recv_x, const int64_t* topk_idx, const float* topk_weights,

@@ -21,6 +21,7 @@
 #include <stdint.h>
 
 #include "launch.h"
+#include "layout_core.h"
 #include "rows.h"
 
 #ifndef MOEDX_PACK_WAVE_CHUNKS
@@ -80,31 +81,44 @@ __device__ __forceinline__ void write_handle_rows(const HandleRows& hr, const To
     if (d.row >= 0) hr.recv_src_idx[d.row] = t;
 }
 
-// CPL = 16-byte chunks each lane moves per pass over its part of the row.
+// One wave's part of token t's bf16 row: chunks [c_begin, c_end).  The row
+// loads are issued by pack_bf16_load (all of a lane's chunks in flight at
+// once), before the row lookup; pack_bf16_store writes the part to each of the
+// token's rows d, plus the handle rows and recv_topk_* from the first part.
 template <int CPL>
-__global__ __launch_bounds__(kRowThreads) void pack_bf16_kernel(
-    const u32x4* __restrict__ x, int T, int H8, RowSplit rs, RowMap rm, HandleRows hr,
-    u32x4* __restrict__ recv_x, const int64_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_weights, int K, int E, int P, BucketDiv bucket,
-    int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_topk_weights) {
-    const int lane = threadIdx.x & 63;
-    int t, part;
-    row_part(rs, &t, &part);
-    if (t >= T) return;
+__device__ __forceinline__ void pack_bf16_load(const u32x4* __restrict__ x, int t, int H8,
+                                               int c_begin, int c_end, int lane, u32x4 (&v)[CPL]) {
     const u32x4* src = x + (int64_t)t * H8;
-    const int c_begin = part * rs.per;
-    const int c_end = min(c_begin + rs.per, H8);
-    // One pass (CPL * 64 >= rs.per): the row loads go out before the row lookup.
-    u32x4 v[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = c_begin + i * 64 + lane;
         if (c < c_end) v[i] = load_row(src + c);
     }
-    const TokenRows d = token_rows(rm, t, lane);
-    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
+}
+
+// pack_bf16_load as buffer loads over [c_begin, c_end) of the row (chunks past
+// c_end read 0 and are never stored): no load sits behind a branch, so a later
+// wait for loads issued before these need not wait for these.
+template <int CPL>
+__device__ __forceinline__ void pack_bf16_load_nobranch(const u32x4* __restrict__ x, int t,
+                                                        int H8, int c_begin, int c_end, int lane,
+                                                        u32x4 (&v)[CPL]) {
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4*>(x + (int64_t)t * H8 + c_begin), (short)0, (c_end - c_begin) * 16,
+        0x00020000);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (i * 64 + lane) * 16, 0, 0);
+}
+
+template <int CPL>
+__device__ __forceinline__ void pack_bf16_store(
+    const u32x4 (&v)[CPL], const TokenRows& d, int t, int part, int H8, int c_begin, int c_end,
+    int lane, int R, const HandleRows& hr, u32x4* __restrict__ recv_x,
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_weights, int K, int E,
+    int P, BucketDiv bucket, int64_t* __restrict__ recv_topk_idx,
+    float* __restrict__ recv_topk_weights) {
+    if (part == 0) write_handle_rows(hr, d, t, R, lane);
     {
-        const int base = c_begin;
         uint64_t m = d.dest;
         while (m) {
             const int r = __builtin_ctzll(m);
@@ -113,7 +127,7 @@ __global__ __launch_bounds__(kRowThreads) void pack_bf16_kernel(
             u32x4* dst = recv_x + (int64_t)row * H8;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
-                const int c = base + i * 64 + lane;
+                const int c = c_begin + i * 64 + lane;
                 if (c < c_end) store_row(v[i], dst + c);
             }
         }
@@ -133,6 +147,144 @@ __global__ __launch_bounds__(kRowThreads) void pack_bf16_kernel(
             if (recv_topk_weights) recv_topk_weights[row * K + lane] = mine ? w : 0.0f;
         }
     }
+}
+
+// CPL = 16-byte chunks each lane moves per pass over its part of the row.
+template <int CPL>
+__global__ __launch_bounds__(kRowThreads) void pack_bf16_kernel(
+    const u32x4* __restrict__ x, int T, int H8, RowSplit rs, RowMap rm, HandleRows hr,
+    u32x4* __restrict__ recv_x, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_weights, int K, int E, int P, BucketDiv bucket,
+    int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_topk_weights) {
+    const int lane = threadIdx.x & 63;
+    int t, part;
+    row_part(rs, &t, &part);
+    if (t >= T) return;
+    const int c_begin = part * rs.per;
+    const int c_end = min(c_begin + rs.per, H8);
+    // One pass (CPL * 64 >= rs.per): the row loads go out before the row lookup.
+    u32x4 v[CPL];
+    pack_bf16_load<CPL>(x, t, H8, c_begin, c_end, lane, v);
+    const TokenRows d = token_rows(rm, t, lane);
+    pack_bf16_store<CPL>(v, d, t, part, H8, c_begin, c_end, lane, rm.R, hr, recv_x, topk_idx,
+                         topk_weights, K, E, P, bucket, recv_topk_idx, recv_topk_weights);
+}
+
+// ---- first dispatch on a handle whose prefixes are not yet computed ------------
+
+// Rows of token t from the layout's partials alone (at most 64 groups, R a
+// multiple of 4 and at most 16): lane l holds group l's count of every bucket,
+// loaded as R / 4 16-byte words of its group_cnt row, so that a wave asks for
+// each line of group_cnt once.  Two buckets share a 32-bit word (16-bit fields:
+// a bucket holds at most 4096 tokens here) and one wave prefix sum per pair
+// gives the bucket totals (lane 63) and the counts of the groups before t's
+// group g (lane g - 1).  The bucket offsets are the running sum of the totals.
+// Then as token_rows: lane r holds row(t, r).  The loads are issued by
+// load_group_counts, the rows computed by token_rows_from_counts.
+template <int RB>
+struct GroupCounts {
+    u32x4 c[RB / 4];  // lane l: buckets 4q..4q+3 of group l
+    uint64_t gm;      // lane l: token_mask of token 64 g + l
+};
+
+template <int RB>
+__device__ __forceinline__ GroupCounts<RB> load_group_counts(const uint64_t* token_mask,
+                                                             const int32_t* group_cnt, int T,
+                                                             int R, int t, int lane) {
+    const int ng = num_groups(T);
+    const __amdgpu_buffer_rsrc_t gc = word_buffer(group_cnt, ng * R);
+    const unsigned int lbase = lane < ng ? (unsigned int)(lane * R) : kNoWord;
+    GroupCounts<RB> gcnt;
+#pragma unroll
+    for (int q = 0; q < RB / 4; ++q) {
+        const unsigned int i = 4 * q < R ? lbase + (unsigned int)(4 * q) : kNoWord;
+        gcnt.c[q] = __builtin_amdgcn_raw_buffer_load_b128(gc, (int)(i * 4u), 0, 0);
+    }
+    const int tj = ((t >> 6) << 6) + lane;
+    gcnt.gm = tj < T ? token_mask[tj] : 0ull;
+    return gcnt;
+}
+
+template <int RB>
+__device__ __forceinline__ TokenRows token_rows_from_counts(const GroupCounts<RB>& gcnt, int R,
+                                                            int64_t rows, int t, int lane) {
+    const int g = t >> 6;
+    const int j = t & 63;
+    const uint64_t gm = gcnt.gm;
+    int base = 0, pfx = 0, run = 0;
+#pragma unroll
+    for (int p = 0; p < RB; p += 2) {
+        if (p >= R) break;  // wave-uniform
+        const uint32_t lo = gcnt.c[p >> 2][p & 3], hi = gcnt.c[p >> 2][(p & 3) + 1];
+        const uint32_t incl = (uint32_t)wave_inclusive_sum((int)(lo | (hi << 16)));
+        const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+        const uint32_t pre = g > 0 ? __builtin_amdgcn_readlane(incl, g - 1) : 0u;
+        if (lane == p) {
+            base = run;
+            pfx = (int)(pre & 0xffffu);
+        }
+        run += (int)(tot & 0xffffu);
+        if (lane == p + 1) {
+            base = run;
+            pfx = (int)(pre >> 16);
+        }
+        run += (int)(tot >> 16);
+    }
+    const uint64_t mine = readlane64(gm, j);
+    const uint64_t below = (j == 0) ? 0ull : (~0ull >> (64 - j));
+    int pos = -1;
+    uint64_t m = mine;
+    while (m) {
+        const int r = __builtin_ctzll(m);
+        m &= m - 1;
+        const int c = __popcll(__ballot((gm >> r) & 1u) & below);
+        if (lane == r) pos = pfx + c;
+    }
+    const int64_t row64 = pos >= 0 ? (int64_t)base + pos : -1;
+    const int row = (row64 >= 0 && row64 < rows) ? (int)row64 : -1;
+    return TokenRows{row, pos, mine, __ballot(row >= 0)};
+}
+
+// The workgroup that finishes the handle runs the layout's straight-line
+// finishing step for one chunk of 64 groups and 16 tiles: its LDS holds the
+// group prefixes of up to 64 groups of 16 buckets.
+using FirstLds = LayoutShared<kGroup * 16, 0>;
+constexpr int kFirstChunks = 1;
+constexpr int kFirstTiles = 16;
+
+// The first dispatch on a capacity-mode handle prepared with the layout's
+// partials only.  Workgroup 0 finishes the handle (every prefix, total and
+// channel matrix, as the layout's finishing step); every other workgroup is a
+// pack_bf16_kernel workgroup that finds its token's rows from the partials
+// (token_rows_from_counts) instead of from the prefixes, so nothing in this
+// launch waits for workgroup 0.
+template <int CPL, int RB>
+__global__ __launch_bounds__(kRowThreads) void pack_bf16_first_kernel(
+    LayoutArgs la, int ntiles, const u32x4* __restrict__ x, int H8, RowSplit rs, int64_t rows,
+    HandleRows hr, u32x4* __restrict__ recv_x, const float* __restrict__ topk_weights,
+    int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_topk_weights) {
+    __shared__ FirstLds s;
+    if (blockIdx.x == 0) {
+        layout_finish_fast<kFirstChunks, kFirstTiles>(la, ntiles, s, (const TileToken*)nullptr);
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((blockIdx.x - 1) * kRowWavesPerBlock +
+                                                 (threadIdx.x >> 6));
+    const int t = (int)rs.div.div((uint32_t)w);
+    const int part = w - t * rs.split;
+    if (t >= la.T) return;
+    const int c_begin = part * rs.per;
+    const int c_end = min(c_begin + rs.per, H8);
+    // The counts go out first: their prefix sums run while the row is in flight.
+    const GroupCounts<RB> gcnt =
+        load_group_counts<RB>(la.token_mask, la.group_cnt, la.T, la.R, t, lane);
+    u32x4 v[CPL];
+    pack_bf16_load_nobranch<CPL>(x, t, H8, c_begin, c_end, lane, v);
+    const TokenRows d = token_rows_from_counts<RB>(gcnt, la.R, rows, t, lane);
+    pack_bf16_store<CPL>(v, d, t, part, H8, c_begin, c_end, lane, la.R, hr, recv_x, la.topk_idx,
+                         topk_weights, la.K, la.E, la.P, la.bucket, recv_topk_idx,
+                         recv_topk_weights);
 }
 
 // ---- FP8 -------------------------------------------------------------------
@@ -464,6 +616,46 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
         default: MOEDX_PACK(16);
     }
 #undef MOEDX_PACK
+}
+
+bool pack_first_fits(int T, int R, int E, int C) {
+    return layout_fast_finish_fits<kFirstChunks, kFirstTiles>(T, R, E, C, num_tiles(T), true,
+                                                              FirstLds::kGp) &&
+           R <= 16 && R % 4 == 0;
+}
+
+hipError_t launch_pack_bf16_first(const LayoutArgs& la, const void* x, int H, int64_t rows,
+                                  const HandleRows& hr, void* recv_x, const float* topk_weights,
+                                  int64_t* recv_topk_idx, float* recv_topk_weights,
+                                  const Launch& L) {
+    const int T = la.T;
+    const int H8 = H / 8;
+    const int split = pack_split(H8, kWaveChunks);
+    const RowSplit rs = make_row_split(H8, split);
+    const dim3 grid(1 + pack_blocks(T, split)), block(kRowThreads);
+    const u32x4* xs = static_cast<const u32x4*>(x);
+    u32x4* rx = static_cast<u32x4*>(recv_x);
+    const int ntiles = num_tiles(T);
+#define MOEDX_FIRST(N, B)                                                                       \
+    return launch_kernel(pack_bf16_first_kernel<N, B>, grid, block, L, la, ntiles, xs, H8, rs, \
+                         rows, hr, rx, topk_weights, recv_topk_idx, recv_topk_weights)
+#define MOEDX_FIRST_CPL(B)              \
+    switch (pick_cpl(rs.per)) {         \
+        case 1: MOEDX_FIRST(1, B);      \
+        case 2: MOEDX_FIRST(2, B);      \
+        case 4: MOEDX_FIRST(4, B);      \
+        case 7: MOEDX_FIRST(7, B);      \
+        case 8: MOEDX_FIRST(8, B);      \
+        case 14: MOEDX_FIRST(14, B);    \
+        default: MOEDX_FIRST(16, B);    \
+    }
+    if (la.R <= 8) {
+        MOEDX_FIRST_CPL(8)
+    } else {
+        MOEDX_FIRST_CPL(16)
+    }
+#undef MOEDX_FIRST_CPL
+#undef MOEDX_FIRST
 }
 
 hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,

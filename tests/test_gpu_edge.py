@@ -208,3 +208,21 @@ def test_large_batch_global_scan_paths(oracle):
 ], ids=lambda v: str(v))
 def test_layout_finishing_step_limits(oracle, T, E, K, R, C):
     run_case(oracle, _rand(T, E, K, p_empty=0.02, seed=T + R + C), 8, E, R, C, capacity=(T % 2 == 0))
+
+
+# The first capacity-mode dispatch finishes the handle in its own launch when
+# T <= 4096 and R is a multiple of 4 up to 16 (it reads its receive rows from
+# the layout's partials); otherwise a separate finishing step runs before the
+# pack.  Shapes on both sides: the 64-group limit, ragged groups, R = 4, 8, 12,
+# 16 and R not a multiple of 4.
+@pytest.mark.parametrize("T,E,K,R,C", [
+    (4096, 64, 8, 8, 8),      # 64 groups, one launch
+    (4097, 64, 8, 8, 8),      # 65 groups: separate finishing step
+    (333, 48, 6, 4, 3),       # ragged last group, R = 4
+    (1500, 96, 8, 12, 6),     # R = 12 (16-bucket lookup, 4 buckets unused)
+    (4096, 256, 8, 16, 20),   # R = 16 at 64 groups
+    (777, 36, 5, 6, 4),       # R = 6: separate finishing step
+    (64, 16, 4, 8, 2),        # one group
+], ids=lambda v: str(v))
+def test_first_capacity_dispatch_one_launch(oracle, T, E, K, R, C):
+    run_case(oracle, _rand(T, E, K, p_empty=0.05, seed=3 * T + R), 16, E, R, C, capacity=True)
