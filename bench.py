@@ -78,7 +78,7 @@ TRAFFIC_SOURCES = {"layout": "layout.hip", "get_layout": "layout.hip", "pack": "
                    "combine_fp8_skewed": "combine.hip", "combine_reuse": "combine.hip",
                    "ll_dispatch": "ll.hip", "ll_combine": "ll.hip"}
 # headers every kernel source includes: a change there changes the kernels too
-SHARED_HEADERS = ("launch.h", "rows.h", "fastdiv.h")
+SHARED_HEADERS = ("launch.h", "rows.h", "fastdiv.h", "layout_core.h")
 
 
 def source_digest(src):
@@ -290,6 +290,7 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
                 "reps": reps}
 
     def handle_rows(buf, h, ws):
+        C.check(C.moedx_handle_finish(buf.ctx, h, exr))  # capacity mode: N comes with the prefixes
         dev_n = ctypes.c_void_p()
         shape = (ctypes.c_int64 * 2)()
         C.check(C.moedx_handle_tensor(h, C.MOEDX_T_NUM_RECV, ctypes.byref(dev_n), shape))

@@ -96,6 +96,7 @@ SIGNATURES = {
     "moedx_handle_num_recv": (_I, [_P, ctypes.POINTER(_I64)]),
     "moedx_handle_recv_tokens_per_expert": (_I, [_P, _P]),
     "moedx_handle_tensor": (_I, [_P, _I, _PP, ctypes.POINTER(_I64)]),
+    "moedx_handle_finish": (_I, [_P, _P, _EX]),
     "moedx_handle_destroy": (_I, [_P]),
     "moedx_dispatch": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _EX]),
     "moedx_dispatch_fp8": (_I, [_P, _P, _P, _I, _I, ctypes.POINTER(moedx_fp8), _P, _P, _EX]),

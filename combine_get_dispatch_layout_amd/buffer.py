@@ -107,12 +107,22 @@ class Handle:
     holds its arrays (kept alive as long as the handle)."""
 
     def __init__(self, ptr: int, workspace: torch.Tensor, T: int, K: int, low_latency: bool,
-                 capacity: int = 0):
+                 capacity: int = 0, buffer: "Optional[Buffer]" = None):
         self.ptr = ptr
         self.workspace = workspace
         self.T, self.K = T, K
         self.low_latency = low_latency
         self.capacity = capacity
+        self.buffer = buffer  # the Buffer whose ctx prepared it (normal handles)
+
+    def finish(self) -> None:
+        """Write a capacity-mode handle's prefixes, totals and N on the current
+        stream now rather than on its first dispatch or combine (nothing runs
+        when they are already written)."""
+        if self.low_latency or self.buffer is None:
+            return
+        ex = C.make_exec(_stream(), None, None, C.MOEDX_ASYNC)
+        C.check(C.moedx_handle_finish(self.buffer.ctx, self.ptr, ctypes.byref(ex)))
 
     def tensor(self, which: int, dtype: torch.dtype) -> torch.Tensor:
         """View of one handle array (MOEDX_T_*) inside the workspace."""
@@ -139,6 +149,7 @@ class Handle:
 
     # handle fields named on the handle-reuse page
     def fields(self) -> dict:
+        self.finish()
         if self.low_latency:
             return {"src_idx": self.tensor(C.MOEDX_T_LL_SRC_IDX, torch.int32),
                     "slot_of": self.tensor(C.MOEDX_T_LL_SLOT_OF, torch.int32)}
@@ -245,7 +256,7 @@ class Buffer:
         ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream, no_sync)
         C.check(C.moedx_dispatch_prepare(self.ctx, _ptr(topk_idx), T, K, _ptr(ws), nbytes.value,
                                          num_worst_tokens, ctypes.byref(h), ctypes.byref(ex)))
-        return Handle(h.value, ws, T, K, False, num_worst_tokens), self._event(done)
+        return Handle(h.value, ws, T, K, False, num_worst_tokens, self), self._event(done)
 
     def dispatch(self, x, handle: Optional[Handle] = None, num_tokens_per_rank=None,
                  num_tokens_per_rdma_rank=None, is_token_in_rank=None, num_tokens_per_expert=None,

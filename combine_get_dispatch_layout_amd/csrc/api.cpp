@@ -587,6 +587,23 @@ int moedx_handle_tensor(const moedx_handle* h, int which, const void** dev, int6
     return MOEDX_OK;
 }
 
+int moedx_handle_finish(moedx_ctx* ctx, const moedx_handle* h, const moedx_exec* exec) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!h || h->kind != kNormal) return fail(MOEDX_EINVAL, "a normal handle is required");
+    if (h->E != ctx->E || h->R != ctx->R || h->C != ctx->C)
+        return fail(MOEDX_ESTATE, "handle was prepared on a ctx with a different E/R/C");
+    Exec ex;
+    if (int rc = exec_begin(ctx, exec, &ex)) return rc;
+    if (h->prefixes_pending) {
+        HIP_OR_FAIL(launch_layout_finish(handle_layout_args(ctx, h, nullptr), ex.launch()));
+        ctx->stats.layout_launches += 1;
+        h->prefixes_pending = false;
+    } else {
+        HIP_OR_FAIL(ex.no_kernel());
+    }
+    return exec_end(ex);
+}
+
 int moedx_handle_destroy(moedx_handle* h) {
     delete h;
     return MOEDX_OK;

@@ -230,6 +230,13 @@ MOEDX_API int moedx_handle_recv_tokens_per_expert(const moedx_handle *h, int32_t
  * capacity in capacity mode (rows past N are unspecified). */
 MOEDX_API int moedx_handle_tensor(const moedx_handle *h, int which, const void **dev,
                                   int64_t shape[2]);
+/* Write a capacity-mode handle's prefixes, totals and N (the prefix matrices
+ * and counts of [HR] What the Handle Contains) now, on exec's stream, instead
+ * of on the handle's first dispatch or combine (moedx_dispatch_prepare).  No
+ * kernel runs when they are already written or enqueued (exact mode, or after
+ * a first use).  Normal handles only. */
+MOEDX_API int moedx_handle_finish(moedx_ctx *ctx, const moedx_handle *h,
+                                  const moedx_exec *exec);
 MOEDX_API int moedx_handle_destroy(moedx_handle *h);
 
 /* ---- dispatch (token pack) ([GCU] dispatch_forward; [HR] Fast Path) ------- */

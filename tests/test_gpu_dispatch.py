@@ -223,3 +223,39 @@ def test_training_pairings(oracle, w, tokens):
                                     recv_topk_weights=grad_rtw.numpy())
     assert_bf16_within_1ulp("dispatch_backward x", np_(gx), want_x)
     assert_equal("dispatch_backward weights", np_(gw).view(np.uint32), want_w.view(np.uint32))
+
+
+@pytest.mark.parametrize("w", [wl.TINY, wl.PREFILL], ids=lambda w: w.name)
+def test_capacity_handle_finished_before_first_use(oracle, w):
+    """A capacity-mode handle read before any dispatch: the explicit finish
+    writes its prefixes, totals and N (once; a second finish runs nothing),
+    and the first dispatch that follows packs from those prefixes."""
+    dev = device()
+    print(f"[finish] {w.name}", flush=True)
+    inp = wl.make_inputs(w)
+    E, R, C, T, K = w.experts, w.ranks, _channels(w), w.tokens, w.topk
+    ref = oracle_first_dispatch(oracle, inp, E, R, C)
+    N = ref.prefix.num_recv
+    buf = make_buffer(E, R, C, T)
+    h, _ = buf.prepare(inp.topk_idx.to(dev), T * min(K, R))
+    before = buf.stats()
+    h.finish()
+    h.finish()
+    f = h.fields()
+    torch.cuda.synchronize()
+    assert buf.stats()["layout_launches"] == before["layout_launches"] + 1
+    assert_equal("num_tokens_per_rank", np_(f["num_tokens_per_rank"]), ref.layout.num_tokens_per_rank)
+    assert_equal("num_tokens_per_expert", np_(f["num_tokens_per_expert"]),
+                 ref.layout.num_tokens_per_expert)
+    assert_equal("rank_prefix_matrix", np_(f["rank_prefix_matrix"]), ref.prefix.rank_prefix_matrix)
+    assert_equal("channel_prefix_matrix", np_(f["channel_prefix_matrix"]),
+                 ref.prefix.channel_prefix_matrix)
+    assert_equal("recv_channel_prefix_matrix", np_(f["recv_channel_prefix_matrix"]),
+                 ref.prefix.recv_channel_prefix_matrix)
+    assert int(np_(f["num_recv"])[0]) == N
+    recv, _, _, _, h2, _ = buf.dispatch(inp.x.to(dev), handle=h)
+    torch.cuda.synchronize()
+    assert h2 is h
+    assert buf.stats()["layout_launches"] == before["layout_launches"] + 1
+    check_handle(h, ref, N)
+    assert_equal("recv_x", np_(recv)[:N], ref.recv_x)
