@@ -506,10 +506,13 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
     int rc = exec_begin(ctx, exec, &ex);
     hipError_t e = hipSuccess;
     if (rc == MOEDX_OK) {
-        // Capacity mode: the partials only; the first dispatch (or combine)
-        // on the handle finishes the prefixes.
+        // Capacity mode, where a first bf16 dispatch can finish the prefixes
+        // in its own launch: the partials only, and the first dispatch (or
+        // combine) on the handle finishes them.  Elsewhere the layout kernel
+        // writes every prefix itself.
         const LayoutArgs a = handle_layout_args(ctx, h, topk_idx);
-        const bool partials = capacity_rows > 0 && T > 0;
+        const bool partials =
+            capacity_rows > 0 && T > 0 && pack_first_fits(T, h->R, h->E, h->C);
         e = partials ? launch_layout_partials(a, ex.launch()) : launch_layout(a, ex.launch());
         h->prefixes_pending = partials;
         if (e != hipSuccess) rc = hip_fail(e, "layout launch");

@@ -207,13 +207,14 @@ MOEDX_API int moedx_handle_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  *     moedx_handle_num_recv / moedx_handle_recv_tokens_per_expert work.
  *   capacity_rows  > 0 (capacity mode, num_worst_tokens of [GCU]): no host
  *     wait; capacity_rows must be >= T * min(K, R) so that every row fits;
- *     N stays on the device (MOEDX_T_NUM_RECV).  Only the layout's
- *     per-token outputs and partial counts run here; the prefixes, totals and
- *     N (rank and channel prefix matrices, num_tokens_per_rank/expert,
- *     MOEDX_T_NUM_RECV) are written on the stream of the handle's first
- *     moedx_dispatch, moedx_dispatch_fp8 or moedx_combine, ahead of or by its
- *     kernel: read them after that call.  In exact mode the call blocks on
- *     the host even when exec->done is given.
+ *     N stays on the device (MOEDX_T_NUM_RECV).  For T <= 4096 and R a
+ *     multiple of 4 up to 16 only the layout's per-token outputs and partial
+ *     counts run here; the prefixes, totals and N (rank and channel prefix
+ *     matrices, num_tokens_per_rank/expert, MOEDX_T_NUM_RECV) are written on
+ *     the stream of the handle's first moedx_dispatch (by its pack kernel,
+ *     for bf16), moedx_dispatch_fp8, moedx_combine or moedx_handle_finish:
+ *     read them after that call.  In exact mode the call blocks on the host
+ *     even when exec->done is given.
  * *out receives a new handle (moedx_handle_destroy frees it). */
 MOEDX_API int moedx_dispatch_prepare(moedx_ctx *ctx, const int64_t *topk_idx, int T, int K,
                                      void *workspace, size_t workspace_bytes,

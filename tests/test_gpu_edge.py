@@ -212,16 +212,16 @@ def test_layout_finishing_step_limits(oracle, T, E, K, R, C):
 
 # The first capacity-mode dispatch finishes the handle in its own launch when
 # T <= 4096 and R is a multiple of 4 up to 16 (it reads its receive rows from
-# the layout's partials); otherwise a separate finishing step runs before the
-# pack.  Shapes on both sides: the 64-group limit, ragged groups, R = 4, 8, 12,
-# 16 and R not a multiple of 4.
+# the layout's partials); otherwise the layout writes every prefix at prepare.
+# Shapes on both sides: the 64-group limit, ragged groups, R = 4, 8, 12, 16
+# and R not a multiple of 4.
 @pytest.mark.parametrize("T,E,K,R,C", [
     (4096, 64, 8, 8, 8),      # 64 groups, one launch
-    (4097, 64, 8, 8, 8),      # 65 groups: separate finishing step
+    (4097, 64, 8, 8, 8),      # 65 groups: prefixes at prepare
     (333, 48, 6, 4, 3),       # ragged last group, R = 4
     (1500, 96, 8, 12, 6),     # R = 12 (16-bucket lookup, 4 buckets unused)
     (4096, 256, 8, 16, 20),   # R = 16 at 64 groups
-    (777, 36, 5, 6, 4),       # R = 6: separate finishing step
+    (777, 36, 5, 6, 4),       # R = 6: prefixes at prepare
     (64, 16, 4, 8, 2),        # one group
 ], ids=lambda v: str(v))
 def test_first_capacity_dispatch_one_launch(oracle, T, E, K, R, C):
