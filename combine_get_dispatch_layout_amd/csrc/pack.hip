@@ -30,9 +30,6 @@
 #ifndef MOEDX_PACK_FP8_WAVE_BLOCKS
 #define MOEDX_PACK_FP8_WAVE_BLOCKS 8  // 1x128 blocks of an FP8 row per wave (at most)
 #endif
-#ifndef MOEDX_PACK_NT_LOAD
-#define MOEDX_PACK_NT_LOAD 0  // streaming (non-temporal) loads of x
-#endif
 #ifndef MOEDX_PACK_NT_STORE
 #define MOEDX_PACK_NT_STORE 1  // streaming, write-through stores of receive rows
 #endif
@@ -51,14 +48,6 @@ constexpr int kWaveBlocks = MOEDX_PACK_FP8_WAVE_BLOCKS;
 static_assert(kWaveChunks >= 1 && kWaveChunks <= 128, "bf16 / byte parts: at most 2 chunks per lane");
 static_assert(kWaveBlocks >= 1 && kWaveBlocks <= 8, "FP8 parts: at most 2 chunks per lane");
 
-template <typename V>
-__device__ __forceinline__ V load_row(const V* p) {
-#if MOEDX_PACK_NT_LOAD
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
-}
 
 // 16-byte receive-row stores: streaming (nt) and written through to memory at
 // system scope (sc0 sc1), which measured about 1 us faster than plain
@@ -85,29 +74,18 @@ __device__ __forceinline__ void write_handle_rows(const HandleRows& hr, const To
 // loads are issued by pack_bf16_load (all of a lane's chunks in flight at
 // once), before the row lookup; pack_bf16_store writes the part to each of the
 // token's rows d, plus the handle rows and recv_topk_* from the first part.
+// Chunks [c_begin, c_end) of one row, lane l taking c_begin + 64 i + l into
+// v[i] (all of a lane's chunks in flight at once), as buffer loads: chunks
+// past c_end read 0 and no load sits behind a branch, so a wait for loads
+// issued before these (the row lookup's) need not wait for these.
 template <int CPL>
-__device__ __forceinline__ void pack_bf16_load(const u32x4* __restrict__ x, int t, int H8,
-                                               int c_begin, int c_end, int lane, u32x4 (&v)[CPL]) {
-    const u32x4* src = x + (int64_t)t * H8;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = c_begin + i * 64 + lane;
-        if (c < c_end) v[i] = load_row(src + c);
-    }
-}
-
-// pack_bf16_load as buffer loads over [c_begin, c_end) of the row (chunks past
-// c_end read 0 and are never stored): no load sits behind a branch, so a later
-// wait for loads issued before these need not wait for these.
-template <int CPL>
-__device__ __forceinline__ void pack_bf16_load_nobranch(const u32x4* __restrict__ x, int t,
-                                                        int H8, int c_begin, int c_end, int lane,
-                                                        u32x4 (&v)[CPL]) {
+__device__ __forceinline__ void load_row_part(const u32x4* __restrict__ row, int c_begin, int c_end,
+                                              int lane, u32x4 (&v)[CPL]) {
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<u32x4*>(x + (int64_t)t * H8 + c_begin), (short)0, (c_end - c_begin) * 16,
-        0x00020000);
+        const_cast<u32x4*>(row + c_begin), (short)0, (c_end - c_begin) * 16, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (i * 64 + lane) * 16, 0, 0);
+    for (int i = 0; i < CPL; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (i * 64 + lane) * 16, 0, 0);
 }
 
 template <int CPL>
@@ -162,10 +140,13 @@ __global__ __launch_bounds__(kRowThreads) void pack_bf16_kernel(
     if (t >= T) return;
     const int c_begin = part * rs.per;
     const int c_end = min(c_begin + rs.per, H8);
-    // One pass (CPL * 64 >= rs.per): the row loads go out before the row lookup.
+    // One pass (CPL * 64 >= rs.per).  The lookup's loads go out first, then
+    // the row loads (no branch), so the lookup waits for its own loads only
+    // and runs while the row is in flight.
+    const RowLoads lk = token_rows_load(rm, t, lane);
     u32x4 v[CPL];
-    pack_bf16_load<CPL>(x, t, H8, c_begin, c_end, lane, v);
-    const TokenRows d = token_rows(rm, t, lane);
+    load_row_part<CPL>(x + (int64_t)t * H8, c_begin, c_end, lane, v);
+    const TokenRows d = token_rows_from(rm, lk, t, lane);
     pack_bf16_store<CPL>(v, d, t, part, H8, c_begin, c_end, lane, rm.R, hr, recv_x, topk_idx,
                          topk_weights, K, E, P, bucket, recv_topk_idx, recv_topk_weights);
 }
@@ -280,7 +261,7 @@ __global__ __launch_bounds__(kRowThreads) void pack_bf16_first_kernel(
     const GroupCounts<RB> gcnt =
         load_group_counts<RB>(la.token_mask, la.group_cnt, la.T, la.R, t, lane);
     u32x4 v[CPL];
-    pack_bf16_load_nobranch<CPL>(x, t, H8, c_begin, c_end, lane, v);
+    load_row_part<CPL>(x + (int64_t)t * H8, c_begin, c_end, lane, v);
     const TokenRows d = token_rows_from_counts<RB>(gcnt, la.R, rows, t, lane);
     pack_bf16_store<CPL>(v, d, t, part, H8, c_begin, c_end, lane, la.R, hr, recv_x, la.topk_idx,
                          topk_weights, la.K, la.E, la.P, la.bucket, recv_topk_idx,
@@ -360,14 +341,12 @@ __global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(
     const int G = H8 >> 4;  // blocks per row; parts hold whole blocks (rs counts blocks)
     const int c_begin = part * rs.per * 16;
     const int c_end = min(part * rs.per + rs.per, G) * 16;
-    // One pass (CPL * 64 >= 16 * rs.per): the row loads go out before the row lookup.
+    // One pass (CPL * 64 >= 16 * rs.per): the lookup's loads, then the row
+    // loads (chunks past c_end read 0).
+    const RowLoads lk = token_rows_load(rm, t, lane);
     u32x4 v[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = c_begin + i * 64 + lane;
-        v[i] = c < c_end ? load_row(src + c) : u32x4{0u, 0u, 0u, 0u};
-    }
-    const TokenRows d = token_rows(rm, t, lane);
+    load_row_part<CPL>(src, c_begin, c_end, lane, v);
+    const TokenRows d = token_rows_from(rm, lk, t, lane);
     if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     {
         const int base = c_begin;
@@ -512,14 +491,11 @@ __global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(
     const u32x4* src = codes + (int64_t)t * C16;
     const int c_begin = part * rs.per;
     const int c_end = min(c_begin + rs.per, C16);
-    // One pass (CPL * 64 >= rs.per): the row loads go out before the row lookup.
+    // One pass (CPL * 64 >= rs.per): the lookup's loads, then the row loads.
+    const RowLoads lk = token_rows_load(rm, t, lane);
     u32x4 v[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = c_begin + i * 64 + lane;
-        if (c < c_end) v[i] = load_row(src + c);
-    }
-    const TokenRows d = token_rows(rm, t, lane);
+    load_row_part<CPL>(src, c_begin, c_end, lane, v);
+    const TokenRows d = token_rows_from(rm, lk, t, lane);
     if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
     {
         const int base = c_begin;

@@ -28,32 +28,57 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// t must be wave-uniform and < rm.T.
-__device__ __forceinline__ TokenRows token_rows(const RowMap& rm, int t, int lane) {
+// The loads of a row lookup: the group's token masks and, on lanes r < R,
+// what bucket r's base and group prefix are made of (nothing is computed from
+// them here, so that no wait sits before the caller's next loads).
+struct RowLoads {
+    uint64_t gm;  // lane l: token_mask of token 64 g + l (0 past T)
+    int rp;       // lane r < R: rank_prefix_matrix[r]
+    int cnt;      // lane r < R: num_tokens_per_rank[r]
+    int pfx;      // lane r < R: group_prefix[g][r]
+};
+
+// Issues the loads only (t wave-uniform, < rm.T); a kernel that issues its
+// row loads after this call lets the lookup's wait skip them.
+__device__ __forceinline__ RowLoads token_rows_load(const RowMap& rm, int t, int lane) {
     const int g = t >> 6;
-    const int j = t & 63;
     const int tj = (g << 6) + lane;
-    const uint64_t gm = tj < rm.T ? rm.token_mask[tj] : 0ull;
-    const uint64_t mine = readlane64(gm, j);
-    int base = 0, pfx = 0;
+    RowLoads l;
+    l.gm = tj < rm.T ? rm.token_mask[tj] : 0ull;
+    l.rp = 0;
+    l.cnt = 0;
+    l.pfx = 0;
     if (lane < rm.R) {
-        base = rm.rank_prefix_matrix[lane] - rm.num_tokens_per_rank[lane];
-        pfx = rm.group_prefix[(int64_t)g * rm.R + lane];
+        l.rp = rm.rank_prefix_matrix[lane];
+        l.cnt = rm.num_tokens_per_rank[lane];
+        l.pfx = rm.group_prefix[(int64_t)g * rm.R + lane];
     }
+    return l;
+}
+
+__device__ __forceinline__ TokenRows token_rows_from(const RowMap& rm, const RowLoads& l, int t,
+                                                     int lane) {
+    const int j = t & 63;
+    const uint64_t mine = readlane64(l.gm, j);
     const uint64_t below = (j == 0) ? 0ull : (~0ull >> (64 - j));
     int pos = -1;
     uint64_t m = mine;
     while (m) {
         const int r = __builtin_ctzll(m);
         m &= m - 1;
-        const int c = __popcll(__ballot((gm >> r) & 1u) & below);
-        if (lane == r) pos = pfx + c;
+        const int c = __popcll(__ballot((l.gm >> r) & 1u) & below);
+        if (lane == r) pos = l.pfx + c;
     }
     // A row past the receive buffer (impossible for a consistent handle) is
     // dropped rather than written: the kernels stay inside their buffers.
-    const int64_t row64 = pos >= 0 ? (int64_t)base + pos : -1;
+    const int64_t row64 = pos >= 0 ? (int64_t)(l.rp - l.cnt) + pos : -1;
     const int row = (row64 >= 0 && row64 < rm.rows) ? (int)row64 : -1;
     return TokenRows{row, pos, mine, __ballot(row >= 0)};
+}
+
+// t must be wave-uniform and < rm.T.
+__device__ __forceinline__ TokenRows token_rows(const RowMap& rm, int t, int lane) {
+    return token_rows_from(rm, token_rows_load(rm, t, lane), t, lane);
 }
 
 }  // namespace moedx
