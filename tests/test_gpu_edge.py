@@ -214,10 +214,15 @@ def test_layout_finishing_step_limits(oracle, T, E, K, R, C):
 # T <= 4096 and R is a multiple of 4 up to 16 (it reads its receive rows from
 # the layout's partials); otherwise the layout writes every prefix at prepare.
 # Shapes on both sides: the 64-group limit, ragged groups, R = 4, 8, 12, 16
-# and R not a multiple of 4.
+# and R not a multiple of 4, and larger batches up to the layout's fast
+# finishing limits.
 @pytest.mark.parametrize("T,E,K,R,C", [
     (4096, 64, 8, 8, 8),      # 64 groups, one launch
     (4097, 64, 8, 8, 8),      # 65 groups: prefixes at prepare
+    (8192, 64, 8, 8, 8),      # 128 groups: prefixes at prepare
+    (8193, 64, 8, 8, 8),      # 129 groups
+    (6000, 96, 8, 12, 6),     # ragged last group, R = 12
+    (8192, 256, 8, 16, 20),   # R = 16 at 128 groups, 32 tiles per expert thread
     (333, 48, 6, 4, 3),       # ragged last group, R = 4
     (1500, 96, 8, 12, 6),     # R = 12 (16-bucket lookup, 4 buckets unused)
     (4096, 256, 8, 16, 20),   # R = 16 at 64 groups
