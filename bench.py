@@ -5,17 +5,21 @@ Workload: 4096 tokens x 7168 hidden bf16, 256 experts top-8 with group-limited
 routing (8 groups of 32 experts, 4 groups kept), 8 logical rank buckets, 24
 channels; seeded synthetic inputs (x ~ N(0,1) in bf16, softmax gate weights).
 
-One step = layout (counts, masks and every prefix) + bf16 pack (with
-recv_topk_idx / recv_topk_weights and the handle's send_head / recv_src_idx) +
-gate-weighted combine of the identity expert's rows, in capacity mode (no host
-synchronisation inside the step); each is one kernel launch.
+One step = the dispatch — the layout's counts and masks at prepare, then the
+bf16 first pack on that handle, which also finishes every prefix (with
+recv_topk_idx / recv_topk_weights and the handle's send_head / recv_src_idx) —
++ the gate-weighted combine of the identity expert's rows, in capacity mode (no
+host synchronisation inside the step); three kernel launches.
 
-Timing: each op is launched back to back `--steps` times between two HIP
-events on its stream, rotating over enough buffer sets that every launch reads
-its input from HBM: at least twice the 256 MB Infinity Cache is read between
-two reads of one set (the cache otherwise serves a good part of a just-written
-receive buffer, and keeps up to four copies of x while the pack's streaming
-stores pass); a step's time is the sum of the three per-op means.  The value is algorithmic bytes / step time (GB/s); tokens/s and
+Timing: each op (dispatch on a fresh handle, combine) runs back to back
+`--steps` times between two HIP events on its stream, rotating over enough
+buffer sets that every launch reads its input from HBM: at least twice the
+256 MB Infinity Cache is read between two reads of one set (the cache otherwise
+serves a good part of a just-written receive buffer, and keeps up to four
+copies of x while the pack's streaming stores pass); a step's time is the sum
+of the two per-op means.  Each kernel's own duration (events stamped at its
+start and end) is reported beside it.  The value is algorithmic bytes / step
+time (GB/s); tokens/s and
 the fraction of the 8 TB/s HBM peak are reported beside it, with whole steps
 back to back (cache-assisted, labelled as such) and the CPU oracle timed on the
 same workload as a baseline.
