@@ -177,9 +177,15 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     int t, part;
     row_part(rs, &t, &part);
     if (t >= T) return;
-    const int base = lane < rm.R ? rm.rank_prefix_matrix[lane] - rm.num_tokens_per_rank[lane] : 0;
+    // Every lookup load goes out before the first wait: bucket r's base is
+    // formed only after the item's loads are issued.
+    int rp = 0, cnt = 0;
+    if (lane < rm.R) {
+        rp = rm.rank_prefix_matrix[lane];
+        cnt = rm.num_tokens_per_rank[lane];
+    }
     const ItemLoads ld = item_loads(rm, slot_bucket, gate_weights, K, t, lane);
-    const Visits vs = item_visits(ld, base, rm.rows, t, lane, gate_weights != nullptr);
+    const Visits vs = item_visits(ld, rp - cnt, rm.rows, t, lane, gate_weights != nullptr);
 
     // This wave's chunks; lanes past the row end read a valid chunk and store nothing.
     const int c_begin = part * CPL * 64;
