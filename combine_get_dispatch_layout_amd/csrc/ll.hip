@@ -57,6 +57,19 @@ constexpr int kVisitBatch = 8;  // slot rows whose loads one combine pass issues
 
 // grid = T * slices (+1): workgroup b < T * slices handles token b / slices,
 // row slice b % slices; the extra last workgroup writes every expert's count.
+// cnt[k] += entries among v (kCountBatch per thread) equal to lane k's expert.
+__device__ __forceinline__ void count_matches(const int64_t (&v)[kCountBatch], int64_t ek, int K,
+                                              int32_t (&cnt)[kMaxTopk]) {
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k) {
+        if (k < K) {
+            const int64_t e = __builtin_amdgcn_readlane((int)ek, k);
+#pragma unroll
+            for (int b = 0; b < kCountBatch; ++b) cnt[k] += __popcll(__ballot(v[b] == e && e >= 0));
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void ll_dispatch_kernel(
     const u32x4* __restrict__ x, const int64_t* __restrict__ topk_idx, int T, int K, int H8,
     int E, int cap, int slices, u32x4* __restrict__ recv_x, int32_t* __restrict__ recv_count,
@@ -80,43 +93,48 @@ __global__ __launch_bounds__(kThreads) void ll_dispatch_kernel(
     }
     const int t = blockIdx.x / slices;
     const int slice = blockIdx.x - t * slices;
-    // This slice's chunk range of x[t]; the first chunk of each thread is
-    // loaded now, so that its latency overlaps the slot counting below.
+    // This slice's chunk range of x[t].
     const int c0 = (int)((int64_t)H8 * slice / slices);
     const int c1 = (int)((int64_t)H8 * (slice + 1) / slices);
     const u32x4* src = x + (int64_t)t * H8;
-    u32x4 first = {0u, 0u, 0u, 0u};
-    if (recv_x != nullptr && c0 + tid < c1) first = __builtin_nontemporal_load(src + c0 + tid);
 
-    // Lane k holds the token's k-th expert (-1 when empty or out of range).
-    int64_t ek = -1;
-    if (lane < K) {
-        const int64_t e = topk_idx[(int64_t)t * K + lane];
-        ek = (e >= 0 && e < E) ? e : -1;
-    }
+    // Lane k < K: the token's k-th entry as loaded (validity is applied after
+    // every load below is issued, so that nothing waits for it before then).
+    int64_t e_raw = -1;
+    if (lane < K) e_raw = topk_idx[(int64_t)t * K + lane];
     // Slot of (t, k) = earlier (token, slot) entries naming the same expert:
     // each pass loads kCountBatch entries per thread, then one ballot per
     // (entry, k) counts the matches of 64 entries at once.
+    const int n_before = t * K;
+    int64_t v[kCountBatch];
+#pragma unroll
+    for (int b = 0; b < kCountBatch; ++b) {
+        const int i = b * kThreads + tid;
+        v[b] = i < n_before ? topk_idx[i] : -2;
+    }
+    // The first chunk of this thread's part of the row goes out after the first
+    // pass's entries, as a streaming buffer load (no branch; nothing past c1 or
+    // without recv_x is read), so that its latency overlaps the counting and
+    // the counting waits for its own loads only.
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4*>(src + c0), (short)0, recv_x != nullptr ? (c1 - c0) * 16 : 0,
+        0x00020000);
+    const u32x4 first = __builtin_amdgcn_raw_buffer_load_b128(xr, tid * 16, 0, 2);
+    __builtin_amdgcn_sched_barrier(0);  // keep every use of the loads above below it
+    // Lane k holds the token's k-th expert (-1 when empty or out of range).
+    const int64_t ek = (e_raw >= 0 && e_raw < E) ? e_raw : -1;
     int32_t cnt[kMaxTopk];
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k) cnt[k] = 0;
-    const int n_before = t * K;
-    for (int i0 = 0; i0 < n_before; i0 += kThreads * kCountBatch) {
-        int64_t v[kCountBatch];
+    // The first pass outside the loop: its waits then leave the row load out.
+    count_matches(v, ek, K, cnt);
+    for (int i0 = kThreads * kCountBatch; i0 < n_before; i0 += kThreads * kCountBatch) {
 #pragma unroll
         for (int b = 0; b < kCountBatch; ++b) {
             const int i = i0 + b * kThreads + tid;
             v[b] = i < n_before ? topk_idx[i] : -2;
         }
-#pragma unroll
-        for (int k = 0; k < kMaxTopk; ++k) {
-            if (k < K) {
-                const int64_t e = __builtin_amdgcn_readlane((int)ek, k);
-#pragma unroll
-                for (int b = 0; b < kCountBatch; ++b)
-                    cnt[k] += __popcll(__ballot(v[b] == e && e >= 0));
-            }
-        }
+        count_matches(v, ek, K, cnt);
     }
     if (lane == 0) {
 #pragma unroll
