@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fp8_codec.h"
 #include "launch.h"
 #include "layout_core.h"
 #include "rows.h"
@@ -273,21 +274,6 @@ __global__ __launch_bounds__(kRowThreads) void pack_bf16_first_kernel(
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Nearest OCP E4M3FN code, ties to even, saturating at +/-448 (code 0x7E);
-// NaN -> 0x7F.  Normal range (|q| >= 2^-6): round the fp32 mantissa to 3 bits
-// with the round-half-even bias and re-bias the exponent from 127 to 7;
-// subnormal range: the code is round-half-even(|q| * 2^9).  Branch-free: both
-// ranges are computed and one is selected.
-__device__ __forceinline__ uint32_t e4m3_code(float q) {
-    const uint32_t u = __float_as_uint(q);
-    const uint32_t mag = u & 0x7fffffffu;
-    const uint32_t rn = (mag + 0x7ffffu + ((mag >> 20) & 1u)) >> 20;
-    const uint32_t cn = min(rn - (120u << 3), 0x7eu);  // unused (wrapped) below 2^-6
-    const uint32_t cs = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
-    const uint32_t c = (mag >= 0x3c800000u ? cn : cs) | ((u >> 24) & 0x80u);
-    return mag > 0x7f800000u ? 0x7fu : c;
-}
-
 // Maximum over the 16 lanes of a DPP row (the lanes of one 1x128 block), by
 // lane permutations within the row: swap neighbours, swap pairs, mirror each
 // half, mirror the row.
@@ -299,30 +285,8 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
     return v;
 }
 
-// Correctly rounded a / s from rs = 1/s (itself correctly rounded): the
-// product's error is removed with one exact residual, r = a - q0 * s by a fused
-// multiply-add, and q0 + r * rs rounds to the IEEE quotient.  This holds for
-// every fp32 divisor significand and every bf16 numerator significand (checked
-// exhaustively; scaling by powers of two is exact), which covers a block's
-// values over its scale away from overflow and underflow.
-__device__ __forceinline__ float quotient(float a, float s, float rs) {
-    const float q0 = a * rs;
-    const float r = __builtin_fmaf(-q0, s, a);
-    return __builtin_fmaf(r, rs, q0);
-}
-
 // Scale modes of the FP8 pack (the values of moedx.h's MOEDX_FP8_SCALE_*).
 enum Fp8Mode { kAmax = 0, kPow2 = 1, kUe8m0 = 2, kTensor = 3 };
-
-// The smallest power of two >= t, for a positive normal or infinite t (inf
-// stays inf).  For t = the correctly rounded a' / 448 this is also the smallest
-// power of two >= the real quotient: t is a power of two only when the real
-// quotient is one (a' has at most 24 significant bits, so a' / 448 is a power
-// of two only for a' = 7 * 2^k and lies far from one otherwise).
-__device__ __forceinline__ float pow2_ceil(float t) {
-    const uint32_t b = __float_as_uint(t);
-    return __uint_as_float((b & 0x7fffffu) ? (b & 0x7f800000u) + 0x800000u : b);
-}
 
 // One 16-byte chunk = 8 bf16 values; 16 consecutive lanes (one DPP row) form
 // one 1x128 block.  Codes are bit-identical to encoding the IEEE quotient
@@ -373,22 +337,18 @@ __global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(
                 // on the device), and |q| never exceeds that bound here (the
                 // per-tensor scale clamps), so no saturation or NaN case
                 // reaches it.
-                constexpr float kFloorScale = 1e-4f / 448.0f;
-                constexpr float kR448 = 1.0f / 448.0f;
                 float rs;
                 if (kMode == kTensor) {
                     s = tensor_s;
                     rs = tensor_rs;
                 } else {
-                    const float sa = ab > __float_as_uint(1e-4f)
-                                         ? quotient(__uint_as_float(ab), 448.0f, kR448)
-                                         : kFloorScale;
+                    const float sa = fp8_block_scale(ab);
                     if (kMode == kAmax) {
                         s = sa;
                         rs = 1.0f / s;
                     } else {  // a power of two: its reciprocal flips the exponent
                         s = pow2_ceil(sa);
-                        rs = __uint_as_float((254u << 23) - __float_as_uint(s));
+                        rs = pow2_reciprocal(s);
                     }
                 }
                 float qs[8];
@@ -401,9 +361,7 @@ __global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(
                     if (kMode == kPow2 || kMode == kUe8m0) {
                         q = a * rs;  // exact
                     } else if (kMode == kTensor) {
-                        // Past 2^30 the quotient saturates whatever its rounding.
-                        const float q0 = a * rs;
-                        q = fminf(q0 < 1073741824.0f ? quotient(a, s, rs) : 448.0f, 448.0f);
+                        q = tensor_quotient(a, s, rs);
                     } else {
                         q = quotient(a, s, rs);
                     }
