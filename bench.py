@@ -314,7 +314,7 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
             x = (inp.x if s is None else wl.fresh_x(w, s)).to(dev)
             ws = torch.empty(nb.value, dtype=torch.uint8, device=dev)
             h = ctypes.c_void_p()
-            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, P(ws), nb.value, cap,
+            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, None, None, None, P(ws), nb.value, cap,
                                              ctypes.byref(h), exr))
             if fp8:
                 recv = torch.empty(cap, H, dtype=torch.uint8, device=dev)
@@ -501,7 +501,7 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
     def first_exact(s):
         def f():
             h = ctypes.c_void_p()
-            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, P(s["ws_exact"]),
+            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, None, None, None, P(s["ws_exact"]),
                                              nb_exact.value, 0, ctypes.byref(h),
                                              ctypes.byref(blocking)))
             C.check(C.moedx_dispatch(buf.ctx, h, P(s["x"]), T, H, C.MOEDX_QUANT_NONE, P(idx),
@@ -651,7 +651,7 @@ def batch_sweep(token_counts, steps, log_fn):
                  "rtw": torch.empty(cap, K, dtype=torch.float32, device=dev),
                  "out": torch.empty(T, H, dtype=torch.bfloat16, device=dev)}
             h = ctypes.c_void_p()
-            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, P(s["ws"]), nb.value, cap,
+            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, None, None, None, P(s["ws"]), nb.value, cap,
                                              ctypes.byref(h), exr))
             s["h"] = h
             sets.append(s)
@@ -665,7 +665,7 @@ def batch_sweep(token_counts, steps, log_fn):
             s = sets[i % nsets]
             if name in ("layout", "dispatch"):
                 h = ctypes.c_void_p()
-                C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, P(s["ws"]), nb.value, cap,
+                C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, None, None, None, P(s["ws"]), nb.value, cap,
                                                  ctypes.byref(h), exr))
                 if name == "dispatch":
                     first_pack(h, s)
@@ -779,7 +779,7 @@ def main():
 
     def prepare(s_, e=exr):
         h = ctypes.c_void_p()
-        C.check(C.moedx_dispatch_prepare(ctx, p_idx, T, K, P(s_["ws"]), nbytes.value, cap,
+        C.check(C.moedx_dispatch_prepare(ctx, p_idx, T, K, None, None, None, P(s_["ws"]), nbytes.value, cap,
                                          ctypes.byref(h), e))
         return h
 
@@ -893,7 +893,7 @@ def main():
 
     def exact_step(s_):
         h_ = ctypes.c_void_p()
-        C.check(C.moedx_dispatch_prepare(ctx, p_idx, T, K, P(ws_exact), nb_exact.value, 0,
+        C.check(C.moedx_dispatch_prepare(ctx, p_idx, T, K, None, None, None, P(ws_exact), nb_exact.value, 0,
                                          ctypes.byref(h_), ctypes.byref(blocking)))
         pack(h_, s_)
         combine(h_, s_, ctypes.byref(blocking))

@@ -57,7 +57,8 @@ class moedx_exec(ctypes.Structure):
 class moedx_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "layout_launches", "pack_launches", "pack_fp8_launches",
-        "combine_launches", "ll_dispatch_launches", "ll_combine_launches", "host_syncs")]
+        "combine_launches", "ll_dispatch_launches", "ll_combine_launches", "host_syncs",
+        "scan_launches")]
 
 
 class moedx_fp8(ctypes.Structure):
@@ -84,6 +85,7 @@ SIGNATURES = {
     "moedx_destroy": (_I, [_P]),
     "moedx_ctx_stats": (_I, [_P, ctypes.POINTER(moedx_stats)]),
     "moedx_ctx_stream": (_I, [_P, _PP]),
+    "moedx_ctx_set_stream": (_I, [_P, _P]),
     "moedx_event_record": (_I, [_PP, _P]),
     "moedx_event_create": (_I, [_PP]),
     "moedx_event_wait": (_I, [_P, _P]),
@@ -92,7 +94,7 @@ SIGNATURES = {
     "moedx_event_destroy": (_I, [_P]),
     "moedx_get_dispatch_layout": (_I, [_P, _P, _I, _I, _P, _P, _P, _EX]),
     "moedx_handle_workspace_bytes": (_I, [_P, _I, _I, _I64, ctypes.POINTER(_SZ)]),
-    "moedx_dispatch_prepare": (_I, [_P, _P, _I, _I, _P, _SZ, _I64, _PP, _EX]),
+    "moedx_dispatch_prepare": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _SZ, _I64, _PP, _EX]),
     "moedx_handle_num_recv": (_I, [_P, ctypes.POINTER(_I64)]),
     "moedx_handle_recv_tokens_per_expert": (_I, [_P, _P]),
     "moedx_handle_tensor": (_I, [_P, _I, _PP, ctypes.POINTER(_I64)]),

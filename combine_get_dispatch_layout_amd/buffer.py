@@ -187,6 +187,12 @@ class Buffer:
         C.check(C.moedx_create(ctypes.byref(ctx), self.device, num_experts, num_ranks,
                                num_channels, max_tokens, 0))
         self.ctx = ctx.value
+        # The comm stream (allocate_on_comm_stream) is one of PyTorch's own
+        # pool streams, which live as long as the process: tensors an op used
+        # there record it (_keep), and the caching allocator records an event
+        # on it when such a tensor is freed, possibly after this Buffer is gone.
+        self._ctx_stream = torch.cuda.Stream(device=self.device)
+        C.check(C.moedx_ctx_set_stream(self.ctx, self._ctx_stream.cuda_stream))
 
     _destroy = staticmethod(C.moedx_destroy)
     _release = staticmethod(_release)
@@ -197,6 +203,23 @@ class Buffer:
             self.ctx = None
 
     # -- plumbing ---------------------------------------------------------------
+    def ctx_stream(self) -> "torch.cuda.Stream":
+        """The ctx's own stream (where allocate_on_comm_stream runs an op)."""
+        return self._ctx_stream
+
+    def _keep(self, on_ctx_stream: bool, *tensors) -> None:
+        """An op on the ctx stream uses memory that PyTorch's caching allocator
+        handed out on the caller's stream: record the ctx stream on every such
+        tensor, so that no block is given to a new allocation before the ctx
+        stream's work on it has finished (even when the tensor is a temporary
+        dropped as the call returns)."""
+        if not on_ctx_stream:
+            return
+        s = self.ctx_stream()
+        for t in tensors:
+            if isinstance(t, torch.Tensor) and t.is_cuda and t.numel() > 0:
+                t.record_stream(s)
+
     def _exec(self, previous_event, async_finish, allocate_on_comm_stream, no_sync=False):
         if _deferred:
             _flush_deferred()
@@ -238,24 +261,47 @@ class Buffer:
         ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream)
         C.check(C.moedx_get_dispatch_layout(self.ctx, _ptr(topk_idx), T, K, _ptr(ntr), _ptr(nte),
                                             _ptr(itr), ctypes.byref(ex)))
+        self._keep(allocate_on_comm_stream, topk_idx, ntr, nte, itr)
         return ntr, None, nte, itr, self._event(done)
 
     # -- normal dispatch / combine --------------------------------------------------
     def prepare(self, topk_idx: torch.Tensor, num_worst_tokens: int = 0,
                 previous_event=None, async_finish=False, allocate_on_comm_stream=False,
-                no_sync=False):
+                no_sync=False, num_tokens_per_rank=None, is_token_in_rank=None,
+                num_tokens_per_expert=None):
         """Layout + scan into a new handle (exact mode, or capacity mode with
         ``num_worst_tokens`` receive rows; a capacity-mode handle's prefixes,
-        totals and N are written by its first dispatch or combine)."""
+        totals and N are written by its first dispatch or combine).  Given
+        get_dispatch_layout's ``is_token_in_rank`` and ``num_tokens_per_expert``
+        (and optionally ``num_tokens_per_rank``), no layout runs: the handle is
+        scanned from them."""
         topk_idx = topk_idx.contiguous()
         T, K = topk_idx.shape
+        from_layout = is_token_in_rank is not None or num_tokens_per_expert is not None
+        if from_layout:
+            assert is_token_in_rank is not None and num_tokens_per_expert is not None, \
+                "is_token_in_rank and num_tokens_per_expert go together"
+            assert tuple(is_token_in_rank.shape) == (T, self.num_ranks)
+            assert is_token_in_rank.dtype in (torch.bool, torch.uint8)
+            assert tuple(num_tokens_per_expert.shape) == (self.num_experts,)
+            assert num_tokens_per_expert.dtype == torch.int32
+            is_token_in_rank = is_token_in_rank.contiguous()
+            num_tokens_per_expert = num_tokens_per_expert.contiguous()
+            if num_tokens_per_rank is not None:
+                assert tuple(num_tokens_per_rank.shape) == (self.num_ranks,)
+                num_tokens_per_rank = num_tokens_per_rank.contiguous()
+        else:
+            num_tokens_per_rank = None
         nbytes = ctypes.c_size_t()
         C.check(C.moedx_handle_workspace_bytes(self.ctx, T, K, num_worst_tokens, ctypes.byref(nbytes)))
         ws = torch.empty(nbytes.value, dtype=torch.uint8, device=topk_idx.device)
         h = ctypes.c_void_p()
         ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream, no_sync)
-        C.check(C.moedx_dispatch_prepare(self.ctx, _ptr(topk_idx), T, K, _ptr(ws), nbytes.value,
-                                         num_worst_tokens, ctypes.byref(h), ctypes.byref(ex)))
+        C.check(C.moedx_dispatch_prepare(self.ctx, _ptr(topk_idx), T, K, _ptr(num_tokens_per_rank),
+                                         _ptr(is_token_in_rank), _ptr(num_tokens_per_expert),
+                                         _ptr(ws), nbytes.value, num_worst_tokens,
+                                         ctypes.byref(h), ctypes.byref(ex)))
+        self._keep(allocate_on_comm_stream, topk_idx, ws, is_token_in_rank, num_tokens_per_expert)
         return Handle(h.value, ws, T, K, False, num_worst_tokens, self), self._event(done)
 
     def dispatch(self, x, handle: Optional[Handle] = None, num_tokens_per_rank=None,
@@ -275,9 +321,10 @@ class Buffer:
         them as UE8M0 exponent bytes (and implies ``round_scale``);
         ``fp8_quant_scale`` is one scale for the whole tensor (exclusive with
         ``use_ue8m0``).  With ``handle`` (cached dispatch) topk_idx and
-        topk_weights must be None and only recv_x is produced.  The layout
-        arguments are accepted for call-shape compatibility; the handle is
-        computed from topk_idx on the device."""
+        topk_weights must be None and only recv_x is produced.  On a first
+        dispatch, get_dispatch_layout's outputs (``is_token_in_rank`` and
+        ``num_tokens_per_expert``, with ``num_tokens_per_rank`` if at hand) are
+        reused: the handle is scanned from them and no layout runs again."""
         prequant = isinstance(x, tuple)
         x_scales = None
         if prequant:
@@ -292,8 +339,12 @@ class Buffer:
         first = handle is None
         if first:
             assert topk_idx is not None, "a first dispatch needs topk_idx"
-            handle, _ = self.prepare(topk_idx, num_worst_tokens, previous_event,
-                                     False, allocate_on_comm_stream, no_sync=True)
+            reuse = is_token_in_rank is not None and num_tokens_per_expert is not None
+            handle, _ = self.prepare(
+                topk_idx, num_worst_tokens, previous_event, False, allocate_on_comm_stream,
+                no_sync=True, num_tokens_per_rank=num_tokens_per_rank if reuse else None,
+                is_token_in_rank=is_token_in_rank if reuse else None,
+                num_tokens_per_expert=num_tokens_per_expert if reuse else None)
             previous_event = None
         else:
             assert topk_idx is None and topk_weights is None, \
@@ -336,6 +387,9 @@ class Buffer:
                                      _ptr(ti), _ptr(tw if (first and not fp8) else None),
                                      _ptr(recv_x), _ptr(recv_s), _ptr(rti), _ptr(rtw),
                                      ctypes.byref(ex)))
+            self._keep(allocate_on_comm_stream, ti, tw)
+        self._keep(allocate_on_comm_stream, x, x_scales, recv_x, recv_s, rti, rtw, topk_idx,
+                   topk_weights if first else None)
         per_expert = handle.recv_tokens_per_expert(self.num_experts) if (
             first and handle.capacity == 0) else None
         if out is None:
@@ -366,6 +420,7 @@ class Buffer:
         tw = topk_weights.contiguous() if topk_weights is not None else None
         C.check(C.moedx_combine(self.ctx, handle.ptr, _ptr(x), H, _ptr(gw), _ptr(tw),
                                 _ptr(combined), _ptr(cw), ctypes.byref(ex)))
+        self._keep(allocate_on_comm_stream, x, gw, tw, combined, cw)
         return combined, cw, self._event(done)
 
     # -- low-latency ------------------------------------------------------------

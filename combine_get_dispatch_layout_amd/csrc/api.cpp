@@ -31,6 +31,7 @@ struct moedx_ctx {
     int E, R, P, C, max_tokens;
     BucketDiv bucket;        // e / P as a multiply and shift on the device
     hipStream_t stream;      // the ctx's own stream (default priority)
+    bool owns_stream;        // made by moedx_create (else the caller's, moedx_ctx_set_stream)
     hipEvent_t order_event;  // orders the ctx stream after the caller's
     void* scratch;           // layout ticket + partial counts of the standalone layout
     size_t scratch_bytes;
@@ -50,6 +51,8 @@ struct moedx_handle {
     int64_t n_host;    // exact mode only
     std::vector<int32_t> per_expert_host;
     mutable bool rows_written;  // send_head / recv_src_idx filled by a dispatch
+    bool experts_given;         // prepared from get_dispatch_layout's outputs: the expert
+                                // totals were copied, the tiles' expert partials never exist
     // Capacity mode: prepared with the layout's partials only; the first
     // dispatch or combine finishes the prefixes (or launches the finishing
     // step first).
@@ -237,8 +240,12 @@ static int check_waves(int T, int H) {
 }
 
 // The layout kernel's arguments for a handle: every handle array is written.
+// Only a launch whose workgroups take tickets (the layout kernel that finishes
+// in its last workgroup) gets the ctx's counter; the partials-only layout, the
+// finishing step alone and the first pack leave it untouched, so they may run
+// while a get_dispatch_layout or prepare of the same ctx is counting.
 static LayoutArgs handle_layout_args(const moedx_ctx* ctx, const moedx_handle* h,
-                                     const int64_t* topk_idx) {
+                                     const int64_t* topk_idx, bool takes_tickets) {
     LayoutArgs a{};
     a.topk_idx = topk_idx;
     a.T = h->T;
@@ -262,8 +269,10 @@ static LayoutArgs handle_layout_args(const moedx_ctx* ctx, const moedx_handle* h
     a.recv_channel_prefix_matrix = h->recv_channel_prefix_matrix;
     a.group_cnt = h->group_cnt;
     a.chan_part = h->chan_part;
-    a.tile_expert = h->tile_expert;
-    a.ticket = ctx->ticket;
+    a.tile_expert = h->experts_given ? nullptr : h->tile_expert;
+    a.itr_in = nullptr;
+    a.experts_in = nullptr;
+    a.ticket = takes_tickets ? ctx->ticket : nullptr;
     return a;
 }
 
@@ -271,9 +280,9 @@ static LayoutArgs handle_layout_args(const moedx_ctx* ctx, const moedx_handle* h
 // finishing step, launched here on the op's stream ahead of the op's kernel.
 static int finish_pending(moedx_ctx* ctx, const moedx_handle* h, hipStream_t run) {
     if (!h->prefixes_pending) return MOEDX_OK;
-    HIP_OR_FAIL(launch_layout_finish(handle_layout_args(ctx, h, nullptr),
+    HIP_OR_FAIL(launch_layout_finish(handle_layout_args(ctx, h, nullptr, false),
                                      Launch{run, nullptr, nullptr}));
-    ctx->stats.layout_launches += 1;
+    (h->experts_given ? ctx->stats.scan_launches : ctx->stats.layout_launches) += 1;
     h->prefixes_pending = false;
     return MOEDX_OK;
 }
@@ -318,6 +327,7 @@ int moedx_create(moedx_ctx** out, int device, int num_experts, int num_ranks, in
                        align256((size_t)nt * num_experts * 4);
     hipError_t e = hipSetDevice(device);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
+    if (e == hipSuccess) c->owns_stream = true;
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->order_event, hipEventDisableTiming);
     if (e == hipSuccess) e = hipMalloc(&c->scratch, c->scratch_bytes);
     if (e == hipSuccess) e = hipMemset(c->scratch, 0, c->scratch_bytes);  // the ticket starts at 0
@@ -346,7 +356,7 @@ int moedx_destroy(moedx_ctx* ctx) {
     if (ctx->scratch) (void)hipFree(ctx->scratch);
     if (ctx->pinned) (void)hipHostFree(ctx->pinned);
     if (ctx->order_event) (void)hipEventDestroy(ctx->order_event);
-    if (ctx->stream) (void)hipStreamDestroy(ctx->stream);
+    if (ctx->stream && ctx->owns_stream) (void)hipStreamDestroy(ctx->stream);
     delete ctx;
     return MOEDX_OK;
 }
@@ -355,6 +365,18 @@ int moedx_ctx_stats(const moedx_ctx* ctx, moedx_stats* out) {
     if (int rc = check_ctx(ctx)) return rc;
     if (!out) return fail(MOEDX_EINVAL, "out is NULL");
     *out = ctx->stats;
+    return MOEDX_OK;
+}
+
+int moedx_ctx_set_stream(moedx_ctx* ctx, hipStream_t stream) {
+    if (int rc = check_ctx(ctx)) return rc;
+    if (!stream) return fail(MOEDX_EINVAL, "stream is NULL (the null stream cannot be the ctx's own)");
+    if (stream == ctx->stream) return MOEDX_OK;
+    HIP_OR_FAIL(hipSetDevice(ctx->device));
+    HIP_OR_FAIL(hipStreamSynchronize(ctx->stream));  // nothing of the old stream is left behind
+    if (ctx->owns_stream) HIP_OR_FAIL(hipStreamDestroy(ctx->stream));
+    ctx->stream = stream;
+    ctx->owns_stream = false;
     return MOEDX_OK;
 }
 
@@ -450,6 +472,8 @@ int moedx_get_dispatch_layout(moedx_ctx* ctx, const int64_t* topk_idx, int T, in
     a.num_tokens_per_expert = num_tokens_per_expert;
     a.group_cnt = ctx->group_cnt;
     a.tile_expert = ctx->tile_expert;
+    a.itr_in = nullptr;
+    a.experts_in = nullptr;
     a.ticket = ctx->ticket;
     HIP_OR_FAIL(launch_layout(a, ex.launch()));
     ctx->stats.layout_launches += 1;
@@ -470,13 +494,26 @@ int moedx_handle_workspace_bytes(const moedx_ctx* ctx, int T, int K, int64_t cap
 }
 
 int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K,
-                           void* workspace, size_t workspace_bytes, int64_t capacity_rows,
-                           moedx_handle** out, const moedx_exec* exec) {
+                           const int32_t* num_tokens_per_rank, const uint8_t* is_token_in_rank,
+                           const int32_t* num_tokens_per_expert, void* workspace,
+                           size_t workspace_bytes, int64_t capacity_rows, moedx_handle** out,
+                           const moedx_exec* exec) {
     if (int rc = check_ctx(ctx)) return rc;
     if (!out) return fail(MOEDX_EINVAL, "out is NULL");
     *out = nullptr;
     if (int rc = check_tokens(ctx, T, K)) return rc;
     if ((T > 0 && !topk_idx) || !workspace) return fail(MOEDX_EINVAL, "NULL device pointer");
+    // From layout outputs: num_tokens_per_expert, with is_token_in_rank (which
+    // an empty batch need not name); num_tokens_per_rank only together with them.
+    const bool from_layout = num_tokens_per_expert != nullptr;
+    if (from_layout ? (T > 0 && !is_token_in_rank) : (is_token_in_rank || num_tokens_per_rank))
+        return fail(MOEDX_EINVAL,
+                    "is_token_in_rank and num_tokens_per_expert go together, and "
+                    "num_tokens_per_rank is given only with them");
+    if (from_layout && (!aligned4(num_tokens_per_expert) ||
+                        ((ctx->R & 3) == 0 && !aligned4(is_token_in_rank))))
+        return fail(MOEDX_EINVAL, "layout outputs are misaligned (int32: 4 bytes; "
+                                  "is_token_in_rank rows of a multiple of 4 buckets: 4 bytes)");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(MOEDX_EINVAL, "workspace is not 256-byte aligned");
     if (capacity_rows < 0) return fail(MOEDX_EINVAL, "capacity_rows < 0");
@@ -500,6 +537,7 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
     h->C = ctx->C;
     h->capacity = capacity_rows;
     h->n_host = -1;
+    h->experts_given = from_layout;
     carve_normal(h, static_cast<char*>(workspace), T, K, ctx->E, ctx->R, ctx->C, rows);
 
     Exec ex;
@@ -510,14 +548,18 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
         // in its own launch: the partials only, and the first dispatch (or
         // combine) on the handle finishes them.  Elsewhere the layout kernel
         // writes every prefix itself.
-        const LayoutArgs a = handle_layout_args(ctx, h, topk_idx);
         const bool partials =
             capacity_rows > 0 && T > 0 && pack_first_fits(T, h->R, h->E, h->C);
+        LayoutArgs a = handle_layout_args(ctx, h, topk_idx, !partials);
+        if (from_layout) {  // the scan of the given layout outputs
+            a.itr_in = is_token_in_rank;
+            a.experts_in = num_tokens_per_expert;
+        }
         e = partials ? launch_layout_partials(a, ex.launch()) : launch_layout(a, ex.launch());
         h->prefixes_pending = partials;
         if (e != hipSuccess) rc = hip_fail(e, "layout launch");
     }
-    if (rc == MOEDX_OK) ctx->stats.layout_launches += 1;
+    if (rc == MOEDX_OK) (from_layout ? ctx->stats.scan_launches : ctx->stats.layout_launches) += 1;
     if (rc == MOEDX_OK && capacity_rows == 0) {
         // Exact mode: the host waits for N and the per-expert counts.
         e = hipMemcpyAsync(ctx->pinned, h->num_recv, (size_t)(1 + h->E) * 4,
@@ -598,8 +640,8 @@ int moedx_handle_finish(moedx_ctx* ctx, const moedx_handle* h, const moedx_exec*
     Exec ex;
     if (int rc = exec_begin(ctx, exec, &ex)) return rc;
     if (h->prefixes_pending) {
-        HIP_OR_FAIL(launch_layout_finish(handle_layout_args(ctx, h, nullptr), ex.launch()));
-        ctx->stats.layout_launches += 1;
+        HIP_OR_FAIL(launch_layout_finish(handle_layout_args(ctx, h, nullptr, false), ex.launch()));
+        (h->experts_given ? ctx->stats.scan_launches : ctx->stats.layout_launches) += 1;
         h->prefixes_pending = false;
     } else {
         HIP_OR_FAIL(ex.no_kernel());
@@ -656,7 +698,7 @@ int moedx_dispatch(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, 
     if (T > 0 && quant == MOEDX_QUANT_NONE && h->prefixes_pending &&
         pack_first_fits(T, h->R, h->E, h->C)) {
         // One launch finishes the handle and packs the rows.
-        HIP_OR_FAIL(launch_pack_bf16_first(handle_layout_args(ctx, h, topk_idx), x, H,
+        HIP_OR_FAIL(launch_pack_bf16_first(handle_layout_args(ctx, h, topk_idx, false), x, H,
                                            h->capacity, hr, recv_x, topk_weights, recv_topk_idx,
                                            recv_topk_weights, ex.launch()));
         ctx->stats.pack_launches += 1;

@@ -122,10 +122,19 @@ struct LayoutArgs {
     int32_t* recv_channel_prefix_matrix;   // [R, C] exclusive (handle)
     int32_t* group_cnt;                    // scratch [ceil(T/64), R]
     int32_t* chan_part;                    // scratch [C + 1, R] (handle)
-    int32_t* tile_expert;                  // scratch [ceil(T/256), E]
-    unsigned int* ticket;                  // zero between launches
+    int32_t* tile_expert;                  // scratch [ceil(T/256), E]; null when the expert
+                                           // totals are given (experts_in)
+    // A handle prepared from get_dispatch_layout's outputs: the bucket masks
+    // come from is_token_in_rank [T, R] and the expert totals from
+    // num_tokens_per_expert [E] instead of from topk_idx (null otherwise).
+    const uint8_t* itr_in;
+    const int32_t* experts_in;
+    unsigned int* ticket;                  // zero between launches; null for a launch that
+                                           // takes no ticket (finishing step alone, first pack)
 };
 
+// With a.experts_in set (and a.itr_in, unless T == 0), the scan of a handle
+// from given layout outputs: no expert histogram, masks from is_token_in_rank.
 hipError_t launch_layout(const LayoutArgs& a, const Launch& L);
 
 // The partials and per-token outputs of the layout only (handle arrays

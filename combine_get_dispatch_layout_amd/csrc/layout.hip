@@ -6,6 +6,9 @@
 //     or finishing step on this launch's path).
 //   layout_finish_kernel: the finishing step alone, one workgroup, for a
 //     handle whose first use is not a dispatch that finishes it itself.
+// With kFromLayout the same launches scan a handle from get_dispatch_layout's
+// outputs (is_token_in_rank, num_tokens_per_expert) instead of computing them:
+// the dispatch of the normal-kernel example passes them in.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -18,11 +21,11 @@ namespace {
 
 using FullLds = LayoutShared<8192, 2048>;  // 32 KB of group prefixes, 8 KB of channel partials
 
-template <bool kPartialsOnly>
+template <bool kPartialsOnly, bool kFromLayout>
 __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
     __shared__ FullLds s;
     TileToken tk;
-    if (layout_tile(a, (int)blockIdx.x, (int)gridDim.x, s, &tk, kPartialsOnly)) {
+    if (layout_tile<kFromLayout>(a, (int)blockIdx.x, (int)gridDim.x, s, &tk, kPartialsOnly)) {
         if (!layout_finish(a, (int)gridDim.x, s, &tk)) {
             const int t = (int)blockIdx.x * kTile + (int)threadIdx.x;
             if (t < a.T) layout_token_outputs(a, t, tk);
@@ -51,13 +54,15 @@ BucketDiv bucket_div(int E, int P) {
 }
 
 hipError_t launch_layout(const LayoutArgs& a, const Launch& L) {
-    const int nt = num_tiles(a.T);
-    return launch_kernel(layout_kernel<false>, dim3(nt > 0 ? nt : 1), dim3(kTile), L, a);
+    const dim3 grid(num_tiles(a.T) > 0 ? num_tiles(a.T) : 1);
+    if (a.experts_in != nullptr) return launch_kernel(layout_kernel<false, true>, grid, dim3(kTile), L, a);
+    return launch_kernel(layout_kernel<false, false>, grid, dim3(kTile), L, a);
 }
 
 hipError_t launch_layout_partials(const LayoutArgs& a, const Launch& L) {
-    const int nt = num_tiles(a.T);
-    return launch_kernel(layout_kernel<true>, dim3(nt > 0 ? nt : 1), dim3(kTile), L, a);
+    const dim3 grid(num_tiles(a.T) > 0 ? num_tiles(a.T) : 1);
+    if (a.experts_in != nullptr) return launch_kernel(layout_kernel<true, true>, grid, dim3(kTile), L, a);
+    return launch_kernel(layout_kernel<true, false>, grid, dim3(kTile), L, a);
 }
 
 hipError_t launch_layout_finish(const LayoutArgs& a, const Launch& L) {

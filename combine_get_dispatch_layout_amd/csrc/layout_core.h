@@ -125,10 +125,10 @@ __device__ __forceinline__ void layout_token_outputs(const LayoutArgs& a, int t,
 }
 
 // The NS slots of one token (NS >= K, row = its topk_idx row): its bucket
-// mask, its slot buckets in *tk and its experts counted in the LDS histogram.
-// Slots past K re-read slot K - 1 and are ignored; ids outside [0, E) are
-// empty slots.
-template <int NS, typename Lds>
+// mask, its slot buckets in *tk and (kHist) its experts counted in the LDS
+// histogram.  Slots past K re-read slot K - 1 and are ignored; ids outside
+// [0, E) are empty slots.
+template <int NS, bool kHist, typename Lds>
 __device__ __forceinline__ uint64_t tile_slots(const LayoutArgs& a, const int64_t* row,
                                                Lds& s, TileToken* tk) {
     const int K = a.K, E = a.E;
@@ -143,9 +143,35 @@ __device__ __forceinline__ uint64_t tile_slots(const LayoutArgs& a, const int64_
         const int b = a.bucket.of(valid ? (int)e : 0);
         mask |= valid ? (1ull << b) : 0ull;
         tk->sb[k >> 2] ^= valid ? (uint32_t)(0xff ^ b) << (8 * (k & 3)) : 0u;
-        if (valid) atomicAdd(&s.hist[(int)e], 1);
+        if (kHist && valid) atomicAdd(&s.hist[(int)e], 1);
     }
     return mask;
+}
+
+// Bucket mask of a token from its is_token_in_rank row (bytes [row, row + R)
+// of the buffer itr; a nonzero byte is a member): 32-bit buffer loads when R is
+// a multiple of 4, else byte loads, all issued before the first is used.
+__device__ __forceinline__ uint64_t itr_row_mask(__amdgpu_buffer_rsrc_t itr, int row, int R) {
+    uint64_t m = 0;
+    if ((R & 3) == 0) {
+        uint32_t w[kMaxRanks / 4];
+#pragma unroll
+        for (int q = 0; q < kMaxRanks / 4; ++q)  // words past the row: past the buffer, 0
+            w[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                itr, 4 * q < R ? row + 4 * q : (int)(kNoWord * 4u), 0, 0);
+#pragma unroll
+        for (int q = 0; q < kMaxRanks / 4; ++q) {
+            const uint32_t v = w[q];
+            const uint64_t nib = (uint64_t)((v & 0xffu) != 0) | ((uint64_t)((v & 0xff00u) != 0) << 1) |
+                                 ((uint64_t)((v & 0xff0000u) != 0) << 2) |
+                                 ((uint64_t)((v & 0xff000000u) != 0) << 3);
+            m |= nib << (4 * q);
+        }
+    } else {
+        for (int r = 0; r < R; ++r)
+            m |= (uint64_t)(__builtin_amdgcn_raw_buffer_load_b8(itr, row + r, 0, 0) != 0) << r;
+    }
+    return m;
 }
 
 // Phase 1 for tile `tile` of `ntiles`.  Returns true in the workgroup that took
@@ -153,8 +179,11 @@ __device__ __forceinline__ uint64_t tile_slots(const LayoutArgs& a, const int64_
 // see that its own per-token outputs (*tk) are written; the other workgroups
 // have written theirs when this returns.  With partials_only every workgroup
 // stores its partials and per-token outputs and returns false: the finishing
-// step runs in a later launch.
-template <typename Lds>
+// step runs in a later launch.  kFromLayout: the bucket masks come from the
+// given is_token_in_rank (a.itr_in), topk_idx gives only the slot buckets, no
+// expert is counted, and tile 0 copies the given expert totals (a.experts_in)
+// into the handle.
+template <bool kFromLayout = false, typename Lds>
 __device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int ntiles, Lds& s,
                                             TileToken* tk, bool partials_only = false) {
     const int tid = threadIdx.x;
@@ -171,17 +200,37 @@ __device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int n
     tk->mask = 0;
 #pragma unroll
     for (int w = 0; w < kMaxTopk / 4; ++w) tk->sb[w] = 0xffffffffu;
+    constexpr int kEq = kMaxExperts / kTile;
+    int32_t ecopy[kEq];  // kFromLayout, tile 0: the given expert totals
+    if (kFromLayout && tile == 0) {
+#pragma unroll
+        for (int q = 0; q < kEq; ++q)
+            ecopy[q] = tid + q * kTile < E ? a.experts_in[tid + q * kTile] : 0;
+    }
     if (T > 0) {
-        for (int e = tid; e < E; e += kTile) s.hist[e] = 0;
-        __syncthreads();
+        if (!kFromLayout) {
+            for (int e = tid; e < E; e += kTile) s.hist[e] = 0;
+            __syncthreads();
+        }
         if (t < T) {
             // Every slot load is issued before the first is used (one memory
             // round trip); slots past K re-read slot K - 1 and are ignored.
             const int64_t* row = a.topk_idx + (int64_t)t * K;
-            if (K <= kMaxTopk / 2)
-                mask = tile_slots<kMaxTopk / 2>(a, row, s, tk);
-            else
-                mask = tile_slots<kMaxTopk>(a, row, s, tk);
+            if (kFromLayout) {
+                const __amdgpu_buffer_rsrc_t itr = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint8_t*>(a.itr_in), (short)0, T * R, 0x00020000);
+                const uint64_t given = itr_row_mask(itr, t * R, R);
+                if (K <= kMaxTopk / 2)
+                    (void)tile_slots<kMaxTopk / 2, false>(a, row, s, tk);
+                else
+                    (void)tile_slots<kMaxTopk, false>(a, row, s, tk);
+                mask = given;
+            } else {
+                if (K <= kMaxTopk / 2)
+                    mask = tile_slots<kMaxTopk / 2, true>(a, row, s, tk);
+                else
+                    mask = tile_slots<kMaxTopk, true>(a, row, s, tk);
+            }
             tk->mask = mask;
         }
         // Bucket counts over the wave's 64 tokens (a group), eight buckets at
@@ -223,8 +272,15 @@ __device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int n
                 }
             }
         }
-        __syncthreads();
-        for (int e = tid; e < E; e += kTile) a.tile_expert[(int64_t)tile * E + e] = s.hist[e];
+        if (!kFromLayout) {
+            __syncthreads();
+            for (int e = tid; e < E; e += kTile) a.tile_expert[(int64_t)tile * E + e] = s.hist[e];
+        }
+    }
+    if (kFromLayout && tile == 0) {
+#pragma unroll
+        for (int q = 0; q < kEq; ++q)
+            if (tid + q * kTile < E) a.num_tokens_per_expert[tid + q * kTile] = ecopy[q];
     }
     if (partials_only) {  // a later launch finishes (the kernel boundary publishes)
         if (t < T) layout_token_outputs(a, t, *tk);
@@ -281,16 +337,18 @@ __device__ __forceinline__ void layout_finish_fast(const LayoutArgs& a, int ntil
     const int nch = (ng + kGroup - 1) / kGroup;
     const int nb = a.channel_prefix_matrix != nullptr ? (a.C + 1) * R : 0;
     // Expert partials: thread i < E * per_e sums tiles i / E, i / E + per_e, ...
-    // of expert i % E (experts past 256 are summed after the fast part).
+    // of expert i % E (experts past 256 are summed after the fast part).  A
+    // handle scanned from given layout outputs has its totals already.
+    const bool experts = a.tile_expert != nullptr;
     const int per_e = layout_per_expert(E);
-    const bool e_thread = tid < E * per_e;
+    const bool e_thread = experts && tid < E * per_e;
     const int e0 = tid % E;
     for (int e = tid; e < E; e += kTile) s.hist[e] = 0;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     // Indices first, then every load.
     const __amdgpu_buffer_rsrc_t gc = word_buffer(a.group_cnt, ng * R);
-    const __amdgpu_buffer_rsrc_t te = word_buffer(a.tile_expert, ntiles * E);
+    const __amdgpu_buffer_rsrc_t te = word_buffer(a.tile_expert, experts ? ntiles * E : 0);
     const __amdgpu_buffer_rsrc_t cp = word_buffer(a.chan_part, nb);
     const unsigned int ebase = e_thread ? (unsigned int)((tid / E) * E + e0) : kNoWord;
     int32_t cnt[kFastBuckets][kChunks], ev[kTiles], cv[kFastBounds];
@@ -339,13 +397,16 @@ __device__ __forceinline__ void layout_finish_fast(const LayoutArgs& a, int ntil
     for (int u = 0; u < kTiles; ++u) esum += ev[u];
     __syncthreads();  // hist cleared by every thread
     if (e_thread) atomicAdd(&s.hist[e0], esum);
-    for (int e = tid + kTile; e < E; e += kTile) {  // E > 256
-        int32_t v = 0;
-        for (int j = 0; j < ntiles; ++j) v += a.tile_expert[(int64_t)j * E + e];
-        s.hist[e] = v;
+    if (experts) {
+        for (int e = tid + kTile; e < E; e += kTile) {  // E > 256
+            int32_t v = 0;
+            for (int j = 0; j < ntiles; ++j) v += a.tile_expert[(int64_t)j * E + e];
+            s.hist[e] = v;
+        }
     }
     __syncthreads();
-    for (int e = tid; e < E; e += kTile) a.num_tokens_per_expert[e] = s.hist[e];
+    if (experts)
+        for (int e = tid; e < E; e += kTile) a.num_tokens_per_expert[e] = s.hist[e];
     // Bucket offsets: one wave prefix sum over the bucket totals.
     if (wave == 0) {
         const int32_t tot = lane < R ? s.total[lane] : 0;
@@ -369,7 +430,7 @@ __device__ __forceinline__ void layout_finish_fast(const LayoutArgs& a, int ntil
             if (c > 0) a.channel_prefix_matrix[r * a.C + c - 1] = val;
         }
     }
-    if (tid == 0) atomicExch(a.ticket, 0u);
+    if (tid == 0 && a.ticket) atomicExch(a.ticket, 0u);  // only a launch that took tickets
 }
 
 // Phase 2, in the workgroup that took the last ticket of `ntiles` tiles.
@@ -401,8 +462,9 @@ __device__ __forceinline__ bool layout_finish(const LayoutArgs& a, int ntiles, L
     // waits behind a branch.  Every index is computed before the first load.
     // Expert totals: thread i < E * per_e sums the partials of expert i % E
     // from tiles i / E + u * per_e.
+    const bool experts = a.tile_expert != nullptr;  // else the totals are given
     const int per_e = E >= kTile ? 1 : kTile / E;
-    const bool e_thread = tid < E * per_e;
+    const bool e_thread = experts && tid < E * per_e;
     const int e0 = e_thread ? tid % E : 0, part0 = tid / E;
     const unsigned int ebase = e_thread ? (unsigned int)(part0 * E + e0) : kNoWord;
     // Channel-boundary partial counts (written in phase 1), staged in LDS.
@@ -422,7 +484,7 @@ __device__ __forceinline__ bool layout_finish(const LayoutArgs& a, int ntiles, L
     const int sr = tid / L, sj = tid % L;
     const unsigned int gbase = scan_thread ? (unsigned int)(sj * G * R + sr) : kNoWord;
 
-    const __amdgpu_buffer_rsrc_t te = word_buffer(a.tile_expert, nt * E);
+    const __amdgpu_buffer_rsrc_t te = word_buffer(a.tile_expert, experts ? nt * E : 0);
     int32_t ev[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)  // tiles past nt lie past the buffer's end
@@ -457,7 +519,7 @@ __device__ __forceinline__ bool layout_finish(const LayoutArgs& a, int ntiles, L
 #pragma unroll
     for (int q = 1; q < kMaxExperts / kTile; ++q) {  // E > 256 only
         const int i = tid + q * kTile;
-        if (i >= E * per_e) continue;
+        if (!experts || i >= E * per_e) continue;
         const int e = i % E, part = i / E;
         for (int j = part; j < nt; j += per_e * kBatch) {
             int32_t v[kBatch];
@@ -512,7 +574,7 @@ __device__ __forceinline__ bool layout_finish(const LayoutArgs& a, int ntiles, L
 #pragma unroll
     for (int q = 0; q < kMaxExperts / kTile; ++q) {
         const int i = tid + q * kTile;
-        if (i < E * per_e) {
+        if (experts && i < E * per_e) {
             if (per_e == 1) s.hist[i] = esum[q];
             else atomicAdd(&s.hist[i % E], esum[q]);
         }
@@ -530,7 +592,8 @@ __device__ __forceinline__ bool layout_finish(const LayoutArgs& a, int ntiles, L
         if (a.rank_prefix_matrix) a.rank_prefix_matrix[tid] = s.base[tid] + s.total[tid];
         if (a.num_recv && tid == R - 1) *a.num_recv = s.base[tid] + s.total[tid];
     }
-    for (int e = tid; e < E; e += kTile) a.num_tokens_per_expert[e] = s.hist[e];
+    if (experts)
+        for (int e = tid; e < E; e += kTile) a.num_tokens_per_expert[e] = s.hist[e];
     // Channel prefixes, one (boundary, bucket) pair per thread:
     // excl(b, r) = group_prefix[b / 64][r] + (count from the group start to b).
     for (int i = tid; i < nb; i += kTile) {
@@ -547,7 +610,7 @@ __device__ __forceinline__ bool layout_finish(const LayoutArgs& a, int ntiles, L
         if (c < a.C) a.recv_channel_prefix_matrix[r * a.C + c] = val;
         if (c > 0) a.channel_prefix_matrix[r * a.C + c - 1] = val;
     }
-    if (tid == 0) atomicExch(a.ticket, 0u);
+    if (tid == 0 && a.ticket) atomicExch(a.ticket, 0u);  // only a launch that took tickets
     return false;
 }
 

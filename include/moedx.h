@@ -29,9 +29,9 @@
  *     (OCP E4M3FN).
  *   - Execution: see moedx_exec.  Kernels run on the caller's stream unless
  *     MOEDX_ON_CTX_STREAM is set.
- *   - A ctx is not thread-safe; use one ctx per stream.  Calls are stream
- *     ordered; overlapping calls on one ctx from different streams race on the
- *     ctx's scratch memory.
+ *   - A ctx is not thread-safe (one host thread at a time).  Calls are stream
+ *     ordered; of the calls that may overlap on one ctx from different
+ *     streams, moedx_create says which share the ctx's scratch.
  */
 #ifndef MOEDX_H
 #define MOEDX_H
@@ -113,6 +113,9 @@ typedef struct moedx_stats {
     int64_t ll_dispatch_launches;
     int64_t ll_combine_launches;
     int64_t host_syncs;
+    /* scans of a handle from get_dispatch_layout's outputs (moedx_dispatch_prepare
+     * given them): no layout kernel runs for such a handle */
+    int64_t scan_launches;
 } moedx_stats;
 
 /* Which device array of a handle moedx_handle_tensor returns
@@ -145,16 +148,26 @@ MOEDX_API const char *moedx_last_error(void);
  * channel unit of channel_prefix_matrix); max_tokens bounds T for every call
  * and sizes the ctx's scratch.  Allocates the ctx stream (default priority),
  * a small device scratch and a pinned host buffer; flags must be 0.
- * The layout launches of one ctx (moedx_get_dispatch_layout,
- * moedx_dispatch_prepare) share the scratch's completion counter: they must
- * not run concurrently (issue them on one stream, or order them with events);
- * other calls may overlap freely when their buffers do. */
+ * moedx_get_dispatch_layout and moedx_dispatch_prepare of one ctx share the
+ * scratch's completion counter (and get_dispatch_layout its partial counts):
+ * they must not run concurrently with each other (issue them on one stream,
+ * or order them with events).  Every other call (dispatch, combine,
+ * handle_finish, the low-latency calls) leaves that scratch alone and may
+ * overlap with anything whose buffers it does not share. */
 MOEDX_API int moedx_create(moedx_ctx **out, int device, int num_experts, int num_ranks,
                            int num_channels, int max_tokens, uint32_t flags);
 MOEDX_API int moedx_destroy(moedx_ctx *ctx);
 MOEDX_API int moedx_ctx_stats(const moedx_ctx *ctx, moedx_stats *out);
 /* The ctx's own stream (for MOEDX_ON_CTX_STREAM users). */
 MOEDX_API int moedx_ctx_stream(const moedx_ctx *ctx, hipStream_t *out);
+/* Use the caller's `stream` (not the null stream; default priority) as the
+ * ctx's own stream from now on: the comm stream of [EO] may then be one the
+ * caller's runtime owns and keeps alive (a memory pool that records its
+ * streams on blocks, for instance, needs them valid when a block is freed,
+ * which may be after moedx_destroy).  Waits for the previous ctx stream to
+ * drain and destroys it if moedx_create made it; the caller keeps `stream`
+ * alive for the ctx's lifetime, and moedx_destroy does not destroy it. */
+MOEDX_API int moedx_ctx_set_stream(moedx_ctx *ctx, hipStream_t stream);
 
 /* ---- events ([EO] CUDA Event Capture in Buffer; Explicit Stream Waiting) -- */
 
@@ -200,6 +213,19 @@ MOEDX_API int moedx_handle_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  * caller until moedx_handle_destroy).  The handle holds the arrays listed for
  * moedx_handle_tensor plus the bucket of every slot.
  *
+ * Reuse of get_dispatch_layout's outputs (the normal-kernel example of [GCU]
+ * passes num_tokens_per_rank, is_token_in_rank and num_tokens_per_expert from
+ * get_dispatch_layout into dispatch): when num_tokens_per_expert (device int32
+ * [E]) and is_token_in_rank (device uint8 [T, R], nonzero = member; may be
+ * NULL only when T == 0) are given, no layout runs: one scan kernel takes the
+ * bucket membership from is_token_in_rank, the slot buckets from topk_idx,
+ * and copies the expert totals (moedx_stats.scan_launches counts it instead
+ * of layout_launches).  They must be the layout of this topk_idx (the scan
+ * trusts them).  num_tokens_per_rank (device int32 [R]) may be passed with
+ * them, as the pages' call does; the bucket totals are recomputed by the scan,
+ * so it is not read.  Alignment: num_tokens_per_expert 4 bytes,
+ * is_token_in_rank 4 bytes when R % 4 == 0.  All three NULL: the layout runs.
+ *
  * Receive rows are bucket-major and, inside a bucket, in ascending token order
  * (channel order, then token order inside a channel); N = total rows.
  *   capacity_rows == 0 (exact mode): the host waits for N and the per-expert
@@ -217,9 +243,11 @@ MOEDX_API int moedx_handle_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  *     even when exec->done is given.
  * *out receives a new handle (moedx_handle_destroy frees it). */
 MOEDX_API int moedx_dispatch_prepare(moedx_ctx *ctx, const int64_t *topk_idx, int T, int K,
-                                     void *workspace, size_t workspace_bytes,
-                                     int64_t capacity_rows, moedx_handle **out,
-                                     const moedx_exec *exec);
+                                     const int32_t *num_tokens_per_rank,
+                                     const uint8_t *is_token_in_rank,
+                                     const int32_t *num_tokens_per_expert, void *workspace,
+                                     size_t workspace_bytes, int64_t capacity_rows,
+                                     moedx_handle **out, const moedx_exec *exec);
 
 /* N on the host; exact-mode handles only (MOEDX_ESTATE otherwise). */
 MOEDX_API int moedx_handle_num_recv(const moedx_handle *h, int64_t *n);
@@ -332,8 +360,7 @@ MOEDX_API int moedx_ll_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  *   recv_count[e] = |L_e| (int32 [E]), recv_x[e][s] = x[L_e[s]]
  *   (bf16 [E, cap, H]; slots past the count untouched), and in the handle
  *   src_idx[e][s] = L_e[s] and slot_of[t][k] = position of t in L_{topk_idx[t,k]}
- *   (-1 for an empty slot).  Runs as a single kernel launch; there is no
- *   deferred receive hook (no network receive exists on one GPU).
+ *   (-1 for an empty slot).  Runs as a single kernel launch.
  * recv_x == NULL defers the receive (return_recv_hook=True of the low-latency
  *   example: the rows arrive only when the hook runs): counts and the handle
  *   are written, rows are not, and x is not read; moedx_ll_dispatch_recv then

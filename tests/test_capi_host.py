@@ -62,7 +62,7 @@ def test_null_arguments_are_rejected(capi):
     assert capi.moedx_handle_num_recv(None, None) == capi.MOEDX_EINVAL
     assert capi.moedx_handle_tensor(None, 0, None, None) == capi.MOEDX_EINVAL
     assert capi.moedx_ctx_stats(None, None) == capi.MOEDX_EINVAL
-    assert capi.moedx_dispatch_prepare(None, None, 0, 1, None, 0, 0, None, None) == capi.MOEDX_EINVAL
+    assert capi.moedx_dispatch_prepare(None, None, 0, 1, None, None, None, None, 0, 0, None, None) == capi.MOEDX_EINVAL
     assert capi.moedx_combine(None, None, None, 8, None, None, None, None, None) == capi.MOEDX_EINVAL
     assert capi.moedx_handle_finish(None, None, None) == capi.MOEDX_EINVAL
     assert capi.moedx_dispatch_fp8(None, None, None, 0, 128, None, None, None, None) == capi.MOEDX_EINVAL

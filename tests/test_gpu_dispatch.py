@@ -259,3 +259,81 @@ def test_capacity_handle_finished_before_first_use(oracle, w):
     assert buf.stats()["layout_launches"] == before["layout_launches"] + 1
     check_handle(h, ref, N)
     assert_equal("recv_x", np_(recv)[:N], ref.recv_x)
+
+
+@pytest.mark.parametrize("w", NORMAL, ids=lambda w: w.name)
+@pytest.mark.parametrize("mode", ["exact", "capacity"])
+def test_layout_then_dispatch_and_combine(oracle, w, mode):
+    """The normal-kernel example's call order at full size: get_dispatch_layout,
+    then dispatch given its num_tokens_per_rank / is_token_in_rank /
+    num_tokens_per_expert, then the gate-weighted combine.  The layout runs
+    once: the dispatch scans its handle from the given outputs."""
+    dev = device()
+    print(f"[layout->dispatch] {w.name} {mode}", flush=True)
+    inp = wl.make_inputs(w)
+    E, R, C, T, H, K = w.experts, w.ranks, _channels(w), w.tokens, w.hidden, w.topk
+    ref = oracle_first_dispatch(oracle, inp, E, R, C)
+    N = ref.prefix.num_recv
+    buf = make_buffer(E, R, C, T)
+    x, idx, gw = inp.x.to(dev), inp.topk_idx.to(dev), inp.topk_weights.to(dev)
+    ntr, _, nte, itr, _ = buf.get_dispatch_layout(idx, E)
+    cap = T * min(K, R) if mode == "capacity" else 0
+    recv_x, rti, rtw, per_expert, h, _ = buf.dispatch(
+        x, topk_idx=idx, topk_weights=gw, num_tokens_per_rank=ntr, is_token_in_rank=itr,
+        num_tokens_per_expert=nte, num_worst_tokens=cap)
+    comb, _, _ = buf.combine(recv_x, h, gate_weights=gw)
+    torch.cuda.synchronize()
+    st = buf.stats()
+    assert st["layout_launches"] == 1 and st["scan_launches"] == 1, st
+    assert st["pack_launches"] == 1 and st["combine_launches"] == 1, st
+    check_handle(h, ref, N)
+    assert_equal("recv_x", np_(recv_x)[:N], ref.recv_x)
+    assert_equal("recv_topk_idx", np_(rti)[:N], ref.recv_topk_idx)
+    assert_equal("recv_topk_weights", np_(rtw)[:N].view(np.uint32),
+                 ref.recv_topk_weights.view(np.uint32))
+    if not cap:
+        assert per_expert == ref.layout.num_tokens_per_expert.tolist()
+    # softmax gates over identity rows give x back bit for bit (a closed form
+    # of the weighted combine; the oracle's combine is pinned to it)
+    want, _ = oracle.combine(ref.recv_x, inp.topk_idx.numpy(), E, ref.prefix,
+                             gate_weights=inp.topk_weights.numpy())
+    assert_bf16_within_1ulp("combine", np_(comb), want)
+
+
+def test_layout_concurrent_with_first_dispatch(oracle):
+    """One ctx, two streams: get_dispatch_layout runs on one while a first
+    capacity-mode dispatch (whose pack finishes its handle) and a combine of
+    another handle run on the other; then a third layout.  Only the layout
+    launches count tickets, so none of them is disturbed."""
+    dev = device()
+    w = wl.PREFILL
+    inp = wl.make_inputs(w, tokens=4096)
+    inp2 = wl.make_inputs(w, seed=31, tokens=4096)
+    E, R, C, T, K = w.experts, w.ranks, w.channels, 4096, w.topk
+    ref = oracle_first_dispatch(oracle, inp, E, R, C)
+    ref2 = oracle.layout(inp2.topk_idx.numpy(), E, R)
+    buf = make_buffer(E, R, C, T)
+    x, idx, gw = inp.x.to(dev), inp.topk_idx.to(dev), inp.topk_weights.to(dev)
+    idx2 = inp2.topk_idx.to(dev)
+    cap = T * min(K, R)
+    h, _ = buf.prepare(idx, cap)  # partials only: the first pack finishes it
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for rep in range(3):
+        print(f"[concurrent] rep {rep}", flush=True)
+        with torch.cuda.stream(s1):
+            ntr, _, nte, itr, _ = buf.get_dispatch_layout(idx2, E, async_finish=True)
+        with torch.cuda.stream(s2):
+            if rep == 0:
+                recv, _, _, _, _, _ = buf.dispatch(x, handle=h, no_sync=True)
+                comb, _, _ = buf.combine(recv, h, gate_weights=gw, no_sync=True)
+        torch.cuda.synchronize()
+        outs.append((np_(ntr), np_(nte), np_(itr)))
+        if rep == 0:
+            check_handle(h, ref, ref.prefix.num_recv)
+            assert_equal("recv_x", np_(recv)[:ref.prefix.num_recv], ref.recv_x)
+    for ntr_, nte_, itr_ in outs:
+        assert_equal("num_tokens_per_rank", ntr_, ref2.num_tokens_per_rank)
+        assert_equal("num_tokens_per_expert", nte_, ref2.num_tokens_per_expert)
+        assert_equal("is_token_in_rank", itr_, ref2.is_token_in_rank)

@@ -16,10 +16,14 @@ pytestmark = pytest.mark.gpu
 
 
 def run_case(o, idx: np.ndarray, H: int, E: int, R: int, C: int, seed: int = 0,
-             x_u16: np.ndarray = None, capacity: bool = False, fp8: bool = False):
+             x_u16: np.ndarray = None, capacity: bool = False, fp8: bool = False,
+             from_layout: bool = False):
+    """get_dispatch_layout, then a first dispatch (that reuses the layout's
+    outputs when from_layout), then the combine, all against the oracle."""
     dev = device()
     T, K = idx.shape
-    print(f"[edge] T={T} K={K} H={H} E={E} R={R} C={C} cap={capacity} fp8={fp8}", flush=True)
+    print(f"[edge] T={T} K={K} H={H} E={E} R={R} C={C} cap={capacity} fp8={fp8} "
+          f"from_layout={from_layout}", flush=True)
     g = torch.Generator().manual_seed(seed)
     x = torch.randn(T, H, generator=g).to(torch.bfloat16)
     if x_u16 is not None:
@@ -34,16 +38,26 @@ def run_case(o, idx: np.ndarray, H: int, E: int, R: int, C: int, seed: int = 0,
     assert_equal("num_tokens_per_expert", np_(nte), ref.layout.num_tokens_per_expert)
     assert_equal("is_token_in_rank", np_(itr).reshape(T, R), ref.layout.is_token_in_rank)
     cap = T * min(K, R) if capacity else 0
+    reuse = dict(num_tokens_per_rank=ntr, is_token_in_rank=itr,
+                 num_tokens_per_expert=nte) if from_layout else {}
+    layouts = buf.stats()["layout_launches"]
+
+    def no_second_layout():
+        if from_layout:  # the handle was scanned from the layout's outputs
+            st = buf.stats()
+            assert st["layout_launches"] == layouts and st["scan_launches"] >= 1, st
+
     if fp8:
         (codes, scales), _, _, _, h, _ = buf.dispatch(x.to(dev), topk_idx=ti, fp8=True,
-                                                      num_worst_tokens=cap)
+                                                      num_worst_tokens=cap, **reuse)
         cref, sref = o.pack_fp8(bf16_bits(x), ref.prefix)
         assert_equal("codes", np_(codes)[:N], cref)
         assert_equal("scales", np_(scales)[:N].view(np.uint32), sref.view(np.uint32))
         check_handle(h, ref, N)
+        no_second_layout()
         return
     recv, rti, rtw, _, h, _ = buf.dispatch(x.to(dev), topk_idx=ti, topk_weights=w.to(dev),
-                                           num_worst_tokens=cap)
+                                           num_worst_tokens=cap, **reuse)
     torch.cuda.synchronize()
     check_handle(h, ref, N)
     assert_equal("recv_x", np_(recv)[:N], ref.recv_x)
@@ -54,6 +68,7 @@ def run_case(o, idx: np.ndarray, H: int, E: int, R: int, C: int, seed: int = 0,
                               recv_topk_weights=ref.recv_topk_weights)
     assert_bf16_within_1ulp("combine", np_(comb).reshape(T, H), want)
     assert_equal("combined_topk_weights", np_(cw).reshape(T, K).view(np.uint32), want_cw.view(np.uint32))
+    no_second_layout()
 
 
 def _rand(T, E, K, p_empty=0.0, seed=0):
@@ -231,3 +246,29 @@ def test_layout_finishing_step_limits(oracle, T, E, K, R, C):
 ], ids=lambda v: str(v))
 def test_first_capacity_dispatch_one_launch(oracle, T, E, K, R, C):
     run_case(oracle, _rand(T, E, K, p_empty=0.05, seed=3 * T + R), 16, E, R, C, capacity=True)
+
+
+# A first dispatch given get_dispatch_layout's outputs (the normal-kernel
+# example's call order): the handle is scanned from is_token_in_rank and the
+# expert totals instead of running the layout again.  Shapes over every path:
+# empty batch, one token, ragged tiles, R = 1, 3, 6 (byte loads of the mask
+# rows) and 64, empty slots and buckets, exact and capacity mode (one-launch
+# first dispatch, prefixes at prepare), FP8, and both finishing steps.
+@pytest.mark.parametrize("T,E,K,R,C,p_empty,capacity,fp8", [
+    (0, 16, 4, 4, 3, 0.0, False, False),
+    (1, 16, 4, 4, 8, 0.0, True, False),
+    (257, 64, 6, 16, 7, 0.0, False, False),
+    (3001, 64, 6, 16, 7, 0.1, True, False),
+    (300, 12, 3, 3, 5, 0.4, False, False),
+    (300, 8, 8, 1, 3, 0.0, True, False),
+    (777, 36, 5, 6, 4, 0.05, True, False),
+    (700, 1024, 16, 64, 33, 0.0, False, False),
+    (4096, 64, 8, 8, 8, 0.05, True, False),
+    (4097, 64, 8, 8, 8, 0.05, True, False),
+    (16385, 64, 6, 16, 8, 0.02, False, False),
+    (500, 64, 6, 16, 5, 0.0, True, True),
+    (1000, 256, 8, 8, 24, 0.0, False, True),
+], ids=lambda v: str(v))
+def test_dispatch_from_layout_outputs(oracle, T, E, K, R, C, p_empty, capacity, fp8):
+    run_case(oracle, _rand(T, E, K, p_empty=p_empty, seed=T + 5 * R), 128 if fp8 else 16, E, R,
+             C, capacity=capacity, fp8=fp8, from_layout=True)
