@@ -113,13 +113,32 @@ def measured_traffic(op):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name, family / model /
+    stepping, and the number of logical CPUs it lists."""
+    fields, cpus = {}, 0
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            key = line.split(":", 1)[0].strip()
+            if key == "processor":
+                cpus += 1
+            elif key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                fields[key] = line.split(":", 1)[1].strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    return (f"{fields.get('model name', 'unknown')} (family {fields.get('cpu family', '?')}, "
+            f"model {fields.get('model', '?')}, stepping {fields.get('stepping', '?')}; "
+            f"{cpus} logical CPUs listed)")
+
+
+def cpu_threads():
+    """Host threads for the oracle's all-cores leg: the CPUs this process may
+    run on, capped by OMP_NUM_THREADS where it is set (a GPU machine gives one GPU
+    a share of its cores and says so there)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(n, 1)
 
 
 def kernel_us_distribution(C, stream, launch, n, flush):
@@ -149,8 +168,50 @@ def kernel_us_distribution(C, stream, launch, n, flush):
             "mean": round(statistics.mean(d), 2)}
 
 
-def cpu_baseline(inp, w, budget_s):
-    """The CPU oracle (single thread, as it stands) on the same inputs."""
+def oracle_step(o, x, idx, gw, E, R, C, threads=1, pool=None):
+    """One step of the CPU oracle: layout, prefixes, bf16 pack with recv_topk_*,
+    gate-weighted combine.  With threads > 1 the per-token parts (layout, pack,
+    combine) run over `threads` contiguous token ranges at once (the oracle's
+    C functions release the GIL); each range calls the oracle unchanged on its
+    rows, the range counts of the layout are added up, and the prefixes, a
+    sequential scan, run once.  Returns (N, receive rows, combined rows)."""
+    import dataclasses
+
+    import numpy as np
+
+    T, K = idx.shape
+    H = x.shape[1]
+    if threads <= 1:
+        lay = o.layout(idx, E, R)
+        pre = o.prefix(lay.is_token_in_rank, C)
+        rx, _, _ = o.pack_bf16(x, idx, gw, E, pre)
+        out, _ = o.combine(rx, idx, E, pre, gate_weights=gw)
+        return pre.num_recv, rx, out
+    bounds = [(T * i // threads, T * (i + 1) // threads) for i in range(threads)]
+    itr = np.empty((T, R), np.uint8)
+    lays = list(pool.map(lambda b: o.layout(idx[b[0]:b[1]], E, R, out_itr=itr[b[0]:b[1]]),
+                         bounds))
+    ntr = sum(lay.num_tokens_per_rank for lay in lays)
+    pre = o.prefix(itr, C)
+    assert int(ntr.sum()) == pre.num_recv
+    N = pre.num_recv
+    rx = np.zeros((N, H), np.uint16)
+    rti = np.empty((N, K), np.int64)
+    rtw = np.empty((N, K), np.float32)
+    rows = lambda b: dataclasses.replace(pre, send_head=pre.send_head[b[0]:b[1]])  # noqa: E731
+    list(pool.map(lambda b: o.pack_bf16(x[b[0]:b[1]], idx[b[0]:b[1]], gw[b[0]:b[1]], E, rows(b),
+                                        out=(rx, rti, rtw)), bounds))
+    out = np.empty((T, H), np.uint16)
+    list(pool.map(lambda b: o.combine(rx, idx[b[0]:b[1]], E, rows(b), gate_weights=gw[b[0]:b[1]],
+                                      out=out[b[0]:b[1]]), bounds))
+    return N, rx, out
+
+
+def cpu_baseline(inp, w, budget_s, threads=1):
+    """The CPU oracle (as it stands) on the same inputs, on `threads` host
+    threads: median step time, steps run, N."""
+    import concurrent.futures as cf
+
     import numpy as np
     import oracle as om
 
@@ -160,17 +221,14 @@ def cpu_baseline(inp, w, budget_s):
     gw = inp.topk_weights.numpy()
     times = []
     N = 0
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        lay = o.layout(idx, w.experts, w.ranks)
-        pre = o.prefix(lay.is_token_in_rank, w.channels)
-        rx, _, _ = o.pack_bf16(x, idx, gw, w.experts, pre)
-        o.combine(rx, idx, w.experts, pre, gate_weights=gw)
-        times.append(time.perf_counter() - t0)
-        N = pre.num_recv
-        if time.perf_counter() - t_start >= budget_s or len(times) >= 20:
-            break
+    with cf.ThreadPoolExecutor(max_workers=threads) as pool:
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            N = oracle_step(o, x, idx, gw, w.experts, w.ranks, w.channels, threads, pool)[0]
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start >= budget_s or len(times) >= 20:
+                break
     return statistics.median(times), len(times), N
 
 
@@ -426,6 +484,49 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
                                        row_bytes("combine", T, H, K, E, N=N, R=w.ranks),
                                        {"recv_rows": N, "dtype": "bf16",
                                         "per_launch_us": per_launch(fns)})
+
+    # -- the first FP8 dispatch on a fresh handle (layout with every prefix at
+    # prepare, then the FP8 pack, which also writes send_head / recv_src_idx),
+    # and get_dispatch_layout alone, on the same workload
+    log_fn(f"[bench] rows first_dispatch_fp8 / get_layout_fp8_skewed: {w.name}")
+    R4 = w.ranks
+    nb4 = ctypes.c_size_t()
+    C.check(C.moedx_handle_workspace_bytes(buf.ctx, T, K, cap4, ctypes.byref(nb4)))
+    for s in sets:
+        s["ws_first"] = torch.empty(nb4.value, dtype=torch.uint8, device=dev)
+
+    def first_fp8(s):
+        def f():
+            h = ctypes.c_void_p()
+            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, None, None, None,
+                                             P(s["ws_first"]), nb4.value, cap4, ctypes.byref(h),
+                                             exr))
+            C.check(C.moedx_dispatch(buf.ctx, h, P(s["x"]), T, H, C.MOEDX_QUANT_FP8_E4M3_1X128,
+                                     None, None, P(s["recv"]), P(s["scales"]), None, None, exr))
+            C.moedx_handle_destroy(h)
+        return f
+
+    ms_f8 = timed([first_fp8(s) for s in sets])
+    lay4 = 8 * T * K + T * R4 + 4 * (2 * R4 + E + 2 * R4 * w.channels)
+    rows["first_dispatch_fp8"] = entry(
+        w, "first_dispatch_fp8", ms_f8, lay4 + row_bytes("pack_fp8", T, H, K, E, N=N) + 4 * T * R4 + 4 * N,
+        {"recv_rows": N, "dtype": "bf16->e4m3",
+         "note": "prepare (the layout with every prefix: 128 groups of 64 tokens) + the FP8 pack "
+                 "with the handle's send_head / recv_src_idx, on a fresh capacity-mode handle"})
+    for s in sets:
+        s["ntr"] = torch.empty(R4, dtype=torch.int32, device=dev)
+        s["nte"] = torch.empty(E, dtype=torch.int32, device=dev)
+        s["itr"] = torch.empty(T, R4, dtype=torch.uint8, device=dev)
+
+    def get_layout4(s):
+        return lambda: C.check(C.moedx_get_dispatch_layout(
+            buf.ctx, P(idx), T, K, P(s["ntr"]), P(s["nte"]), P(s["itr"]), cur[0]))
+
+    fns = [get_layout4(s) for s in sets]
+    ms = timed(fns)
+    rows["get_layout_fp8_skewed"] = entry(
+        w, "get_layout_fp8_skewed", ms, row_bytes("get_layout", T, H, K, E, R=R4),
+        {"bound_note": "latency (under 1 MB)", "per_launch_us": per_launch(fns)})
     for s in sets:
         C.moedx_handle_destroy(s["h"])
     del sets, buf, u8, pq
@@ -549,6 +650,58 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
                                {"bound_note": "latency (under 0.3 MB)", "per_launch_us": dist}, cpu)
     del lsets, buf
 
+    # -- the whole step on the tiny workload (launch-bound; its 0.4 MB stay in
+    # the caches whatever the rotation)
+    w = wl.TINY
+    log_fn(f"[bench] row tiny_step: {w.name}")
+    inp = wl.make_inputs(w)
+    T, H, K, E, R, Ch = w.tokens, w.hidden, w.topk, w.experts, w.ranks, w.channels
+    buf = Buffer(E, R, num_channels=Ch, max_tokens=T)
+    cap1 = T * min(K, R)
+    nb1 = ctypes.c_size_t()
+    C.check(C.moedx_handle_workspace_bytes(buf.ctx, T, K, cap1, ctypes.byref(nb1)))
+    idx1, gw1 = inp.topk_idx.to(dev), inp.topk_weights.to(dev)
+    tsets = [{"x": inp.x.to(dev), "ws": torch.empty(nb1.value, dtype=torch.uint8, device=dev),
+              "recv": torch.empty(cap1, H, dtype=torch.bfloat16, device=dev),
+              "rti": torch.empty(cap1, K, dtype=torch.int64, device=dev),
+              "rtw": torch.empty(cap1, K, dtype=torch.float32, device=dev),
+              "out": torch.empty(T, H, dtype=torch.bfloat16, device=dev)} for _ in range(NSETS)]
+
+    def tiny_step(s):
+        def f():
+            h = ctypes.c_void_p()
+            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx1), T, K, None, None, None, P(s["ws"]),
+                                             nb1.value, cap1, ctypes.byref(h), exr))
+            C.check(C.moedx_dispatch(buf.ctx, h, P(s["x"]), T, H, C.MOEDX_QUANT_NONE, P(idx1),
+                                     P(gw1), P(s["recv"]), None, P(s["rti"]), P(s["rtw"]), exr))
+            C.check(C.moedx_combine(buf.ctx, h, P(s["recv"]), H, P(gw1), None, P(s["out"]), None,
+                                    exr))
+            C.moedx_handle_destroy(h)
+        return f
+
+    ms = timed([tiny_step(s) for s in tsets])
+    ref_n = secs = reps = None
+    if o is not None:
+        xs1 = u16(inp.x)
+        ids1, gws1 = inp.topk_idx.numpy(), inp.topk_weights.numpy()
+        secs, reps = _median_time(lambda: oracle_step(o, xs1, ids1, gws1, E, R, Ch), cpu_budget_s / 16,
+                                  max_reps=20)
+        ref_n = oracle_step(o, xs1, ids1, gws1, E, R, Ch)[0]
+    h0 = ctypes.c_void_p()
+    C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx1), T, K, None, None, None, P(tsets[0]["ws"]),
+                                     nb1.value, cap1, ctypes.byref(h0), exr))
+    N1 = handle_rows(buf, h0, tsets[0]["ws"])
+    C.moedx_handle_destroy(h0)
+    assert ref_n is None or ref_n == N1
+    b1 = sum(algorithmic_bytes(T, H, K, E, R, Ch, N1).values())
+    rows["tiny_step"] = entry(
+        w, "tiny_step", ms, b1,
+        {"recv_rows": N1, "dtype": "bf16",
+         "note": "layout partials + first pack (finishing the handle) + gate-weighted combine, "
+                 "capacity mode; launch-bound, inputs cache-resident"},
+        cpu_entry(b1, secs, reps, f"oracle step on the full {T}-token workload") if o else None)
+    del tsets, buf
+
     # -- low-latency dispatch and combine on the 128-token decode workload -------
     w = wl.LL_DECODE
     log_fn(f"[bench] rows ll_dispatch / ll_combine: {w.name}")
@@ -601,7 +754,10 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
         secs, reps = _median_time(lambda: o.ll_combine(recv_o, idn, wn, slot_o), cpu_budget_s / 8)
         cpu_c = cpu_entry(row_bytes("ll_combine", T, H, K, E, V=V), secs, reps,
                           f"oracle ll_combine on the full {T}-token workload")
-    note = {"bound_note": "latency: a few MB per launch", "slots_filled": V}
+    note = {"bound_note": "latency: a few MB per launch", "slots_filled": V,
+            "cache_note": f"inputs ({inp.x.numel() * 2 / 1e6:.1f} MB of x, the handle) rotate over "
+                          f"{NSETS} sets: they stay in the Infinity Cache, as a decode step's "
+                          "activations would"}
     rows["ll_dispatch"] = entry(w, "ll_dispatch", ms_d, row_bytes("ll_dispatch", T, H, K, E, V=V),
                                 dict(note, per_launch_us=dist_d), cpu_d)
     rows["ll_combine"] = entry(w, "ll_combine", ms_c, row_bytes("ll_combine", T, H, K, E, V=V),
@@ -802,6 +958,30 @@ def main():
         C.moedx_event_destroy(b)
         return ms.value
 
+    # The normal-kernel example's call order: get_dispatch_layout into its own
+    # outputs, then the first dispatch given them (a scan of the handle from
+    # is_token_in_rank and the expert totals, then the first pack).
+    lay_out = [{"ntr": torch.empty(R, dtype=torch.int32, device=dev),
+                "nte": torch.empty(E, dtype=torch.int32, device=dev),
+                "itr": torch.empty(T, R, dtype=torch.uint8, device=dev)} for _ in range(NSETS)]
+
+    def layout_call(lo, e=exr):
+        C.check(C.moedx_get_dispatch_layout(ctx, p_idx, T, K, P(lo["ntr"]), P(lo["nte"]),
+                                            P(lo["itr"]), e))
+
+    def prepare_from(s_, lo, e=exr):
+        h = ctypes.c_void_p()
+        C.check(C.moedx_dispatch_prepare(ctx, p_idx, T, K, P(lo["ntr"]), P(lo["itr"]),
+                                         P(lo["nte"]), P(s_["ws"]), nbytes.value, cap,
+                                         ctypes.byref(h), e))
+        return h
+
+    def layout_then_dispatch(j, e_scan=None):
+        layout_call(lay_out[j])
+        h = prepare_from(sets[j], lay_out[j], e_scan if e_scan is not None else exr)
+        pack(h, sets[j])
+        C.moedx_handle_destroy(h)
+
     # Each set's handle, finished by its first pack; the combine runs on these.
     handles = [prepare(s_) for s_ in sets]
     for h, s_ in zip(handles, sets):
@@ -824,6 +1004,8 @@ def main():
                 C.moedx_handle_destroy(prepare(sets[j]))
             elif op == "dispatch":
                 dispatch(sets[j])
+            elif op == "layout_then_dispatch":
+                layout_then_dispatch(j)
             else:
                 combine(handles[j], sets[j])
         b = record()
@@ -840,6 +1022,8 @@ def main():
                 C.moedx_handle_destroy(prepare(sets[j], e))
             elif op == "pack":
                 dispatch(sets[j], exr, e)
+            elif op == "scan":
+                layout_then_dispatch(j, e)
             else:
                 combine(handles[j], sets[j], e)
         return kernel_us_distribution(C, stream, launch, n, flush)
@@ -859,7 +1043,7 @@ def main():
         return elapsed_ms(a, b) / n
 
     log(f"[bench] warmup {args.warmup}")
-    for op in ("layout", "dispatch", "combine"):
+    for op in ("layout", "dispatch", "combine", "layout_then_dispatch"):
         op_avg_ms(op, max(args.warmup, 1))
     pipelined_ms(max(args.warmup, 1))
     torch.cuda.synchronize()
@@ -883,6 +1067,9 @@ def main():
     wall = time.perf_counter() - wall0
     dist = {op: op_kernel_us(op, args.steps) for op in ("layout", "pack", "combine")}
     t_pack = dist["pack"]["mean"] * 1e-3  # ms: the first pack alone, kernel-stamped
+    log("[bench] the pages' call order: get_dispatch_layout, dispatch given its outputs, combine")
+    t_ltd = op_avg_ms("layout_then_dispatch", args.steps)
+    scan_dist = op_kernel_us("scan", args.steps)
 
     # Exact mode through the API on the host clock: the host waits for N after
     # the layout (no capacity bound), then the pack and the combine run.
@@ -937,13 +1124,21 @@ def main():
 
     cpu = None
     if args.cpu_budget_s > 0:
-        log(f"[bench] CPU oracle baseline (~{args.cpu_budget_s:.0f} s)")
-        t_cpu, reps, n_cpu = cpu_baseline(inp, w, args.cpu_budget_s)
-        assert n_cpu == N
-        cpu = {"value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle", "tokens_per_s": round(T / t_cpu, 1), "cpu_model": cpu_model(),
-               "sample": f"median of {reps} full {T}x{H} steps (layout+prefix+pack+weighted "
-                         f"combine), single-threaded C oracle"}
+        threads = cpu_threads()
+        log(f"[bench] CPU oracle baseline on {threads} threads and on 1 "
+            f"(~{args.cpu_budget_s:.0f} s)")
+        t_all, reps_all, n_all = cpu_baseline(inp, w, args.cpu_budget_s / 3, threads)
+        t_one, reps_one, n_one = cpu_baseline(inp, w, 2 * args.cpu_budget_s / 3, 1)
+        assert n_all == N and n_one == N
+        cpu = {"value": round(step_bytes / t_all / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle", "tokens_per_s": round(T / t_all, 1), "cpu_model": cpu_model(),
+               "affinity_cpus": len(os.sched_getaffinity(0)),
+               "sample": f"median of {reps_all} full {T}x{H} steps (layout+prefix+pack+weighted "
+                         f"combine) of the C oracle, its per-token parts over {threads} token "
+                         f"ranges on {threads} threads (the prefix scan on one)",
+               "single_thread": {"value": round(step_bytes / t_one / 1e9, 4), "unit": "GB/s",
+                                 "cores": 1, "tokens_per_s": round(T / t_one, 1),
+                                 "sample": f"median of {reps_one} full steps, one thread"}}
 
     rows = None
     if not args.no_rows:
@@ -981,6 +1176,18 @@ def main():
         "kernels_us_per_launch": dist,
         "kernel_GBps": {"pack": round(bytes_["pack"] / (t_pack * 1e-3) / 1e9, 1),
                         "combine": round(bytes_["combine"] / (t_comb_k * 1e-3) / 1e9, 1)},
+        "layout_then_dispatch": {
+            "dispatch_us": round(t_ltd * 1e3, 2), "combine_us": round(t_comb * 1e3, 2),
+            "step_us": round((t_ltd + t_comb) * 1e3, 2),
+            "GBps": round(step_bytes / ((t_ltd + t_comb) * 1e-3) / 1e9, 1),
+            "roofline_frac": round(step_bytes / ((t_ltd + t_comb) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(T / ((t_ltd + t_comb) * 1e-3), 1),
+            "scan_kernel_us_per_launch": scan_dist,
+            "note": "the normal-kernel example's order: get_dispatch_layout, then the first "
+                    "dispatch given num_tokens_per_rank / is_token_in_rank / "
+                    "num_tokens_per_expert (a scan of the handle from them, no second layout, "
+                    "then the first pack), then the same combine; same buffer rotation and "
+                    "byte count as the step"},
         "pipelined_ms_per_step": round(ms_pipe, 5),
         "exact_mode_api_wall_us": {
             "median": round(statistics.median(wall_exact), 1),

@@ -21,11 +21,15 @@ namespace {
 
 using FullLds = LayoutShared<8192, 2048>;  // 32 KB of group prefixes, 8 KB of channel partials
 
-template <bool kPartialsOnly, bool kFromLayout>
+// kMaxR: 0 computes the layout from topk_idx; 8, 16 or 64 scans a handle from
+// given layout outputs with up to that many buckets.
+template <bool kPartialsOnly, int kMaxR>
 __global__ __launch_bounds__(kTile) void layout_kernel(LayoutArgs a) {
     __shared__ FullLds s;
     TileToken tk;
-    if (layout_tile<kFromLayout>(a, (int)blockIdx.x, (int)gridDim.x, s, &tk, kPartialsOnly)) {
+    if (layout_tile<(kMaxR > 0), (kMaxR > 0 ? kMaxR : kMaxRanks)>(a, (int)blockIdx.x,
+                                                                   (int)gridDim.x, s, &tk,
+                                                                   kPartialsOnly)) {
         if (!layout_finish(a, (int)gridDim.x, s, &tk)) {
             const int t = (int)blockIdx.x * kTile + (int)threadIdx.x;
             if (t < a.T) layout_token_outputs(a, t, tk);
@@ -53,16 +57,25 @@ BucketDiv bucket_div(int E, int P) {
     return BucketDiv{0u, 0u};  // not reached for E <= 1024
 }
 
+namespace {
+
+template <bool kPartialsOnly>
+hipError_t launch_layout_kind(const LayoutArgs& a, const Launch& L) {
+    const dim3 grid(num_tiles(a.T) > 0 ? num_tiles(a.T) : 1), block(kTile);
+    if (a.experts_in == nullptr) return launch_kernel(layout_kernel<kPartialsOnly, 0>, grid, block, L, a);
+    if (a.R <= 8) return launch_kernel(layout_kernel<kPartialsOnly, 8>, grid, block, L, a);
+    if (a.R <= 16) return launch_kernel(layout_kernel<kPartialsOnly, 16>, grid, block, L, a);
+    return launch_kernel(layout_kernel<kPartialsOnly, kMaxRanks>, grid, block, L, a);
+}
+
+}  // namespace
+
 hipError_t launch_layout(const LayoutArgs& a, const Launch& L) {
-    const dim3 grid(num_tiles(a.T) > 0 ? num_tiles(a.T) : 1);
-    if (a.experts_in != nullptr) return launch_kernel(layout_kernel<false, true>, grid, dim3(kTile), L, a);
-    return launch_kernel(layout_kernel<false, false>, grid, dim3(kTile), L, a);
+    return launch_layout_kind<false>(a, L);
 }
 
 hipError_t launch_layout_partials(const LayoutArgs& a, const Launch& L) {
-    const dim3 grid(num_tiles(a.T) > 0 ? num_tiles(a.T) : 1);
-    if (a.experts_in != nullptr) return launch_kernel(layout_kernel<true, true>, grid, dim3(kTile), L, a);
-    return launch_kernel(layout_kernel<true, false>, grid, dim3(kTile), L, a);
+    return launch_layout_kind<true>(a, L);
 }
 
 hipError_t launch_layout_finish(const LayoutArgs& a, const Launch& L) {

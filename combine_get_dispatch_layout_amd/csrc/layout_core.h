@@ -148,28 +148,48 @@ __device__ __forceinline__ uint64_t tile_slots(const LayoutArgs& a, const int64_
     return mask;
 }
 
-// Bucket mask of a token from its is_token_in_rank row (bytes [row, row + R)
-// of the buffer itr; a nonzero byte is a member): 32-bit buffer loads when R is
-// a multiple of 4, else byte loads, all issued before the first is used.
-__device__ __forceinline__ uint64_t itr_row_mask(__amdgpu_buffer_rsrc_t itr, int row, int R) {
+// A token's is_token_in_rank row (bytes [row, row + R) of the buffer itr; a
+// nonzero byte is a member), for R <= MR: the loads only, so that the slot
+// loads can go out before anything waits for these.  32-bit words when R is a
+// multiple of 4, else single bytes; loads past the row read past the buffer's
+// end (0).
+template <int MR>
+struct ItrRow {
+    uint32_t w[MR];  // words: w[0..MR/4); bytes: w[0..MR)
+};
+
+template <int MR>
+__device__ __forceinline__ ItrRow<MR> itr_row_load(__amdgpu_buffer_rsrc_t itr, int row, int R) {
+    ItrRow<MR> x;
+    constexpr int kPast = (int)(kNoWord * 4u);
+    if ((R & 3) == 0) {
+#pragma unroll
+        for (int q = 0; q < MR / 4; ++q)
+            x.w[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(itr, 4 * q < R ? row + 4 * q : kPast,
+                                                                    0, 0);
+    } else {
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+            x.w[r] = __builtin_amdgcn_raw_buffer_load_b8(itr, r < R ? row + r : kPast, 0, 0);
+    }
+    return x;
+}
+
+template <int MR>
+__device__ __forceinline__ uint64_t itr_row_mask(const ItrRow<MR>& x, int R) {
     uint64_t m = 0;
     if ((R & 3) == 0) {
-        uint32_t w[kMaxRanks / 4];
 #pragma unroll
-        for (int q = 0; q < kMaxRanks / 4; ++q)  // words past the row: past the buffer, 0
-            w[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-                itr, 4 * q < R ? row + 4 * q : (int)(kNoWord * 4u), 0, 0);
-#pragma unroll
-        for (int q = 0; q < kMaxRanks / 4; ++q) {
-            const uint32_t v = w[q];
+        for (int q = 0; q < MR / 4; ++q) {
+            const uint32_t v = x.w[q];
             const uint64_t nib = (uint64_t)((v & 0xffu) != 0) | ((uint64_t)((v & 0xff00u) != 0) << 1) |
                                  ((uint64_t)((v & 0xff0000u) != 0) << 2) |
                                  ((uint64_t)((v & 0xff000000u) != 0) << 3);
             m |= nib << (4 * q);
         }
     } else {
-        for (int r = 0; r < R; ++r)
-            m |= (uint64_t)(__builtin_amdgcn_raw_buffer_load_b8(itr, row + r, 0, 0) != 0) << r;
+#pragma unroll
+        for (int r = 0; r < MR; ++r) m |= (uint64_t)(x.w[r] != 0) << r;
     }
     return m;
 }
@@ -182,8 +202,9 @@ __device__ __forceinline__ uint64_t itr_row_mask(__amdgpu_buffer_rsrc_t itr, int
 // step runs in a later launch.  kFromLayout: the bucket masks come from the
 // given is_token_in_rank (a.itr_in), topk_idx gives only the slot buckets, no
 // expert is counted, and tile 0 copies the given expert totals (a.experts_in)
-// into the handle.
-template <bool kFromLayout = false, typename Lds>
+// into the handle.  kMaxR (kFromLayout): a bound on R that sizes the mask
+// row's loads.
+template <bool kFromLayout = false, int kMaxR = kMaxRanks, typename Lds>
 __device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int ntiles, Lds& s,
                                             TileToken* tk, bool partials_only = false) {
     const int tid = threadIdx.x;
@@ -217,14 +238,16 @@ __device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int n
             // round trip); slots past K re-read slot K - 1 and are ignored.
             const int64_t* row = a.topk_idx + (int64_t)t * K;
             if (kFromLayout) {
+                // the mask row's loads, then the slots' (issued before either
+                // is waited for), then the mask
                 const __amdgpu_buffer_rsrc_t itr = __builtin_amdgcn_make_buffer_rsrc(
                     const_cast<uint8_t*>(a.itr_in), (short)0, T * R, 0x00020000);
-                const uint64_t given = itr_row_mask(itr, t * R, R);
+                const ItrRow<kMaxR> given = itr_row_load<kMaxR>(itr, t * R, R);
                 if (K <= kMaxTopk / 2)
                     (void)tile_slots<kMaxTopk / 2, false>(a, row, s, tk);
                 else
                     (void)tile_slots<kMaxTopk, false>(a, row, s, tk);
-                mask = given;
+                mask = itr_row_mask<kMaxR>(given, R);
             } else {
                 if (K <= kMaxTopk / 2)
                     mask = tile_slots<kMaxTopk / 2, true>(a, row, s, tk);

@@ -136,12 +136,16 @@ class Oracle:
         return np.array([f(int(v)) for v in c], dtype=np.float32).reshape(np.shape(codes))
 
     # -- layout and handle ----------------------------------------------
-    def layout(self, topk_idx: np.ndarray, num_experts: int, num_ranks: int) -> Layout:
+    def layout(self, topk_idx: np.ndarray, num_experts: int, num_ranks: int,
+               out_itr: Optional[np.ndarray] = None) -> Layout:
+        """out_itr: a C-contiguous uint8 [T, R] array (a row range of a larger
+        one, say) that receives is_token_in_rank."""
         idx = _c(topk_idx, np.int64)
         T, K = idx.shape
         ntr = np.empty(num_ranks, np.int32)
         nte = np.empty(num_experts, np.int32)
-        itr = np.empty((T, num_ranks), np.uint8)
+        itr = np.empty((T, num_ranks), np.uint8) if out_itr is None else out_itr
+        assert itr.shape == (T, num_ranks) and itr.dtype == np.uint8 and itr.flags["C_CONTIGUOUS"]
         rc = self.lib.oracle_layout(_ptr(idx), T, K, num_experts, num_ranks,
                                     _ptr(ntr), _ptr(nte), _ptr(itr))
         if rc != 0:
@@ -164,16 +168,24 @@ class Oracle:
 
     # -- pack -------------------------------------------------------------
     def pack_bf16(self, x_u16: np.ndarray, topk_idx, topk_weights, num_experts: int,
-                  pre: Prefix, with_topk: bool = True):
+                  pre: Prefix, with_topk: bool = True, out: Optional[tuple] = None):
+        """out: preallocated (recv_x [N, H], recv_topk_idx [N, K] or None,
+        recv_topk_weights [N, K] or None), written in place (a token range of
+        x with the same rows of pre.send_head writes that range's rows)."""
         x = _c(x_u16, np.uint16)
         T, H = x.shape
         idx = _c(topk_idx, np.int64)
         K = idx.shape[1]
         R = pre.send_head.shape[1]
+        assert pre.send_head.shape[0] == T
         N = pre.num_recv
-        recv_x = np.zeros((N, H), np.uint16)
-        rti = np.empty((N, K), np.int64) if with_topk else None
-        rtw = np.empty((N, K), np.float32) if (with_topk and topk_weights is not None) else None
+        if out is not None:
+            recv_x, rti, rtw = out
+            assert recv_x.shape == (N, H) and recv_x.dtype == np.uint16
+        else:
+            recv_x = np.zeros((N, H), np.uint16)
+            rti = np.empty((N, K), np.int64) if with_topk else None
+            rtw = np.empty((N, K), np.float32) if (with_topk and topk_weights is not None) else None
         w = _c(topk_weights, np.float32) if topk_weights is not None else None
         self.lib.oracle_pack_bf16(_ptr(x), T, H, _ptr(idx), _ptr(w), K, num_experts, R,
                                   _ptr(pre.send_head), _ptr(pre.rank_prefix_matrix),
@@ -247,15 +259,21 @@ class Oracle:
 
     # -- combine ------------------------------------------------------------
     def combine(self, y_u16: np.ndarray, topk_idx, num_experts: int, pre: Prefix,
-                gate_weights=None, recv_topk_weights=None):
+                gate_weights=None, recv_topk_weights=None, out: Optional[np.ndarray] = None):
+        """out: a preallocated C-contiguous uint16 [T, H] array (a token range of
+        a larger one, with the same rows of topk_idx, pre.send_head and
+        gate_weights) that receives the combined rows."""
         y = _c(y_u16, np.uint16)
         H = y.shape[1]
         idx = _c(topk_idx, np.int64)
         T, K = idx.shape
         R = pre.send_head.shape[1]
+        assert pre.send_head.shape[0] == T
         gw = _c(gate_weights, np.float32) if gate_weights is not None else None
         rtw = _c(recv_topk_weights, np.float32) if recv_topk_weights is not None else None
-        out = np.empty((T, H), np.uint16)
+        if out is None:
+            out = np.empty((T, H), np.uint16)
+        assert out.shape == (T, H) and out.dtype == np.uint16 and out.flags["C_CONTIGUOUS"]
         cw = np.empty((T, K), np.float32) if rtw is not None else None
         self.lib.oracle_combine(_ptr(y), T, H, _ptr(idx), K, num_experts, R,
                                 _ptr(pre.send_head), _ptr(pre.rank_prefix_matrix),

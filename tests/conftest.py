@@ -14,5 +14,8 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def oracle():
+    """The CPU oracle; MOEDX_ORACLE_LIB names another build of it (the
+    sanitizer run of test_oracle_sanitized.py)."""
     from oracle import Oracle
-    return Oracle()
+    path = os.environ.get("MOEDX_ORACLE_LIB")
+    return Oracle(path) if path else Oracle()

@@ -39,3 +39,28 @@ def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch)
     monkeypatch.setitem(bench.TRAFFIC_SOURCES, "pack", "combine.hip")
     assert bench.measured_traffic("pack") is None
     assert bench.measured_traffic("no_such_op") is None
+
+
+def test_all_cores_oracle_leg_equals_the_single_thread_step():
+    """The CPU baseline's all-cores leg only splits the driver over token
+    ranges: its receive rows and combined rows equal the one-thread oracle's."""
+    import concurrent.futures as cf
+
+    import numpy as np
+    import torch
+
+    import oracle as om
+    from combine_get_dispatch_layout_amd import workloads as wl
+
+    w = wl.PREFILL
+    inp = wl.make_inputs(w, tokens=301)
+    o = om.Oracle()
+    x = inp.x.view(torch.int16).numpy().view(np.uint16)[:, :256].copy()
+    idx, gw = inp.topk_idx.numpy(), inp.topk_weights.numpy()
+    n1, rx1, out1 = bench.oracle_step(o, x, idx, gw, w.experts, w.ranks, w.channels)
+    with cf.ThreadPoolExecutor(max_workers=4) as pool:
+        n4, rx4, out4 = bench.oracle_step(o, x, idx, gw, w.experts, w.ranks, w.channels, 7, pool)
+    assert n1 == n4
+    assert np.array_equal(rx1, rx4)
+    assert np.array_equal(out1, out4)
+    assert bench.cpu_threads() >= 1

@@ -88,3 +88,8 @@ def test_releases_wait_for_the_end_of_a_capture():
     bm._release(done.append, 3, _capturing=lambda: False,
                 _flush=lambda: bm._flush_deferred(_capturing=lambda: False))
     assert done == [3, 2, 1] and not bm._deferred
+
+
+
+def test_ctx_set_stream_rejects_null(capi):
+    assert capi.moedx_ctx_set_stream(None, ctypes.c_void_p(256)) == capi.MOEDX_EINVAL
