@@ -93,6 +93,7 @@ SIGNATURES = {
     "moedx_event_elapsed_ms": (_I, [_P, _P, ctypes.POINTER(ctypes.c_float)]),
     "moedx_event_destroy": (_I, [_P]),
     "moedx_get_dispatch_layout": (_I, [_P, _P, _I, _I, _P, _P, _P, _EX]),
+    "moedx_get_dispatch_layout_static": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moedx_handle_workspace_bytes": (_I, [_P, _I, _I, _I64, ctypes.POINTER(_SZ)]),
     "moedx_dispatch_prepare": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _SZ, _I64, _PP, _EX]),
     "moedx_handle_num_recv": (_I, [_P, ctypes.POINTER(_I64)]),

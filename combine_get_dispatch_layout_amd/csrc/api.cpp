@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -287,6 +288,32 @@ static int finish_pending(moedx_ctx* ctx, const moedx_handle* h, hipStream_t run
     return MOEDX_OK;
 }
 
+// ---- the allocation-free layout ---------------------------------------------
+//
+// moedx_get_dispatch_layout_static keeps what moedx_get_dispatch_layout keeps
+// in a ctx's scratch (the ticket counter, the group and tile partial counts)
+// in this file-scope device array instead: every GPU the library runs on holds
+// its own copy, from the code object's load until the process ends.  Host code
+// never passes `scratch` itself to a kernel (on the host it names a stand-in,
+// not device memory): the first call on a device takes the device address with
+// hipGetSymbolAddress and keeps it per device.
+constexpr size_t kStaticScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+unsigned char* g_static_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// Carve of the static scratch: the ticket, then group and tile partials.
+size_t static_layout_bytes(int T, int E, int R) {
+    return 256 + align256((size_t)std::max(num_groups(T), 1) * R * 4) +
+           align256((size_t)std::max(num_tiles(T), 1) * E * 4);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* moedx_last_error(void) { return g_err; }
@@ -478,6 +505,71 @@ int moedx_get_dispatch_layout(moedx_ctx* ctx, const int64_t* topk_idx, int T, in
     HIP_OR_FAIL(launch_layout(a, ex.launch()));
     ctx->stats.layout_launches += 1;
     return exec_end(ex);
+}
+
+int moedx_get_dispatch_layout_static(const int64_t* topk_idx, int T, int K, int E, int R,
+                                     int32_t* num_tokens_per_rank,
+                                     int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                                     hipStream_t stream) {
+    if (R < 1 || R > kMaxRanks) return fail(MOEDX_EINVAL, "R=%d outside [1, %d]", R, kMaxRanks);
+    if (E < 1 || E > kMaxExperts)
+        return fail(MOEDX_EINVAL, "E=%d outside [1, %d]", E, kMaxExperts);
+    if (E % R != 0) return fail(MOEDX_EINVAL, "E=%d is not a multiple of R=%d", E, R);
+    if (K < 1 || K > kMaxTopk) return fail(MOEDX_EINVAL, "K=%d outside [1, %d]", K, kMaxTopk);
+    if (T < 0 || T > (1 << 24)) return fail(MOEDX_EINVAL, "T=%d outside [0, 2^24]", T);
+    if ((T > 0 && (!topk_idx || !is_token_in_rank)) || !num_tokens_per_rank ||
+        !num_tokens_per_expert)
+        return fail(MOEDX_EINVAL, "NULL device pointer");
+    const size_t need = static_layout_bytes(T, E, R);
+    if (need > kStaticScratchBytes)
+        return fail(MOEDX_ECAPACITY,
+                    "T=%d, E=%d, R=%d need %zu bytes of the static scratch, which holds %zu "
+                    "(use moedx_get_dispatch_layout with a ctx)",
+                    T, E, R, need, kStaticScratchBytes);
+    const BucketDiv bucket = bucket_div(E, E / R);
+    if (bucket.mul == 0) return fail(MOEDX_EINVAL, "no exact multiply-shift for E / R");
+    int dev = 0;
+    HIP_OR_FAIL(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOEDX_EINVAL, "device %d >= %d", dev, kMaxDevices);
+    const Launch L{stream, nullptr, nullptr};
+    unsigned char* base = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        if (!g_static_ptr[dev]) {  // once per device, with that device current
+            void* p = nullptr;
+            HIP_OR_FAIL(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+            if (!p) return fail(MOEDX_EHIP, "hipGetSymbolAddress gave no address");
+            // The ticket must start at zero (every layout launch leaves it
+            // there): cleared on this stream ahead of the first layout.  The
+            // address is kept only once the clear is enqueued.
+            HIP_OR_FAIL(launch_zero_words(static_cast<uint32_t*>(p), 1, L));
+            g_static_ptr[dev] = static_cast<unsigned char*>(p);
+        }
+        base = g_static_ptr[dev];
+    }
+    unsigned int* ticket = reinterpret_cast<unsigned int*>(base);
+    LayoutArgs a{};
+    a.topk_idx = topk_idx;
+    a.T = T;
+    a.K = K;
+    a.E = E;
+    a.R = R;
+    a.P = E / R;
+    a.bucket = bucket;
+    a.C = 1;
+    a.per = T > 0 ? T : 1;
+    a.per_div = make_fastdiv((uint32_t)a.per);
+    a.is_token_in_rank = is_token_in_rank;
+    a.num_tokens_per_rank = num_tokens_per_rank;
+    a.num_tokens_per_expert = num_tokens_per_expert;
+    a.group_cnt = reinterpret_cast<int32_t*>(base + 256);
+    a.tile_expert = reinterpret_cast<int32_t*>(
+        base + 256 + align256((size_t)std::max(num_groups(T), 1) * R * 4));
+    a.itr_in = nullptr;
+    a.experts_in = nullptr;
+    a.ticket = ticket;
+    HIP_OR_FAIL(launch_layout(a, L));
+    return MOEDX_OK;
 }
 
 // ---- handle -----------------------------------------------------------------

@@ -146,6 +146,9 @@ hipError_t launch_layout_partials(const LayoutArgs& a, const Launch& L);
 // launch_layout_partials wrote.
 hipError_t launch_layout_finish(const LayoutArgs& a, const Launch& L);
 
+// Zero n 32-bit words with a kernel (capturable, unlike a memset node).
+hipError_t launch_zero_words(uint32_t* p, int n, const Launch& L);
+
 // ---- receive rows ------------------------------------------------------------
 
 // row(t, r) = base[r] + group_prefix[t / 64][r] + (tokens of t's 64-token group

@@ -42,6 +42,11 @@ __global__ __launch_bounds__(kTile) void layout_finish_kernel(LayoutArgs a, int 
     layout_finish(a, ntiles, s, (const TileToken*)nullptr);
 }
 
+__global__ __launch_bounds__(kTile) void zero_words_kernel(uint32_t* __restrict__ p, int n) {
+    const int i = blockIdx.x * kTile + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 }  // namespace
 
 BucketDiv bucket_div(int E, int P) {
@@ -81,6 +86,10 @@ hipError_t launch_layout_partials(const LayoutArgs& a, const Launch& L) {
 hipError_t launch_layout_finish(const LayoutArgs& a, const Launch& L) {
     const int nt = num_tiles(a.T);
     return launch_kernel(layout_finish_kernel, dim3(1), dim3(kTile), L, a, nt > 0 ? nt : 1);
+}
+
+hipError_t launch_zero_words(uint32_t* p, int n, const Launch& L) {
+    return launch_kernel(zero_words_kernel, dim3((n + kTile - 1) / kTile), dim3(kTile), L, p, n);
 }
 
 }  // namespace moedx

@@ -90,6 +90,20 @@ def test_releases_wait_for_the_end_of_a_capture():
     assert done == [3, 2, 1] and not bm._deferred
 
 
-
 def test_ctx_set_stream_rejects_null(capi):
     assert capi.moedx_ctx_set_stream(None, ctypes.c_void_p(256)) == capi.MOEDX_EINVAL
+
+
+def test_static_layout_validates_before_hip(capi):
+    """The allocation-free layout rejects bad shapes and sizes past its static
+    scratch before any HIP call (dummy non-null pointers are never touched)."""
+    p = ctypes.c_void_p(256)
+    assert capi.moedx_get_dispatch_layout_static(p, 10, 2, 16, 3, p, p, p, None) == capi.MOEDX_EINVAL
+    assert capi.moedx_get_dispatch_layout_static(p, 10, 0, 16, 4, p, p, p, None) == capi.MOEDX_EINVAL
+    assert capi.moedx_get_dispatch_layout_static(p, 10, 2, 16, 65, p, p, p, None) == capi.MOEDX_EINVAL
+    assert capi.moedx_get_dispatch_layout_static(p, -1, 2, 16, 4, p, p, p, None) == capi.MOEDX_EINVAL
+    assert capi.moedx_get_dispatch_layout_static(None, 10, 2, 16, 4, p, p, p, None) == capi.MOEDX_EINVAL
+    # 2^20 tokens, 1024 experts, 64 buckets need far more than the 1 MiB scratch
+    rc = capi.moedx_get_dispatch_layout_static(p, 1 << 20, 8, 1024, 64, p, p, p, None)
+    assert rc == capi.MOEDX_ECAPACITY
+    assert "static scratch" in capi.last_error()
