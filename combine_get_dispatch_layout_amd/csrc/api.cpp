@@ -34,11 +34,10 @@ struct moedx_ctx {
     hipStream_t stream;      // the ctx's own stream (default priority)
     bool owns_stream;        // made by moedx_create (else the caller's, moedx_ctx_set_stream)
     hipEvent_t order_event;  // orders the ctx stream after the caller's
-    void* scratch;           // layout ticket + partial counts of the standalone layout
+    void* scratch;           // the handle layouts' ticket + get_dispatch_layout's counters
     size_t scratch_bytes;
     unsigned int* ticket;    // zero between layout launches
-    int32_t* group_cnt;      // [ceil(max_tokens/64), R]
-    int32_t* tile_expert;    // [ceil(max_tokens/256), E]
+    unsigned long long* acc; // [E + R] counters of get_dispatch_layout, zero between launches
     int32_t* pinned;         // host readback: [0] = N, [1..E] = per-expert counts
     moedx_stats stats;
 };
@@ -291,13 +290,13 @@ static int finish_pending(moedx_ctx* ctx, const moedx_handle* h, hipStream_t run
 // ---- the allocation-free layout ---------------------------------------------
 //
 // moedx_get_dispatch_layout_static keeps what moedx_get_dispatch_layout keeps
-// in a ctx's scratch (the ticket counter, the group and tile partial counts)
-// in this file-scope device array instead: every GPU the library runs on holds
-// its own copy, from the code object's load until the process ends.  Host code
-// never passes `scratch` itself to a kernel (on the host it names a stand-in,
-// not device memory): the first call on a device takes the device address with
+// in a ctx's scratch (the E + R counters of the totals) in this file-scope
+// device array instead: every GPU the library runs on holds its own copy,
+// from the code object's load until the process ends.  Host code never passes
+// `scratch` itself to a kernel (on the host it names a stand-in, not device
+// memory): the first call on a device takes the device address with
 // hipGetSymbolAddress and keeps it per device.
-constexpr size_t kStaticScratchBytes = size_t(1) << 20;
+constexpr size_t kStaticScratchBytes = size_t(16) << 10;
 static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
@@ -306,11 +305,8 @@ constexpr int kMaxDevices = 64;
 std::mutex g_static_mu;
 unsigned char* g_static_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
 
-// Carve of the static scratch: the ticket, then group and tile partials.
-size_t static_layout_bytes(int T, int E, int R) {
-    return 256 + align256((size_t)std::max(num_groups(T), 1) * R * 4) +
-           align256((size_t)std::max(num_tiles(T), 1) * E * 4);
-}
+// The static scratch a layout of E experts in R buckets uses: its counters.
+size_t static_layout_bytes(int E, int R) { return (size_t)(E + R) * 8; }
 
 }  // namespace
 
@@ -348,21 +344,18 @@ int moedx_create(moedx_ctx** out, int device, int num_experts, int num_ranks, in
     }
     c->C = num_channels;
     c->max_tokens = max_tokens;
-    const int nt = std::max(num_tiles(max_tokens), 1);
-    const int ng = std::max(num_groups(max_tokens), 1);
-    c->scratch_bytes = 256 + align256((size_t)ng * num_ranks * 4) +
-                       align256((size_t)nt * num_experts * 4);
+    c->scratch_bytes = 256 + align256((size_t)(num_experts + num_ranks) * 8);
     hipError_t e = hipSetDevice(device);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
     if (e == hipSuccess) c->owns_stream = true;
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->order_event, hipEventDisableTiming);
     if (e == hipSuccess) e = hipMalloc(&c->scratch, c->scratch_bytes);
-    if (e == hipSuccess) e = hipMemset(c->scratch, 0, c->scratch_bytes);  // the ticket starts at 0
+    // the ticket and the counters start at 0 (and every launch leaves them there)
+    if (e == hipSuccess) e = hipMemset(c->scratch, 0, c->scratch_bytes);
     if (e == hipSuccess) {
         char* p = static_cast<char*>(c->scratch);
         c->ticket = reinterpret_cast<unsigned int*>(p);
-        c->group_cnt = reinterpret_cast<int32_t*>(p + 256);
-        c->tile_expert = reinterpret_cast<int32_t*>(p + 256 + align256((size_t)ng * num_ranks * 4));
+        c->acc = reinterpret_cast<unsigned long long*>(p + 256);
     }
     if (e == hipSuccess)
         e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned), (size_t)(num_experts + 1) * 4,
@@ -497,12 +490,7 @@ int moedx_get_dispatch_layout(moedx_ctx* ctx, const int64_t* topk_idx, int T, in
     a.is_token_in_rank = is_token_in_rank;
     a.num_tokens_per_rank = num_tokens_per_rank;
     a.num_tokens_per_expert = num_tokens_per_expert;
-    a.group_cnt = ctx->group_cnt;
-    a.tile_expert = ctx->tile_expert;
-    a.itr_in = nullptr;
-    a.experts_in = nullptr;
-    a.ticket = ctx->ticket;
-    HIP_OR_FAIL(launch_layout(a, ex.launch()));
+    HIP_OR_FAIL(launch_layout_totals(a, ctx->acc, ex.launch()));
     ctx->stats.layout_launches += 1;
     return exec_end(ex);
 }
@@ -520,12 +508,12 @@ int moedx_get_dispatch_layout_static(const int64_t* topk_idx, int T, int K, int 
     if ((T > 0 && (!topk_idx || !is_token_in_rank)) || !num_tokens_per_rank ||
         !num_tokens_per_expert)
         return fail(MOEDX_EINVAL, "NULL device pointer");
-    const size_t need = static_layout_bytes(T, E, R);
-    if (need > kStaticScratchBytes)
+    const size_t need = static_layout_bytes(E, R);
+    if (need > kStaticScratchBytes)  // not reached within the bounds above
         return fail(MOEDX_ECAPACITY,
-                    "T=%d, E=%d, R=%d need %zu bytes of the static scratch, which holds %zu "
+                    "E=%d, R=%d need %zu bytes of the static scratch, which holds %zu "
                     "(use moedx_get_dispatch_layout with a ctx)",
-                    T, E, R, need, kStaticScratchBytes);
+                    E, R, need, kStaticScratchBytes);
     const BucketDiv bucket = bucket_div(E, E / R);
     if (bucket.mul == 0) return fail(MOEDX_EINVAL, "no exact multiply-shift for E / R");
     int dev = 0;
@@ -539,15 +527,14 @@ int moedx_get_dispatch_layout_static(const int64_t* topk_idx, int T, int K, int 
             void* p = nullptr;
             HIP_OR_FAIL(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
             if (!p) return fail(MOEDX_EHIP, "hipGetSymbolAddress gave no address");
-            // The ticket must start at zero (every layout launch leaves it
+            // The counters must start at zero (every launch leaves them
             // there): cleared on this stream ahead of the first layout.  The
             // address is kept only once the clear is enqueued.
-            HIP_OR_FAIL(launch_zero_words(static_cast<uint32_t*>(p), 1, L));
+            HIP_OR_FAIL(launch_zero_words(static_cast<uint32_t*>(p), (int)(kStaticScratchBytes / 4), L));
             g_static_ptr[dev] = static_cast<unsigned char*>(p);
         }
         base = g_static_ptr[dev];
     }
-    unsigned int* ticket = reinterpret_cast<unsigned int*>(base);
     LayoutArgs a{};
     a.topk_idx = topk_idx;
     a.T = T;
@@ -562,13 +549,7 @@ int moedx_get_dispatch_layout_static(const int64_t* topk_idx, int T, int K, int 
     a.is_token_in_rank = is_token_in_rank;
     a.num_tokens_per_rank = num_tokens_per_rank;
     a.num_tokens_per_expert = num_tokens_per_expert;
-    a.group_cnt = reinterpret_cast<int32_t*>(base + 256);
-    a.tile_expert = reinterpret_cast<int32_t*>(
-        base + 256 + align256((size_t)std::max(num_groups(T), 1) * R * 4));
-    a.itr_in = nullptr;
-    a.experts_in = nullptr;
-    a.ticket = ticket;
-    HIP_OR_FAIL(launch_layout(a, L));
+    HIP_OR_FAIL(launch_layout_totals(a, reinterpret_cast<unsigned long long*>(base), L));
     return MOEDX_OK;
 }
 

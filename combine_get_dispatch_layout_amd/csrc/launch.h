@@ -146,6 +146,11 @@ hipError_t launch_layout_partials(const LayoutArgs& a, const Launch& L);
 // launch_layout_partials wrote.
 hipError_t launch_layout_finish(const LayoutArgs& a, const Launch& L);
 
+// get_dispatch_layout's outputs only (is_token_in_rank and the per-bucket and
+// per-expert totals; a.token_mask / a.slot_bucket written when non-null):
+// acc is E + R zeroed 64-bit accumulators, zero again when the launch ends.
+hipError_t launch_layout_totals(const LayoutArgs& a, unsigned long long* acc, const Launch& L);
+
 // Zero n 32-bit words with a kernel (capturable, unlike a memset node).
 hipError_t launch_zero_words(uint32_t* p, int n, const Launch& L);
 

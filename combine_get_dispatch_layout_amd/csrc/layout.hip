@@ -42,6 +42,58 @@ __global__ __launch_bounds__(kTile) void layout_finish_kernel(LayoutArgs a, int 
     layout_finish(a, ntiles, s, (const TileToken*)nullptr);
 }
 
+// get_dispatch_layout's outputs alone (the mask and the two count vectors):
+// no prefix is needed, so the totals come from one round of counting atomics
+// instead of partials, a fence, a ticket and a reload.  Each workgroup counts
+// its 256 tokens per expert and per bucket in LDS and adds every count to a
+// 64-bit accumulator as (1 << 32) + count, the high half counting arrivals;
+// the workgroup whose add sees the last arrival holds the total, writes it
+// and sets the accumulator back to zero for the next launch.  Every launch
+// leaves the accumulators at zero; two launches on one accumulator array must
+// not overlap.
+struct TotalsLds {
+    int32_t hist[kMaxExperts];
+    int32_t bucket[kMaxRanks];
+};
+
+template <int NS>
+__global__ __launch_bounds__(kTile) void layout_totals_kernel(LayoutArgs a,
+                                                              unsigned long long* __restrict__ acc,
+                                                              unsigned int ntiles) {
+    __shared__ TotalsLds s;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int T = a.T, K = a.K, E = a.E, R = a.R;
+    const int t = (int)blockIdx.x * kTile + tid;
+    for (int e = tid; e < E; e += kTile) s.hist[e] = 0;
+    if (tid < R) s.bucket[tid] = 0;
+    __syncthreads();
+    TileToken tk;
+    tk.mask = 0;
+#pragma unroll
+    for (int w = 0; w < kMaxTopk / 4; ++w) tk.sb[w] = 0xffffffffu;
+    if (t < T) tk.mask = tile_slots<NS, true>(a, a.topk_idx + (int64_t)t * K, s, &tk);
+    // tokens of this wave per bucket: lane r keeps bucket r's count
+    int32_t cnt = 0;
+    for (int r = 0; r < R; ++r) {
+        const int c = __popcll(__ballot((tk.mask >> r) & 1u));
+        cnt = lane == r ? c : cnt;
+    }
+    if (lane < R && cnt) atomicAdd(&s.bucket[lane], cnt);
+    if (t < T) layout_token_outputs(a, t, tk);
+    __syncthreads();
+    const unsigned long long arrive = 1ull << 32;
+    for (int i = tid; i < E + R; i += kTile) {
+        const uint32_t v = (uint32_t)(i < E ? s.hist[i] : s.bucket[i - E]);
+        const unsigned long long old = atomicAdd(acc + i, arrive | v);
+        if ((unsigned int)(old >> 32) == ntiles - 1) {  // the last arrival: the total
+            const int32_t total = (int32_t)((uint32_t)old + v);
+            if (i < E) a.num_tokens_per_expert[i] = total;
+            else a.num_tokens_per_rank[i - E] = total;
+            atomicExch(acc + i, 0ull);
+        }
+    }
+}
+
 __global__ __launch_bounds__(kTile) void zero_words_kernel(uint32_t* __restrict__ p, int n) {
     const int i = blockIdx.x * kTile + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -86,6 +138,15 @@ hipError_t launch_layout_partials(const LayoutArgs& a, const Launch& L) {
 hipError_t launch_layout_finish(const LayoutArgs& a, const Launch& L) {
     const int nt = num_tiles(a.T);
     return launch_kernel(layout_finish_kernel, dim3(1), dim3(kTile), L, a, nt > 0 ? nt : 1);
+}
+
+hipError_t launch_layout_totals(const LayoutArgs& a, unsigned long long* acc, const Launch& L) {
+    const int nt = num_tiles(a.T) > 0 ? num_tiles(a.T) : 1;
+    if (a.K <= kMaxTopk / 2)
+        return launch_kernel(layout_totals_kernel<kMaxTopk / 2>, dim3(nt), dim3(kTile), L, a, acc,
+                             (unsigned int)nt);
+    return launch_kernel(layout_totals_kernel<kMaxTopk>, dim3(nt), dim3(kTile), L, a, acc,
+                         (unsigned int)nt);
 }
 
 hipError_t launch_zero_words(uint32_t* p, int n, const Launch& L) {

@@ -203,15 +203,15 @@ MOEDX_API int moedx_get_dispatch_layout(moedx_ctx *ctx, const int64_t *topk_idx,
 /* get_dispatch_layout for callers that cannot allocate (code under HIP graph
  * capture, serving loops or harnesses that forbid allocation): the same
  * outputs as moedx_get_dispatch_layout, for E experts in R buckets, without a
- * ctx.  It allocates nothing: its ticket and partial counts live in a static
- * device array of 1 MiB inside the library (one per GPU, held until the
- * process ends), which bounds 256 + 4*ceil(T/64)*R + 4*ceil(T/256)*E (each
- * term rounded up to 256 bytes); beyond that it returns MOEDX_ECAPACITY.
- * Runs on the current device, on `stream` (a stream of that device), and
- * returns without waiting.  Calls on one GPU share that array: two calls
- * that overlap (on different streams, or from different threads) race and
- * give wrong results; order them.  R in [1, 64], E in [1, 1024], E % R == 0,
- * K in [1, 16], T in [0, 2^24]; other errors as moedx_get_dispatch_layout. */
+ * ctx.  It allocates nothing: its E + R counters (8 bytes each) live in a
+ * static device array of 16 KiB inside the library (one per GPU, held until
+ * the process ends), which holds them for every E and R accepted here (a
+ * request past it would return MOEDX_ECAPACITY).  Runs on the current device,
+ * on `stream` (a stream of that device), and returns without waiting.  Calls
+ * on one GPU share that array: two calls that overlap (on different streams,
+ * or from different threads) race and give wrong results; order them.
+ * R in [1, 64], E in [1, 1024], E % R == 0, K in [1, 16], T in [0, 2^24];
+ * other errors as moedx_get_dispatch_layout. */
 MOEDX_API int moedx_get_dispatch_layout_static(const int64_t *topk_idx, int T, int K, int E, int R,
                                                int32_t *num_tokens_per_rank,
                                                int32_t *num_tokens_per_expert,
