@@ -141,6 +141,41 @@ def cpu_threads():
     return max(n, 1)
 
 
+def hbm_ceilings(nbytes, n, flush):
+    """What plain PyTorch kernels reach on this machine over buffers of `nbytes`:
+    a write-only fill and a copy, each launched n times back to back over
+    enough buffers that every launch reads from (and writes to) HBM rather than
+    the Infinity Cache; GB/s of bytes read plus written."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    k = input_copies(nbytes)
+    words = nbytes // 4
+    bufs = [torch.ones(words, dtype=torch.float32, device=dev) for _ in range(k)]
+    outs = [torch.empty(words, dtype=torch.float32, device=dev) for _ in range(k)]
+    ops = {"write_GBps": (lambda i: outs[i].fill_(0.5), nbytes),
+           "copy_GBps": (lambda i: outs[i].copy_(bufs[i]), 2 * nbytes)}
+    res = {"bytes": int(nbytes), "buffers": k}
+    for name, (op, moved) in ops.items():
+        for i in range(k):  # warm up, fill the rotation
+            op(i)
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            op(i % k)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        res[name] = round(moved / (ms * 1e-3) / 1e9, 1)
+    res["note"] = ("torch's fill_ (write) and copy_ kernels, back to back over "
+                   f"{k} rotating buffers of {nbytes / 1e6:.0f} MB")
+    del bufs, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def kernel_us_distribution(C, stream, launch, n, flush):
     """Per-launch kernel durations of n back-to-back launches: HIP events
     stamped at each kernel's own start and end.  launch(i, exec_ptr) enqueues
@@ -762,6 +797,21 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
                                 dict(note, per_launch_us=dist_d), cpu_d)
     rows["ll_combine"] = entry(w, "ll_combine", ms_c, row_bytes("ll_combine", T, H, K, E, V=V),
                                dict(note, per_launch_us=dist_c), cpu_c)
+    # the launch floor: the same call with no token launches one workgroup that
+    # only writes the E counts (zeros), timed the way every row above is
+    def ll_empty(s):
+        def f():
+            h = ctypes.c_void_p()
+            C.check(C.moedx_ll_dispatch(buf.ctx, None, None, 0, K, H, cap, None, P(s["cnt"]),
+                                        P(s["ws"]), nb.value, ctypes.byref(h), cur[0]))
+            C.moedx_handle_destroy(h)
+        return f
+
+    fns = [ll_empty(s) for s in llsets]
+    rows["launch_floor"] = {
+        "us": round(timed(fns) * 1e3, 2), "per_launch_us": per_launch(fns),
+        "note": "a one-workgroup kernel that writes 1 KB (the low-latency dispatch of an empty "
+                "batch), timed as the rows above: what any launch costs on this path"}
     for s in llsets:
         if s["h"] is not None:
             C.moedx_handle_destroy(s["h"])
@@ -976,9 +1026,9 @@ def main():
                                          ctypes.byref(h), e))
         return h
 
-    def layout_then_dispatch(j, e_scan=None):
+    def layout_then_dispatch(j):
         layout_call(lay_out[j])
-        h = prepare_from(sets[j], lay_out[j], e_scan if e_scan is not None else exr)
+        h = prepare_from(sets[j], lay_out[j])
         pack(h, sets[j])
         C.moedx_handle_destroy(h)
 
@@ -1022,8 +1072,6 @@ def main():
                 C.moedx_handle_destroy(prepare(sets[j], e))
             elif op == "pack":
                 dispatch(sets[j], exr, e)
-            elif op == "scan":
-                layout_then_dispatch(j, e)
             else:
                 combine(handles[j], sets[j], e)
         return kernel_us_distribution(C, stream, launch, n, flush)
@@ -1068,8 +1116,11 @@ def main():
     dist = {op: op_kernel_us(op, args.steps) for op in ("layout", "pack", "combine")}
     t_pack = dist["pack"]["mean"] * 1e-3  # ms: the first pack alone, kernel-stamped
     log("[bench] the pages' call order: get_dispatch_layout, dispatch given its outputs, combine")
+    st0 = buf.stats()
     t_ltd = op_avg_ms("layout_then_dispatch", args.steps)
-    scan_dist = op_kernel_us("scan", args.steps)
+    st1 = buf.stats()
+    ltd_launches = {k: round((st1[k] - st0[k]) / args.steps, 3)
+                    for k in ("layout_launches", "scan_launches", "pack_launches")}
 
     # Exact mode through the API on the host clock: the host waits for N after
     # the layout (no capacity bound), then the pack and the combine run.
@@ -1098,22 +1149,10 @@ def main():
     for h in handles:
         C.moedx_handle_destroy(h)
 
-    log("[bench] plain device copy of one receive buffer (context: practical ceiling)")
-    nb = 2 * N * H
-    src_c = torch.empty(nb // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
-    dst_c = torch.empty_like(src_c)
-    t_copy = []
-    for _ in range(10):
-        flush()
-        ea_, eb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ea_.record(stream)
-        dst_c.copy_(src_c)
-        eb_.record(stream)
-        t_copy.append((ea_, eb_))
-    torch.cuda.synchronize()
-    copy_ms = statistics.median(a.elapsed_time(b) for a, b in t_copy)
-    copy_gbs = 2 * nb / (copy_ms * 1e-3) / 1e9
-    del src_c, dst_c
+    log("[bench] plain device read, write and copy of one receive buffer's size (context: "
+        "practical ceilings)")
+    ceil = hbm_ceilings(2 * N * H, max(args.steps, 10), flush)
+    copy_gbs = ceil["copy_GBps"]
 
     t_comb_k = dist["combine"]["mean"] * 1e-3
     kern = {"pack": (t_pack, bytes_["pack"]), "combine": (t_comb_k, bytes_["combine"])}
@@ -1182,12 +1221,13 @@ def main():
             "GBps": round(step_bytes / ((t_ltd + t_comb) * 1e-3) / 1e9, 1),
             "roofline_frac": round(step_bytes / ((t_ltd + t_comb) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "tokens_per_s": round(T / ((t_ltd + t_comb) * 1e-3), 1),
-            "scan_kernel_us_per_launch": scan_dist,
+            "launches_per_dispatch": ltd_launches,
             "note": "the normal-kernel example's order: get_dispatch_layout, then the first "
                     "dispatch given num_tokens_per_rank / is_token_in_rank / "
-                    "num_tokens_per_expert (a scan of the handle from them, no second layout, "
-                    "then the first pack), then the same combine; same buffer rotation and "
-                    "byte count as the step"},
+                    "num_tokens_per_expert (its handle borrows the partials the layout left "
+                    "in the ctx: no second layout and no scan, the first pack finishes the "
+                    "handle), then the same combine; same buffer rotation and byte count as "
+                    "the step"},
         "pipelined_ms_per_step": round(ms_pipe, 5),
         "exact_mode_api_wall_us": {
             "median": round(statistics.median(wall_exact), 1),
@@ -1197,6 +1237,7 @@ def main():
                     "combine, host wait"},
         "pipelined_GBps_cache_assisted": round(step_bytes / (ms_pipe * 1e-3) / 1e9, 1),
         "copy_ceiling_GBps": round(copy_gbs, 1),
+        "hbm_ceilings": ceil,
         "algorithmic_bytes": bytes_,
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,

@@ -35,9 +35,29 @@ struct moedx_ctx {
     bool owns_stream;        // made by moedx_create (else the caller's, moedx_ctx_set_stream)
     hipEvent_t order_event;  // orders the ctx stream after the caller's
     void* scratch;           // the handle layouts' ticket + get_dispatch_layout's counters
-    size_t scratch_bytes;
+    size_t scratch_bytes;    //   and the partials it leaves for a handle to borrow
     unsigned int* ticket;    // zero between layout launches
     unsigned long long* acc; // [E + R] counters of get_dispatch_layout, zero between launches
+    // What the last get_dispatch_layout left: the partials a handle scanned
+    // from its outputs would hold ([max_tokens] masks, [max_tokens, 16] slot
+    // buckets, [ceil(max_tokens/64), R] group counts, [C + 1, R] channel
+    // partials, [E] expert totals), and which call that was.
+    uint64_t* lay_mask;
+    int8_t* lay_slot_bucket;
+    int32_t* lay_group_cnt;
+    int32_t* lay_chan_part;
+    int32_t* lay_experts;
+    struct {
+        bool valid;
+        const int64_t* topk_idx;
+        const uint8_t* is_token_in_rank;
+        const int32_t* num_tokens_per_expert;
+        int T, K;
+        hipStream_t stream;  // where that layout ran
+    } last;
+    moedx_handle* pending;   // the handle borrowing those partials, before its first pack
+    hipEvent_t borrow_done;  // recorded after a first pack that read them on another stream
+    bool borrow_armed;       // borrow_done recorded since the last layout
     int32_t* pinned;         // host readback: [0] = N, [1..E] = per-expert counts
     moedx_stats stats;
 };
@@ -53,6 +73,12 @@ struct moedx_handle {
     mutable bool rows_written;  // send_head / recv_src_idx filled by a dispatch
     bool experts_given;         // prepared from get_dispatch_layout's outputs: the expert
                                 // totals were copied, the tiles' expert partials never exist
+    // Borrowing the partials that ctx's last get_dispatch_layout left in its
+    // scratch (prepared from exactly those outputs): set until the first pack
+    // reads them, or until they are copied into the handle's own arrays.
+    mutable moedx_ctx* borrow_ctx;
+    mutable hipEvent_t adopted;  // recorded after a copy enqueued on another op's stream
+    bool orphaned;               // its borrow_ctx was destroyed first: nothing to finish from
     // Capacity mode: prepared with the layout's partials only; the first
     // dispatch or combine finishes the prefixes (or launches the finishing
     // step first).
@@ -310,6 +336,59 @@ size_t static_layout_bytes(int E, int R) { return (size_t)(E + R) * 8; }
 
 }  // namespace
 
+// A borrowing handle's partials copied from its ctx's scratch into its own
+// arrays, on `run`: the handle becomes one scanned from the layout's outputs
+// whose prefixes are still pending.  `elsewhere`: the copy runs on the stream
+// of another op (a layout about to overwrite the scratch); the handle's next
+// op then waits for it.
+static int settle_borrow(moedx_handle* h, hipStream_t run, bool elsewhere) {
+    moedx_ctx* c = h->borrow_ctx;
+    if (!c) return MOEDX_OK;
+    AdoptArgs a{};
+    a.mask_src = c->lay_mask;
+    a.slot_bucket_src = c->lay_slot_bucket;
+    a.group_cnt_src = c->lay_group_cnt;
+    a.chan_part_src = c->lay_chan_part;
+    a.experts_src = c->lay_experts;
+    a.token_mask = h->token_mask;
+    a.is_token_in_rank = h->is_token_in_rank;
+    a.slot_bucket = h->slot_bucket;
+    a.group_cnt = h->group_cnt;
+    a.chan_part = h->chan_part;
+    a.num_tokens_per_expert = h->num_tokens_per_expert;
+    a.T = h->T;
+    a.K = h->K;
+    a.R = h->R;
+    a.E = h->E;
+    a.n_group_cnt = num_groups(h->T) * h->R;
+    a.n_chan_part = (h->C + 1) * h->R;
+    HIP_OR_FAIL(launch_adopt(a, Launch{run, nullptr, nullptr}));
+    c->stats.scan_launches += 1;
+    if (elsewhere) {
+        if (!h->adopted) HIP_OR_FAIL(hipEventCreateWithFlags(&h->adopted, hipEventDisableTiming));
+        HIP_OR_FAIL(hipEventRecord(h->adopted, run));
+    }
+    c->pending = nullptr;
+    h->borrow_ctx = nullptr;
+    return MOEDX_OK;
+}
+
+// Before an op reads a handle: a borrowed layout is copied in (on the op's own
+// stream), and a copy enqueued on another stream is waited for.
+static int handle_ready(const moedx_handle* hc, hipStream_t run) {
+    moedx_handle* h = const_cast<moedx_handle*>(hc);
+    if (h->orphaned)
+        return fail(MOEDX_ESTATE, "the ctx whose layout this handle borrowed was destroyed "
+                                  "before the handle's first use");
+    if (int rc = settle_borrow(h, run, false)) return rc;
+    if (h->adopted) {
+        HIP_OR_FAIL(hipStreamWaitEvent(run, h->adopted, 0));
+        (void)hipEventDestroy(h->adopted);
+        h->adopted = nullptr;
+    }
+    return MOEDX_OK;
+}
+
 extern "C" {
 
 const char* moedx_last_error(void) { return g_err; }
@@ -344,7 +423,14 @@ int moedx_create(moedx_ctx** out, int device, int num_experts, int num_ranks, in
     }
     c->C = num_channels;
     c->max_tokens = max_tokens;
-    c->scratch_bytes = 256 + align256((size_t)(num_experts + num_ranks) * 8);
+    const size_t mt = (size_t)std::max(max_tokens, 1);
+    const size_t ng = (size_t)std::max(num_groups(max_tokens), 1);
+    const size_t off_mask = 256 + align256((size_t)(num_experts + num_ranks) * 8);
+    const size_t off_sb = off_mask + align256(mt * 8);
+    const size_t off_gc = off_sb + align256(mt * kMaxTopk);
+    const size_t off_cp = off_gc + align256(ng * num_ranks * 4);
+    const size_t off_ex = off_cp + align256((size_t)(num_channels + 1) * num_ranks * 4);
+    c->scratch_bytes = off_ex + align256((size_t)num_experts * 4);
     hipError_t e = hipSetDevice(device);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
     if (e == hipSuccess) c->owns_stream = true;
@@ -356,7 +442,13 @@ int moedx_create(moedx_ctx** out, int device, int num_experts, int num_ranks, in
         char* p = static_cast<char*>(c->scratch);
         c->ticket = reinterpret_cast<unsigned int*>(p);
         c->acc = reinterpret_cast<unsigned long long*>(p + 256);
+        c->lay_mask = reinterpret_cast<uint64_t*>(p + off_mask);
+        c->lay_slot_bucket = reinterpret_cast<int8_t*>(p + off_sb);
+        c->lay_group_cnt = reinterpret_cast<int32_t*>(p + off_gc);
+        c->lay_chan_part = reinterpret_cast<int32_t*>(p + off_cp);
+        c->lay_experts = reinterpret_cast<int32_t*>(p + off_ex);
     }
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->borrow_done, hipEventDisableTiming);
     if (e == hipSuccess)
         e = hipHostMalloc(reinterpret_cast<void**>(&c->pinned), (size_t)(num_experts + 1) * 4,
                           hipHostMallocDefault);
@@ -371,11 +463,16 @@ int moedx_create(moedx_ctx** out, int device, int num_experts, int num_ranks, in
 
 int moedx_destroy(moedx_ctx* ctx) {
     if (!ctx) return MOEDX_OK;
+    if (ctx->pending) {  // it can no longer be finished
+        ctx->pending->borrow_ctx = nullptr;
+        ctx->pending->orphaned = true;
+    }
     (void)hipSetDevice(ctx->device);
     if (ctx->stream) (void)hipStreamSynchronize(ctx->stream);
     if (ctx->scratch) (void)hipFree(ctx->scratch);
     if (ctx->pinned) (void)hipHostFree(ctx->pinned);
     if (ctx->order_event) (void)hipEventDestroy(ctx->order_event);
+    if (ctx->borrow_done) (void)hipEventDestroy(ctx->borrow_done);
     if (ctx->stream && ctx->owns_stream) (void)hipStreamDestroy(ctx->stream);
     delete ctx;
     return MOEDX_OK;
@@ -476,6 +573,15 @@ int moedx_get_dispatch_layout(moedx_ctx* ctx, const int64_t* topk_idx, int T, in
         return fail(MOEDX_EINVAL, "NULL device pointer");
     Exec ex;
     if (int rc = exec_begin(ctx, exec, &ex)) return rc;
+    // The scratch is about to be rewritten: a handle still borrowing it gets
+    // its copy first, and a first pack that read it must have finished.
+    if (ctx->pending) {
+        if (int rc = settle_borrow(ctx->pending, ex.run, true)) return rc;
+    }
+    if (ctx->borrow_armed) {
+        HIP_OR_FAIL(hipStreamWaitEvent(ex.run, ctx->borrow_done, 0));
+        ctx->borrow_armed = false;
+    }
     LayoutArgs a{};
     a.topk_idx = topk_idx;
     a.T = T;
@@ -490,8 +596,22 @@ int moedx_get_dispatch_layout(moedx_ctx* ctx, const int64_t* topk_idx, int T, in
     a.is_token_in_rank = is_token_in_rank;
     a.num_tokens_per_rank = num_tokens_per_rank;
     a.num_tokens_per_expert = num_tokens_per_expert;
+    // the partials a handle prepared from these outputs borrows
+    a.token_mask = ctx->lay_mask;
+    a.slot_bucket = ctx->lay_slot_bucket;
+    a.group_cnt = ctx->lay_group_cnt;
+    a.chan_part = ctx->lay_chan_part;
+    a.experts_copy = ctx->lay_experts;
+    ctx->last.valid = false;
     HIP_OR_FAIL(launch_layout_totals(a, ctx->acc, ex.launch()));
     ctx->stats.layout_launches += 1;
+    ctx->last.valid = true;
+    ctx->last.topk_idx = topk_idx;
+    ctx->last.is_token_in_rank = is_token_in_rank;
+    ctx->last.num_tokens_per_expert = num_tokens_per_expert;
+    ctx->last.T = T;
+    ctx->last.K = K;
+    ctx->last.stream = ex.run;
     return exec_end(ex);
 }
 
@@ -616,13 +736,27 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
     Exec ex;
     int rc = exec_begin(ctx, exec, &ex);
     hipError_t e = hipSuccess;
-    if (rc == MOEDX_OK) {
-        // Capacity mode, where a first bf16 dispatch can finish the prefixes
-        // in its own launch: the partials only, and the first dispatch (or
-        // combine) on the handle finishes them.  Elsewhere the layout kernel
-        // writes every prefix itself.
-        const bool partials =
-            capacity_rows > 0 && T > 0 && pack_first_fits(T, h->R, h->E, h->C);
+    // Capacity mode, where a first bf16 dispatch can finish the prefixes in
+    // its own launch: the partials only, and the first dispatch (or combine)
+    // on the handle finishes them.  Elsewhere the layout kernel writes every
+    // prefix itself.
+    const bool partials = capacity_rows > 0 && T > 0 && pack_first_fits(T, h->R, h->E, h->C);
+    // Given exactly the outputs of this ctx's last get_dispatch_layout, the
+    // handle borrows the partials that call left in the ctx's scratch: nothing
+    // runs now, and the first pack finishes the handle from them.
+    const bool borrow = partials && from_layout && ctx->last.valid &&
+                        ctx->last.topk_idx == topk_idx &&
+                        ctx->last.is_token_in_rank == is_token_in_rank &&
+                        ctx->last.num_tokens_per_expert == num_tokens_per_expert &&
+                        ctx->last.T == T && ctx->last.K == K;
+    if (rc == MOEDX_OK && borrow) {
+        if (ctx->pending) rc = settle_borrow(ctx->pending, ex.run, true);  // one borrower at a time
+        if (rc == MOEDX_OK) {
+            e = ex.no_kernel();
+            if (e != hipSuccess) rc = hip_fail(e, "event record");
+        }
+        h->prefixes_pending = true;
+    } else if (rc == MOEDX_OK) {
         LayoutArgs a = handle_layout_args(ctx, h, topk_idx, !partials);
         if (from_layout) {  // the scan of the given layout outputs
             a.itr_in = is_token_in_rank;
@@ -631,8 +765,9 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
         e = partials ? launch_layout_partials(a, ex.launch()) : launch_layout(a, ex.launch());
         h->prefixes_pending = partials;
         if (e != hipSuccess) rc = hip_fail(e, "layout launch");
+        if (rc == MOEDX_OK)
+            (from_layout ? ctx->stats.scan_launches : ctx->stats.layout_launches) += 1;
     }
-    if (rc == MOEDX_OK) (from_layout ? ctx->stats.scan_launches : ctx->stats.layout_launches) += 1;
     if (rc == MOEDX_OK && capacity_rows == 0) {
         // Exact mode: the host waits for N and the per-expert counts.
         e = hipMemcpyAsync(ctx->pinned, h->num_recv, (size_t)(1 + h->E) * 4,
@@ -650,6 +785,10 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
     if (rc != MOEDX_OK) {
         delete h;
         return rc;
+    }
+    if (borrow) {
+        h->borrow_ctx = ctx;
+        ctx->pending = h;
     }
     *out = h;
     return MOEDX_OK;
@@ -712,6 +851,7 @@ int moedx_handle_finish(moedx_ctx* ctx, const moedx_handle* h, const moedx_exec*
         return fail(MOEDX_ESTATE, "handle was prepared on a ctx with a different E/R/C");
     Exec ex;
     if (int rc = exec_begin(ctx, exec, &ex)) return rc;
+    if (int rc = handle_ready(h, ex.run)) return rc;
     if (h->prefixes_pending) {
         HIP_OR_FAIL(launch_layout_finish(handle_layout_args(ctx, h, nullptr, false), ex.launch()));
         (h->experts_given ? ctx->stats.scan_launches : ctx->stats.layout_launches) += 1;
@@ -723,6 +863,9 @@ int moedx_handle_finish(moedx_ctx* ctx, const moedx_handle* h, const moedx_exec*
 }
 
 int moedx_handle_destroy(moedx_handle* h) {
+    if (!h) return MOEDX_OK;
+    if (h->borrow_ctx && h->borrow_ctx->pending == h) h->borrow_ctx->pending = nullptr;
+    if (h->adopted) (void)hipEventDestroy(h->adopted);
     delete h;
     return MOEDX_OK;
 }
@@ -771,14 +914,38 @@ int moedx_dispatch(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, 
     if (T > 0 && quant == MOEDX_QUANT_NONE && h->prefixes_pending &&
         pack_first_fits(T, h->R, h->E, h->C)) {
         // One launch finishes the handle and packs the rows.
-        HIP_OR_FAIL(launch_pack_bf16_first(handle_layout_args(ctx, h, topk_idx, false), x, H,
-                                           h->capacity, hr, recv_x, topk_weights, recv_topk_idx,
-                                           recv_topk_weights, ex.launch()));
+        LayoutArgs la = handle_layout_args(ctx, h, topk_idx, false);
+        HandleTokens ht{};
+        moedx_ctx* bc = h->borrow_ctx;
+        if (bc) {  // partials borrowed from a layout: read from its ctx's scratch
+            la.group_cnt = bc->lay_group_cnt;
+            la.chan_part = bc->lay_chan_part;
+            la.token_mask = bc->lay_mask;
+            la.tile_expert = nullptr;
+            la.experts_in = bc->lay_experts;
+            ht = HandleTokens{h->token_mask, h->is_token_in_rank, h->slot_bucket,
+                              bc->lay_slot_bucket};
+        } else if (int rc = handle_ready(h, ex.run)) {  // also refuses an orphaned borrower
+            return rc;
+        }
+        HIP_OR_FAIL(launch_pack_bf16_first(la, ht, x, H, h->capacity, hr, recv_x, topk_weights,
+                                           recv_topk_idx, recv_topk_weights, ex.launch()));
         ctx->stats.pack_launches += 1;
         h->prefixes_pending = false;
         h->rows_written = true;
+        if (bc) {
+            // Read on another stream than the layout's: the ctx's next layout
+            // waits for this pack (on one stream, the stream orders them).
+            if (ex.run != bc->last.stream) {
+                HIP_OR_FAIL(hipEventRecord(bc->borrow_done, ex.run));
+                bc->borrow_armed = true;
+            }
+            bc->pending = nullptr;
+            h->borrow_ctx = nullptr;
+        }
         return exec_end(ex);
     }
+    if (int rc = handle_ready(h, ex.run)) return rc;
     if (int rc = finish_pending(ctx, h, ex.run)) return rc;
     if (T == 0) {
         HIP_OR_FAIL(ex.no_kernel());
@@ -837,6 +1004,7 @@ int moedx_dispatch_fp8(moedx_ctx* ctx, const moedx_handle* h, const void* x, int
                     h->R, h->T, h->capacity > 0 ? h->capacity : h->n_host};
     const HandleRows hr = h->rows_written ? HandleRows{nullptr, nullptr}
                                           : HandleRows{h->send_head, h->recv_src_idx};
+    if (int rc = handle_ready(h, ex.run)) return rc;
     if (int rc = finish_pending(ctx, h, ex.run)) return rc;
     if (T == 0) {
         HIP_OR_FAIL(ex.no_kernel());
@@ -875,6 +1043,7 @@ int moedx_combine(moedx_ctx* ctx, const moedx_handle* h, const uint16_t* y, int 
     if (int rc = exec_begin(ctx, exec, &ex)) return rc;
     const RowMap rm{h->token_mask, h->group_prefix, h->rank_prefix_matrix, h->num_tokens_per_rank,
                     h->R, h->T, h->capacity > 0 ? h->capacity : h->n_host};
+    if (int rc = handle_ready(h, ex.run)) return rc;
     if (int rc = finish_pending(ctx, h, ex.run)) return rc;
     if (h->T == 0) {
         HIP_OR_FAIL(ex.no_kernel());

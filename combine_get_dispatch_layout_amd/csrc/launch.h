@@ -129,6 +129,7 @@ struct LayoutArgs {
     // num_tokens_per_expert [E] instead of from topk_idx (null otherwise).
     const uint8_t* itr_in;
     const int32_t* experts_in;
+    int32_t* experts_copy;  // get_dispatch_layout: a second copy of the expert totals (or null)
     unsigned int* ticket;                  // zero between launches; null for a launch that
                                            // takes no ticket (finishing step alone, first pack)
 };
@@ -174,15 +175,46 @@ struct HandleRows {
     int32_t* recv_src_idx;  // [rows]
 };
 
-// First dispatch (bf16) on a handle prepared with launch_layout_partials, in
-// one launch that also finishes the handle's prefixes; for T <= 4096, R a
-// multiple of 4 up to 16 and (C + 1) * R <= 768 (pack_first_fits).  `la`
-// carries every handle array.
+// Per-token handle arrays that a first pack writes when its handle borrowed
+// the partials of a get_dispatch_layout left in a ctx's scratch (all null
+// otherwise): each token's bucket mask and is_token_in_rank row, and its slot
+// buckets copied from slot_bucket_src.
+struct HandleTokens {
+    uint64_t* token_mask;        // [T]
+    uint8_t* is_token_in_rank;   // [T, R]
+    int8_t* slot_bucket;         // [T, K]
+    const int8_t* slot_bucket_src;
+};
+
+// First dispatch (bf16) on a handle prepared with launch_layout_partials (or
+// borrowing a layout's partials, ht), in one launch that also finishes the
+// handle's prefixes; for T <= 4096, R a multiple of 4 up to 16 and
+// (C + 1) * R <= 768 (pack_first_fits).  `la` carries every handle array
+// (group_cnt, chan_part and token_mask being the partials read).
 bool pack_first_fits(int T, int R, int E, int C);
-hipError_t launch_pack_bf16_first(const LayoutArgs& la, const void* x, int H, int64_t rows,
-                                  const HandleRows& hr, void* recv_x, const float* topk_weights,
-                                  int64_t* recv_topk_idx, float* recv_topk_weights,
-                                  const Launch& L);
+hipError_t launch_pack_bf16_first(const LayoutArgs& la, const HandleTokens& ht, const void* x,
+                                  int H, int64_t rows, const HandleRows& hr, void* recv_x,
+                                  const float* topk_weights, int64_t* recv_topk_idx,
+                                  float* recv_topk_weights, const Launch& L);
+
+// Copy of borrowed layout partials into a handle's own arrays (and its
+// is_token_in_rank rows from the token masks): what a scan of the layout's
+// outputs would have written.
+struct AdoptArgs {
+    const uint64_t* mask_src;
+    const int8_t* slot_bucket_src;
+    const int32_t* group_cnt_src;
+    const int32_t* chan_part_src;
+    const int32_t* experts_src;
+    uint64_t* token_mask;
+    uint8_t* is_token_in_rank;
+    int8_t* slot_bucket;
+    int32_t* group_cnt;
+    int32_t* chan_part;
+    int32_t* num_tokens_per_expert;
+    int T, K, R, E, n_group_cnt, n_chan_part;
+};
+hipError_t launch_adopt(const AdoptArgs& a, const Launch& L);
 
 hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
                             void* recv_x, const int64_t* topk_idx, const float* topk_weights,

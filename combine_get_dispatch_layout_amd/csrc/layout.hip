@@ -79,6 +79,13 @@ __global__ __launch_bounds__(kTile) void layout_totals_kernel(LayoutArgs a,
         cnt = lane == r ? c : cnt;
     }
     if (lane < R && cnt) atomicAdd(&s.bucket[lane], cnt);
+    // With a ctx: the group and channel partials a handle scanned from these
+    // outputs would hold, left in the ctx's scratch with the token masks and
+    // slot buckets (layout_token_outputs), so that a dispatch prepared from
+    // this layout can finish its handle in its first pack.
+    if (a.group_cnt)
+        group_partials(a, (int)blockIdx.x * kLayoutWaves + (tid >> 6), tk.mask, lane,
+                       a.chan_part != nullptr);
     if (t < T) layout_token_outputs(a, t, tk);
     __syncthreads();
     const unsigned long long arrive = 1ull << 32;
@@ -87,11 +94,33 @@ __global__ __launch_bounds__(kTile) void layout_totals_kernel(LayoutArgs a,
         const unsigned long long old = atomicAdd(acc + i, arrive | v);
         if ((unsigned int)(old >> 32) == ntiles - 1) {  // the last arrival: the total
             const int32_t total = (int32_t)((uint32_t)old + v);
-            if (i < E) a.num_tokens_per_expert[i] = total;
-            else a.num_tokens_per_rank[i - E] = total;
+            if (i < E) {
+                a.num_tokens_per_expert[i] = total;
+                if (a.experts_copy) a.experts_copy[i] = total;
+            } else {
+                a.num_tokens_per_rank[i - E] = total;
+            }
             atomicExch(acc + i, 0ull);
         }
     }
+}
+
+// One thread per token copies its mask, is_token_in_rank row and slot
+// buckets; the small partial arrays are copied by the first threads.
+__global__ __launch_bounds__(kTile) void adopt_kernel(AdoptArgs a) {
+    const int i = blockIdx.x * kTile + threadIdx.x;
+    if (i < a.T) {
+        const uint64_t m = a.mask_src[i];
+        a.token_mask[i] = m;
+        for (int r = 0; r < a.R; ++r)
+            a.is_token_in_rank[(int64_t)i * a.R + r] = (uint8_t)((m >> r) & 1u);
+        for (int k = 0; k < a.K; ++k)
+            a.slot_bucket[(int64_t)i * a.K + k] = a.slot_bucket_src[(int64_t)i * a.K + k];
+    }
+    const int n = gridDim.x * kTile;
+    for (int j = i; j < a.n_group_cnt; j += n) a.group_cnt[j] = a.group_cnt_src[j];
+    for (int j = i; j < a.n_chan_part; j += n) a.chan_part[j] = a.chan_part_src[j];
+    for (int j = i; j < a.E; j += n) a.num_tokens_per_expert[j] = a.experts_src[j];
 }
 
 __global__ __launch_bounds__(kTile) void zero_words_kernel(uint32_t* __restrict__ p, int n) {
@@ -147,6 +176,11 @@ hipError_t launch_layout_totals(const LayoutArgs& a, unsigned long long* acc, co
                              (unsigned int)nt);
     return launch_kernel(layout_totals_kernel<kMaxTopk>, dim3(nt), dim3(kTile), L, a, acc,
                          (unsigned int)nt);
+}
+
+hipError_t launch_adopt(const AdoptArgs& a, const Launch& L) {
+    const int nt = num_tiles(a.T) > 0 ? num_tiles(a.T) : 1;
+    return launch_kernel(adopt_kernel, dim3(nt), dim3(kTile), L, a);
 }
 
 hipError_t launch_zero_words(uint32_t* p, int n, const Launch& L) {

@@ -194,6 +194,50 @@ __device__ __forceinline__ uint64_t itr_row_mask(const ItrRow<MR>& x, int R) {
     return m;
 }
 
+// The partials of group g (the 64 tokens of one wave; this lane's token has
+// bucket mask `mask`): bucket counts over the group and, with channels, the
+// counts from the group's start to every channel boundary inside it.  Eight
+// buckets at a time: each token's bits for buckets j..j+7 are spread to one
+// byte each (a count never exceeds 64, so bytes never carry) and one wave
+// prefix sum per 32-bit half gives, at lane i, the counts over lanes 0..i of
+// four buckets.  Lane 63 holds the group counts; the counts from the group
+// start to a channel boundary at offset o are those of lane o - 1.  Lane r
+// stores bucket r's values.  Wave-uniform g; every lane takes part.
+__device__ __forceinline__ void group_partials(const LayoutArgs& a, int g, uint64_t mask, int lane,
+                                               bool with_channels) {
+    const int T = a.T, R = a.R;
+    const int g_begin = g * kGroup;
+    if (g_begin >= T) return;
+    // First channel boundary at or after g_begin: ceil(g_begin / per).
+    const int c_first =
+        with_channels ? (int)a.per_div.div((uint32_t)(g_begin + a.per - 1)) : a.C + 1;
+    for (int j = 0; j < R; j += 8) {
+        const uint32_t bits = (uint32_t)(mask >> j) & 0xffu;
+        const uint32_t lo = ((bits & 0xfu) * 0x00204081u) & 0x01010101u;
+        const uint32_t hi = ((bits >> 4) * 0x00204081u) & 0x01010101u;
+        const uint32_t slo = (uint32_t)wave_inclusive_sum((int32_t)lo);
+        const uint32_t shi = (uint32_t)wave_inclusive_sum((int32_t)hi);
+        const int rr = lane - j;  // this lane's bucket within the eight
+        const bool mine = rr >= 0 && rr < 8 && lane < R;
+        const int sh = 8 * (rr & 3);
+        {
+            const uint32_t w = rr < 4 ? __builtin_amdgcn_readlane(slo, 63)
+                                      : __builtin_amdgcn_readlane(shi, 63);
+            if (mine) a.group_cnt[(int64_t)g * R + lane] = (int32_t)((w >> sh) & 0xffu);
+        }
+        for (int c = c_first; c <= a.C; ++c) {
+            const int64_t b = layout_boundary(c, a.per, T);
+            if (b >= T || b >= g_begin + kGroup) break;
+            const int off = (int)(b - g_begin);
+            uint32_t w = 0;
+            if (off > 0)
+                w = rr < 4 ? __builtin_amdgcn_readlane(slo, off - 1)
+                           : __builtin_amdgcn_readlane(shi, off - 1);
+            if (mine) a.chan_part[(int64_t)c * R + lane] = (int32_t)((w >> sh) & 0xffu);
+        }
+    }
+}
+
 // Phase 1 for tile `tile` of `ntiles`.  Returns true in the workgroup that took
 // the last ticket (workgroup-uniform), which must then run layout_finish and
 // see that its own per-token outputs (*tk) are written; the other workgroups
@@ -256,45 +300,7 @@ __device__ __forceinline__ bool layout_tile(const LayoutArgs& a, int tile, int n
             }
             tk->mask = mask;
         }
-        // Bucket counts over the wave's 64 tokens (a group), eight buckets at
-        // a time: each token's bits for buckets j..j+7 are spread to one byte
-        // each (a count never exceeds 64, so bytes never carry) and one wave
-        // prefix sum per 32-bit half gives, at lane i, the counts over lanes
-        // 0..i of four buckets.  Lane 63 holds the group counts; the counts
-        // from the group start to a channel boundary at offset o are those of
-        // lane o - 1.  Lane r stores bucket r's values.
-        const int g = tile * kLayoutWaves + wave;
-        const int g_begin = g * kGroup;
-        if (g_begin < T) {  // wave-uniform; every lane takes part in the sums
-            // First channel boundary at or after g_begin: ceil(g_begin / per).
-            const int c_first =
-                with_channels ? (int)a.per_div.div((uint32_t)(g_begin + a.per - 1)) : a.C + 1;
-            for (int j = 0; j < R; j += 8) {
-                const uint32_t bits = (uint32_t)(mask >> j) & 0xffu;
-                const uint32_t lo = ((bits & 0xfu) * 0x00204081u) & 0x01010101u;
-                const uint32_t hi = ((bits >> 4) * 0x00204081u) & 0x01010101u;
-                const uint32_t slo = (uint32_t)wave_inclusive_sum((int32_t)lo);
-                const uint32_t shi = (uint32_t)wave_inclusive_sum((int32_t)hi);
-                const int rr = lane - j;  // this lane's bucket within the eight
-                const bool mine = rr >= 0 && rr < 8 && lane < R;
-                const int sh = 8 * (rr & 3);
-                {
-                    const uint32_t w = rr < 4 ? __builtin_amdgcn_readlane(slo, 63)
-                                              : __builtin_amdgcn_readlane(shi, 63);
-                    if (mine) a.group_cnt[(int64_t)g * R + lane] = (int32_t)((w >> sh) & 0xffu);
-                }
-                for (int c = c_first; c <= a.C; ++c) {
-                    const int64_t b = layout_boundary(c, a.per, T);
-                    if (b >= T || b >= g_begin + kGroup) break;
-                    const int off = (int)(b - g_begin);
-                    uint32_t w = 0;
-                    if (off > 0)
-                        w = rr < 4 ? __builtin_amdgcn_readlane(slo, off - 1)
-                                   : __builtin_amdgcn_readlane(shi, off - 1);
-                    if (mine) a.chan_part[(int64_t)c * R + lane] = (int32_t)((w >> sh) & 0xffu);
-                }
-            }
-        }
+        group_partials(a, tile * kLayoutWaves + wave, mask, lane, with_channels);
         if (!kFromLayout) {
             __syncthreads();
             for (int e = tid; e < E; e += kTile) a.tile_expert[(int64_t)tile * E + e] = s.hist[e];
@@ -430,6 +436,8 @@ __device__ __forceinline__ void layout_finish_fast(const LayoutArgs& a, int ntil
     __syncthreads();
     if (experts)
         for (int e = tid; e < E; e += kTile) a.num_tokens_per_expert[e] = s.hist[e];
+    else if (a.experts_in)  // totals given with the partials: copied into the handle
+        for (int e = tid; e < E; e += kTile) a.num_tokens_per_expert[e] = a.experts_in[e];
     // Bucket offsets: one wave prefix sum over the bucket totals.
     if (wave == 0) {
         const int32_t tot = lane < R ? s.total[lane] : 0;

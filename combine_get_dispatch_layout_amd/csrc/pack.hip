@@ -242,8 +242,8 @@ constexpr int kFirstTiles = 16;
 // launch waits for workgroup 0.
 template <int CPL, int RB>
 __global__ __launch_bounds__(kRowThreads) void pack_bf16_first_kernel(
-    LayoutArgs la, int ntiles, const u32x4* __restrict__ x, int H8, RowSplit rs, int64_t rows,
-    HandleRows hr, u32x4* __restrict__ recv_x, const float* __restrict__ topk_weights,
+    LayoutArgs la, HandleTokens ht, int ntiles, const u32x4* __restrict__ x, int H8, RowSplit rs,
+    int64_t rows, HandleRows hr, u32x4* __restrict__ recv_x, const float* __restrict__ topk_weights,
     int64_t* __restrict__ recv_topk_idx, float* __restrict__ recv_topk_weights) {
     __shared__ FirstLds s;
     if (blockIdx.x == 0) {
@@ -264,6 +264,13 @@ __global__ __launch_bounds__(kRowThreads) void pack_bf16_first_kernel(
     u32x4 v[CPL];
     load_row_part<CPL>(x + (int64_t)t * H8, c_begin, c_end, lane, v);
     const TokenRows d = token_rows_from_counts<RB>(gcnt, la.R, rows, t, lane);
+    if (part == 0 && ht.token_mask != nullptr) {  // a borrowed layout: the token's handle rows
+        if (lane == 0) ht.token_mask[t] = d.mask;
+        if (lane < la.R)
+            ht.is_token_in_rank[(int64_t)t * la.R + lane] = (uint8_t)((d.mask >> lane) & 1u);
+        if (lane < la.K)
+            ht.slot_bucket[(int64_t)t * la.K + lane] = ht.slot_bucket_src[(int64_t)t * la.K + lane];
+    }
     pack_bf16_store<CPL>(v, d, t, part, H8, c_begin, c_end, lane, la.R, hr, recv_x, la.topk_idx,
                          topk_weights, la.K, la.E, la.P, la.bucket, recv_topk_idx,
                          recv_topk_weights);
@@ -558,10 +565,10 @@ bool pack_first_fits(int T, int R, int E, int C) {
            R <= 16 && R % 4 == 0;
 }
 
-hipError_t launch_pack_bf16_first(const LayoutArgs& la, const void* x, int H, int64_t rows,
-                                  const HandleRows& hr, void* recv_x, const float* topk_weights,
-                                  int64_t* recv_topk_idx, float* recv_topk_weights,
-                                  const Launch& L) {
+hipError_t launch_pack_bf16_first(const LayoutArgs& la, const HandleTokens& ht, const void* x,
+                                  int H, int64_t rows, const HandleRows& hr, void* recv_x,
+                                  const float* topk_weights, int64_t* recv_topk_idx,
+                                  float* recv_topk_weights, const Launch& L) {
     const int T = la.T;
     const int H8 = H / 8;
     const int split = pack_split(H8, kWaveChunks);
@@ -571,8 +578,8 @@ hipError_t launch_pack_bf16_first(const LayoutArgs& la, const void* x, int H, in
     u32x4* rx = static_cast<u32x4*>(recv_x);
     const int ntiles = num_tiles(T);
 #define MOEDX_FIRST(N, B)                                                                       \
-    return launch_kernel(pack_bf16_first_kernel<N, B>, grid, block, L, la, ntiles, xs, H8, rs, \
-                         rows, hr, rx, topk_weights, recv_topk_idx, recv_topk_weights)
+    return launch_kernel(pack_bf16_first_kernel<N, B>, grid, block, L, la, ht, ntiles, xs, H8, \
+                         rs, rows, hr, rx, topk_weights, recv_topk_idx, recv_topk_weights)
 #define MOEDX_FIRST_CPL(B)              \
     switch (pick_cpl(rs.per)) {         \
         case 1: MOEDX_FIRST(1, B);      \

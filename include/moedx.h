@@ -149,11 +149,15 @@ MOEDX_API const char *moedx_last_error(void);
  * and sizes the ctx's scratch.  Allocates the ctx stream (default priority),
  * a small device scratch and a pinned host buffer; flags must be 0.
  * moedx_get_dispatch_layout and moedx_dispatch_prepare of one ctx share the
- * scratch's completion counter (and get_dispatch_layout its partial counts):
- * they must not run concurrently with each other (issue them on one stream,
- * or order them with events).  Every other call (dispatch, combine,
- * handle_finish, the low-latency calls) leaves that scratch alone and may
- * overlap with anything whose buffers it does not share. */
+ * scratch's completion counter (and get_dispatch_layout its counters and
+ * partials): they must not run concurrently with each other (issue them on
+ * one stream, or order them with events); the first moedx_dispatch of a
+ * handle that borrowed a layout's partials (moedx_dispatch_prepare) counts as
+ * part of that layout here, and when it runs on another stream than the
+ * layout, the ctx's next get_dispatch_layout waits for it by itself.  Every
+ * other call (dispatch, combine, handle_finish, the low-latency calls) leaves
+ * that scratch alone and may overlap with anything whose buffers it does not
+ * share. */
 MOEDX_API int moedx_create(moedx_ctx **out, int device, int num_experts, int num_ranks,
                            int num_channels, int max_tokens, uint32_t flags);
 MOEDX_API int moedx_destroy(moedx_ctx *ctx);
@@ -242,6 +246,17 @@ MOEDX_API int moedx_handle_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  * them, as the pages' call does; the bucket totals are recomputed by the scan,
  * so it is not read.  Alignment: num_tokens_per_expert 4 bytes,
  * is_token_in_rank 4 bytes when R % 4 == 0.  All three NULL: the layout runs.
+ * When they are exactly the outputs (same pointers, T and K) of this ctx's
+ * last moedx_get_dispatch_layout, in capacity mode where a first bf16
+ * dispatch finishes the handle in its own launch (below), not even the scan
+ * runs: the handle borrows the partial counts, token masks and slot buckets
+ * that get_dispatch_layout left in the ctx's scratch, and its first
+ * moedx_dispatch (bf16) builds the handle from them.  Any other first use, a
+ * later prepare that borrows the same layout, or the ctx's next
+ * moedx_get_dispatch_layout first copies them into the handle (one small
+ * kernel, counted as a scan).  See moedx_create for ordering the next layout
+ * after the first pack.  Destroying the ctx before the handle's first use
+ * leaves the handle unusable (MOEDX_ESTATE).
  *
  * Receive rows are bucket-major and, inside a bucket, in ascending token order
  * (channel order, then token order inside a channel); N = total rows.

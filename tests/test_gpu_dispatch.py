@@ -284,7 +284,10 @@ def test_layout_then_dispatch_and_combine(oracle, w, mode):
     comb, _, _ = buf.combine(recv_x, h, gate_weights=gw)
     torch.cuda.synchronize()
     st = buf.stats()
-    assert st["layout_launches"] == 1 and st["scan_launches"] == 1, st
+    # capacity mode with a one-launch first pack (T <= 4096, R a multiple of 4
+    # up to 16): the handle borrows the layout's partials and no scan runs
+    borrowed = bool(cap) and T <= 4096 and R % 4 == 0 and R <= 16
+    assert st["layout_launches"] == 1 and st["scan_launches"] == (0 if borrowed else 1), st
     assert st["pack_launches"] == 1 and st["combine_launches"] == 1, st
     check_handle(h, ref, N)
     assert_equal("recv_x", np_(recv_x)[:N], ref.recv_x)
