@@ -76,13 +76,14 @@ def algorithmic_bytes(T, H, K, E, R, C, N):
 
 
 TRAFFIC_SOURCES = {"layout": "layout.hip", "get_layout": "layout.hip", "pack": "pack.hip",
+                   "get_layout_fp8_skewed": "layout.hip",
                    "pack_fp8": "pack.hip", "pack_fp8_ue8m0": "pack.hip",
                    "pack_fp8_tensor": "pack.hip", "pack_fp8_prequant": "pack.hip",
                    "cached_dispatch": "pack.hip", "combine": "combine.hip",
                    "combine_fp8_skewed": "combine.hip", "combine_reuse": "combine.hip",
                    "ll_dispatch": "ll.hip", "ll_combine": "ll.hip"}
 # headers every kernel source includes: a change there changes the kernels too
-SHARED_HEADERS = ("launch.h", "rows.h", "fastdiv.h", "layout_core.h")
+SHARED_HEADERS = ("launch.h", "rows.h", "fastdiv.h", "layout_core.h", "fp8_codec.h")
 
 
 def source_digest(src):
