@@ -81,7 +81,8 @@ TRAFFIC_SOURCES = {"layout": "layout.hip", "get_layout": "layout.hip", "pack": "
                    "pack_fp8_tensor": "pack.hip", "pack_fp8_prequant": "pack.hip",
                    "cached_dispatch": "pack.hip", "combine": "combine.hip",
                    "combine_fp8_skewed": "combine.hip", "combine_reuse": "combine.hip",
-                   "ll_dispatch": "ll.hip", "ll_combine": "ll.hip"}
+                   "ll_dispatch": "ll.hip", "ll_combine": "ll.hip", "launch_floor": "ll.hip",
+                   "pack_ltd": "pack.hip"}
 # headers every kernel source includes: a change there changes the kernels too
 SHARED_HEADERS = ("launch.h", "rows.h", "fastdiv.h", "layout_core.h", "fp8_codec.h")
 
