@@ -247,10 +247,12 @@ class Buffer:
     # -- layout -----------------------------------------------------------------
     def get_dispatch_layout(self, topk_idx: torch.Tensor, num_experts: int,
                             previous_event: Optional[EventOverlap] = None,
-                            async_finish: bool = False, allocate_on_comm_stream: bool = False):
+                            async_finish: bool = False, allocate_on_comm_stream: bool = False,
+                            no_sync: bool = False):
         """Returns (num_tokens_per_rank, None, num_tokens_per_expert,
         is_token_in_rank, event); the None stands for the per-RDMA-rank counts,
-        which do not exist on one GPU."""
+        which do not exist on one GPU.  ``no_sync`` returns without blocking
+        (stream order only), as under graph capture."""
         assert num_experts == self.num_experts
         topk_idx = topk_idx.contiguous()
         T, K = topk_idx.shape
@@ -258,7 +260,7 @@ class Buffer:
         ntr = torch.empty(self.num_ranks, dtype=torch.int32, device=dev)
         nte = torch.empty(num_experts, dtype=torch.int32, device=dev)
         itr = torch.empty(T, self.num_ranks, dtype=torch.bool, device=dev)
-        ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream)
+        ex, done = self._exec(previous_event, async_finish, allocate_on_comm_stream, no_sync)
         C.check(C.moedx_get_dispatch_layout(self.ctx, _ptr(topk_idx), T, K, _ptr(ntr), _ptr(nte),
                                             _ptr(itr), ctypes.byref(ex)))
         self._keep(allocate_on_comm_stream, topk_idx, ntr, nte, itr)

@@ -3,8 +3,9 @@
 A capacity-mode first dispatch (layout with every prefix, pack with the
 handle rows and recv_topk_*, gate-weighted combine) needs no host
 synchronisation and records no memset, so it can be captured once and
-replayed with new routing and new rows each time.  Two contexts on two
-streams at once must not share any scratch memory.  Every result is compared
+replayed with new routing and new rows each time; so can get_dispatch_layout
+followed by a dispatch that borrows its partials, and the allocation-free
+layout.  Two contexts on two streams at once must not share any scratch memory.  Every result is compared
 with the oracle: bit-exact for the handle and rows, within one bf16 ulp for
 the combine.
 """
@@ -195,3 +196,101 @@ def test_release_inside_capture_is_deferred(oracle):
         # the next call outside a capture performs the queued releases
         buf.get_dispatch_layout(idx_s, E)
         assert not bm._deferred
+
+
+def test_layout_then_dispatch_hip_graph_replays(oracle):
+    """The normal-mode call order captured once: get_dispatch_layout, the first
+    dispatch given its outputs (the handle borrows the layout's partials, so
+    the captured pack reads what the captured layout writes), the combine;
+    replayed on new routing and rows, with eager layouts of the same ctx
+    between replays."""
+    dev = device()
+    T, H = 1000, 2048
+    cap = T * min(K, R)
+    buf = make_buffer(E, R, C, T)
+    first = _inputs(12, T, H)
+    x_s, idx_s, w_s = first.x.to(dev), first.topk_idx.to(dev), first.topk_weights.to(dev)
+
+    def step():
+        ntr, _, nte, itr, _ = buf.get_dispatch_layout(idx_s, E, no_sync=True)
+        recv, rti, rtw, _, h, _ = buf.dispatch(
+            x_s, topk_idx=idx_s, topk_weights=w_s, num_tokens_per_rank=ntr, is_token_in_rank=itr,
+            num_tokens_per_expert=nte, num_worst_tokens=cap, no_sync=True)
+        out, _, _ = buf.combine(recv, h, gate_weights=w_s, no_sync=True)
+        return recv, rti, rtw, h, out
+
+    step()  # warm the allocator and the library outside the capture
+    torch.cuda.synchronize()
+    scans = buf.stats()["scan_launches"]
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            recv, rti, rtw, h, out = step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert buf.stats()["scan_launches"] == scans  # the captured dispatch borrowed
+    for rep in range(3):
+        inp = _inputs(300 + rep, T, H)
+        x_s.copy_(inp.x.to(dev))
+        idx_s.copy_(inp.topk_idx.to(dev))
+        w_s.copy_(inp.topk_weights.to(dev))
+        print(f"[graph] layout -> dispatch replay {rep}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        _check(oracle, inp, h, recv, rti, rtw, out)
+        # an eager layout of the same ctx between replays (it rewrites the
+        # scratch the captured pack reads; the next replay's layout rewrites it again)
+        other = _inputs(400 + rep, T, H)
+        ntr2, _, nte2, itr2, _ = buf.get_dispatch_layout(other.topk_idx.to(dev), E)
+        ref2 = oracle.layout(other.topk_idx.numpy(), E, R)
+        assert_equal("eager layout", np_(itr2), ref2.is_token_in_rank)
+
+
+def test_static_layout_hip_graph_replays(oracle):
+    """The allocation-free get_dispatch_layout captured in a graph (what it is
+    for) and replayed on new routing, with eager calls between replays."""
+    import ctypes
+
+    from combine_get_dispatch_layout_amd import _capi as Cc
+
+    dev = device()
+    T = 3001
+    ntr = torch.empty(R, dtype=torch.int32, device=dev)
+    nte = torch.empty(E, dtype=torch.int32, device=dev)
+    itr = torch.empty(T, R, dtype=torch.uint8, device=dev)
+    idx_s = torch.from_numpy(wl.random_routing(np.random.default_rng(5), T, E, K)).to(dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def call(idx, a, b, c, stream):
+        Cc.check(Cc.moedx_get_dispatch_layout_static(P(idx), T, K, E, R, P(a), P(b), P(c),
+                                                     ctypes.c_void_p(stream.cuda_stream)))
+
+    call(idx_s, ntr, nte, itr, torch.cuda.current_stream())  # first call on the device: eager
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            call(idx_s, ntr, nte, itr, s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        idx = wl.random_routing(np.random.default_rng(60 + rep), T, E, K, p_empty=0.05)
+        idx_s.copy_(torch.from_numpy(idx).to(dev))
+        print(f"[graph] static layout replay {rep}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.layout(idx, E, R)
+        assert_equal("num_tokens_per_rank", np_(ntr), ref.num_tokens_per_rank)
+        assert_equal("num_tokens_per_expert", np_(nte), ref.num_tokens_per_expert)
+        assert_equal("is_token_in_rank", np_(itr), ref.is_token_in_rank)
+        # an eager call between replays shares the static counters
+        e_ntr = torch.empty_like(ntr)
+        e_nte = torch.empty_like(nte)
+        e_itr = torch.empty_like(itr)
+        call(idx_s, e_ntr, e_nte, e_itr, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert_equal("eager experts", np_(e_nte), ref.num_tokens_per_expert)
