@@ -46,6 +46,10 @@ HBM_PEAK_GBS = 8000.0
 INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (memory-side) cache
 
 
+# Seconds of back-to-back launches before each row of measure_rows is timed.
+ROW_SETTLE_S = 0.05
+
+
 def input_copies(nbytes):
     """Copies of an op's input to rotate over so that at least twice the
     Infinity Cache is read between two reads of one copy: every launch then
@@ -354,7 +358,14 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
         return ms.value / n
 
     def timed(fns):
-        rot_ms(fns, max(warmup, 1))
+        # Warm-up: at least `warmup` launches and ROW_SETTLE_S of back-to-back
+        # work, so that each row is timed after the clocks have settled from the
+        # host-only work (oracle timing, input set-up) before it.
+        t0 = time.perf_counter()
+        n = 0
+        while n < max(warmup, 1) or time.perf_counter() - t0 < ROW_SETTLE_S:
+            rot_ms(fns, max(warmup, 1))
+            n += max(warmup, 1)
         return rot_ms(fns, steps)
 
     # The exec the single-kernel row closures launch with: exr, or one whose

@@ -66,12 +66,22 @@ __device__ __forceinline__ void row_part(const RowSplit& rs, int* t, int* part) 
 }
 
 // Where a launch goes and, optionally, events stamped with the kernel's own
-// start and end (hipExtLaunchKernel), for kernel-accurate timing.
+// start and end (hipExtLaunchKernel), for kernel-accurate timing.  lds_bytes:
+// dynamic LDS per workgroup (0 unless a launcher caps its occupancy).
 struct Launch {
     hipStream_t stream;
     hipEvent_t start;
     hipEvent_t stop;
+    unsigned int lds_bytes;
 };
+
+// Dynamic LDS (bytes) that, beside `static_lds` bytes of static LDS, lets at
+// most `workgroups_per_cu` workgroups of a kernel share one CU (gfx950: 160 KB
+// of LDS per CU, allocated in 512-byte granules).  A row kernel that reads a
+// part of a row and writes it out runs faster on some shapes with fewer waves
+// in flight per CU; its launcher reserves this much LDS, which the kernel does
+// not touch.
+unsigned int occupancy_lds(int workgroups_per_cu, unsigned int static_lds);
 
 template <typename Tup, size_t... I>
 inline void fill_args(void** argv, Tup& tup, std::index_sequence<I...>) {
@@ -85,8 +95,8 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
     std::tuple<KArgs...> tup(static_cast<KArgs>(args)...);
     void* argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
     fill_args(argv, tup, std::index_sequence_for<KArgs...>{});
-    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0,
-                              L.stream, L.start, L.stop, 0);
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv,
+                              L.lds_bytes, L.stream, L.start, L.stop, 0);
 }
 
 // ---- layout ------------------------------------------------------------------

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fp8_codec.h"
 #include "launch.h"
 #include "layout_core.h"
@@ -531,7 +533,30 @@ int pack_split(int units, int units_per_wave) {
 
 int pack_blocks(int T, int split) { return (int)row_blocks(T, split); }
 
+// Workgroups (of 4 waves) per CU that the row-copy kernels below run with,
+// measured with every input read from HBM (kernel time per launch; 8 is what
+// their registers allow, so 8 means no cap):
+//   bf16 cached pack: 7 against 8 -- 48.1-48.4 against 50.1-50.3 us on
+//   4096 x 7168 (8 buckets), 139.0-140.3 against 144.5-146.7 us on 16384 x 4096
+//   (16 buckets), 73.4-74.4 against 72.6-72.9 us on the 8192 x 7168 Zipf
+//   routing; 6 or fewer were slower on all three.
+//   FP8 pack: 4 against 8 -- 49.7-50.0 against 52.0-52.9 us (8192 x 7168 Zipf),
+//   31.9-32.0 against 34.0-34.4 us (4096 x 7168), 82.8 against 90.1-90.4 us
+//   (16384 x 4096); 3 were slower (72-73 us at 8192 x 7168).
+//   The first bf16 pack, whose row lookup is a longer chain of loads, and the
+//   combine were slower under every cap and run uncapped.
+constexpr int kCachedPackWorkgroupsPerCu = 7;
+constexpr int kFp8PackWorkgroupsPerCu = 4;
+
 }  // namespace
+
+unsigned int occupancy_lds(int workgroups_per_cu, unsigned int static_lds) {
+    constexpr unsigned int kLdsPerCu = 160u * 1024u, kMaxPerWorkgroup = 64u * 1024u;
+    if (workgroups_per_cu < 1) return 0;
+    const unsigned int per_wg =
+        std::min((kLdsPerCu / (unsigned int)workgroups_per_cu) & ~511u, kMaxPerWorkgroup);
+    return per_wg > static_lds ? per_wg - static_lds : 0u;
+}
 
 hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
                             void* recv_x, const int64_t* topk_idx, const float* topk_weights,
@@ -543,8 +568,10 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
     const dim3 grid(pack_blocks(T, split)), block(kRowThreads);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x4* rx = static_cast<u32x4*>(recv_x);
-#define MOEDX_PACK(N)                                                                  \
-    return launch_kernel(pack_bf16_kernel<N>, grid, block, L, xs, T, H8, rs, rm, hr, rx, \
+    Launch Lc = L;
+    Lc.lds_bytes = occupancy_lds(kCachedPackWorkgroupsPerCu, 0);
+#define MOEDX_PACK(N)                                                                   \
+    return launch_kernel(pack_bf16_kernel<N>, grid, block, Lc, xs, T, H8, rs, rm, hr, rx, \
                          topk_idx, topk_weights, K, E, P, bucket, recv_topk_idx,         \
                          recv_topk_weights)
     switch (pick_cpl(rs.per)) {
@@ -610,10 +637,12 @@ hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const 
     u32x2* rx = static_cast<u32x2*>(recv_x8);
     const float trs = mode == kTensor ? 1.0f / tensor_scale : 0.0f;
     const bool two = pick_cpl(rs.per * 16) > 1;  // at most 16 * kWaveBlocks chunks
-#define MOEDX_PACK8(M)                                                                       \
-    return two ? launch_kernel(pack_fp8_kernel<2, M>, grid, block, L, xs, T, H8, rs, rm, hr, \
-                               rx, recv_scales, tensor_scale, trs)                           \
-               : launch_kernel(pack_fp8_kernel<1, M>, grid, block, L, xs, T, H8, rs, rm, hr, \
+    Launch Lc = L;
+    Lc.lds_bytes = occupancy_lds(kFp8PackWorkgroupsPerCu, 0);
+#define MOEDX_PACK8(M)                                                                        \
+    return two ? launch_kernel(pack_fp8_kernel<2, M>, grid, block, Lc, xs, T, H8, rs, rm, hr, \
+                               rx, recv_scales, tensor_scale, trs)                            \
+               : launch_kernel(pack_fp8_kernel<1, M>, grid, block, Lc, xs, T, H8, rs, rm, hr, \
                                rx, recv_scales, tensor_scale, trs)
     switch (mode) {
         case kAmax: MOEDX_PACK8(kAmax);
