@@ -53,7 +53,11 @@ def test_ll_decode_config(oracle):
     run_ll(oracle, inp.x, inp.topk_idx.numpy(), inp.topk_weights, w.experts, w.ranks, w.ll_capacity)
 
 
-@pytest.mark.parametrize("T,cap,p_empty", [(1, 4, 0.0), (64, 64, 0.0), (100, 256, 0.3), (37, 40, 0.0)])
+# Up to 4096 tokens: each token's slot counts every earlier entry (24 counting
+# passes of 1024 entries at 4096 x 6), so the larger batches check the
+# multi-pass count and the slot order far past the decode sizes.
+@pytest.mark.parametrize("T,cap,p_empty", [(1, 4, 0.0), (64, 64, 0.0), (100, 256, 0.3), (37, 40, 0.0),
+                                           (256, 256, 0.0), (1000, 1024, 0.1), (4096, 4096, 0.0)])
 def test_ll_shapes(oracle, T, cap, p_empty):
     E, K, H = 32, 6, 512
     idx = wl.random_routing(np.random.default_rng(T), T, E, K, p_empty)
