@@ -539,10 +539,14 @@ int pack_blocks(int T, int split) { return (int)row_blocks(T, split); }
 //   bf16 cached pack: 7 against 8 -- 48.1-48.4 against 50.1-50.3 us on
 //   4096 x 7168 (8 buckets), 139.0-140.3 against 144.5-146.7 us on 16384 x 4096
 //   (16 buckets), 73.4-74.4 against 72.6-72.9 us on the 8192 x 7168 Zipf
-//   routing; 6 or fewer were slower on all three.
+//   routing; 6 or fewer were slower on all three.  A first dispatch through the
+//   same kernel (handle rows and recv_topk_* too) was slower capped (layout +
+//   pack at 16384 x 4096: 177.5-178.0 against 168.5-169.3 us) and runs
+//   uncapped.
 //   FP8 pack: 4 against 8 -- 49.7-50.0 against 52.0-52.9 us (8192 x 7168 Zipf),
 //   31.9-32.0 against 34.0-34.4 us (4096 x 7168), 82.8 against 90.1-90.4 us
-//   (16384 x 4096); 3 were slower (72-73 us at 8192 x 7168).
+//   (16384 x 4096); 3 were slower (72-73 us at 8192 x 7168); a first FP8
+//   dispatch (layout + pack at 8192 x 7168) 59.2-61.9 against 60.0-61.2 us.
 //   The first bf16 pack, whose row lookup is a longer chain of loads, and the
 //   combine were slower under every cap and run uncapped.
 constexpr int kCachedPackWorkgroupsPerCu = 7;
@@ -568,8 +572,9 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
     const dim3 grid(pack_blocks(T, split)), block(kRowThreads);
     const u32x4* xs = static_cast<const u32x4*>(x);
     u32x4* rx = static_cast<u32x4*>(recv_x);
+    const bool cached = hr.send_head == nullptr && recv_topk_idx == nullptr;
     Launch Lc = L;
-    Lc.lds_bytes = occupancy_lds(kCachedPackWorkgroupsPerCu, 0);
+    Lc.lds_bytes = cached ? occupancy_lds(kCachedPackWorkgroupsPerCu, 0) : 0u;
 #define MOEDX_PACK(N)                                                                   \
     return launch_kernel(pack_bf16_kernel<N>, grid, block, Lc, xs, T, H8, rs, rm, hr, rx, \
                          topk_idx, topk_weights, K, E, P, bucket, recv_topk_idx,         \
