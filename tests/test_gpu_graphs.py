@@ -4,8 +4,8 @@ A capacity-mode first dispatch (layout with every prefix, pack with the
 handle rows and recv_topk_*, gate-weighted combine) needs no host
 synchronisation and records no memset, so it can be captured once and
 replayed with new routing and new rows each time; so can get_dispatch_layout
-followed by a dispatch that borrows its partials, and the allocation-free
-layout.  Two contexts on two streams at once must not share any scratch memory.  Every result is compared
+followed by a dispatch that borrows its partials, the allocation-free layout,
+and a first and a cached FP8 dispatch.  Two contexts on two streams at once must not share any scratch memory.  Every result is compared
 with the oracle: bit-exact for the handle and rows, within one bf16 ulp for
 the combine.
 """
@@ -294,3 +294,47 @@ def test_static_layout_hip_graph_replays(oracle):
         call(idx_s, e_ntr, e_nte, e_itr, torch.cuda.current_stream())
         torch.cuda.synchronize()
         assert_equal("eager experts", np_(e_nte), ref.num_tokens_per_expert)
+
+
+def test_fp8_dispatch_hip_graph_replays(oracle):
+    """A capacity-mode FP8 first dispatch (the layout with every prefix, then
+    the FP8 pack, which runs with LDS reserved to cap its occupancy) and a
+    cached FP8 dispatch of another batch of rows through the same handle,
+    captured once and replayed on new routing and rows."""
+    dev = device()
+    T, H = 1000, 1024  # 8 blocks of 1x128 per row
+    cap = T * min(K, R)
+    buf = make_buffer(E, R, C, T)
+    first = _inputs(31, T, H)
+    x_s, idx_s = first.x.to(dev), first.topk_idx.to(dev)
+    x2_s = first.x.to(dev)
+    buf.dispatch(x_s, topk_idx=idx_s, fp8=True, num_worst_tokens=cap, no_sync=True)  # warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            (codes, scales), _, _, _, h, _ = buf.dispatch(x_s, topk_idx=idx_s, fp8=True,
+                                                          num_worst_tokens=cap, no_sync=True)
+            (codes2, scales2), _, _, _, _, _ = buf.dispatch(x2_s, handle=h, fp8=True, no_sync=True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        inp = _inputs(500 + rep, T, H)
+        g = torch.Generator().manual_seed(600 + rep)
+        x2 = (torch.randn(T, H, generator=g) * 3).to(torch.bfloat16)
+        x_s.copy_(inp.x.to(dev))
+        idx_s.copy_(inp.topk_idx.to(dev))
+        x2_s.copy_(x2.to(dev))
+        print(f"[graph] FP8 dispatch replay {rep}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle_first_dispatch(oracle, inp, E, R, C, with_rows=False)
+        N = ref.prefix.num_recv
+        check_handle(h, ref, N)
+        for name, (c_, s_), xb in (("first", (codes, scales), bf16_bits(inp.x)),
+                                   ("cached", (codes2, scales2), bf16_bits(x2))):
+            cref, sref = oracle.pack_fp8(xb, ref.prefix)
+            assert_equal(f"{name} codes", np_(c_)[:N], cref)
+            assert_equal(f"{name} scales", np_(s_)[:N].view(np.uint32), sref.view(np.uint32))
