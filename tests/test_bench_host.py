@@ -42,8 +42,9 @@ def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch)
 
 
 def test_all_cores_oracle_leg_equals_the_single_thread_step():
-    """The CPU baseline's all-cores leg only splits the driver over token
-    ranges: its receive rows and combined rows equal the one-thread oracle's."""
+    """The CPU baseline's all-cores leg only splits the oracle's calls over
+    token ranges: its receive rows and combined rows equal the one-thread
+    oracle's."""
     import concurrent.futures as cf
 
     import numpy as np
