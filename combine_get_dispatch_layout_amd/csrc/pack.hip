@@ -534,8 +534,8 @@ int pack_split(int units, int units_per_wave) {
 int pack_blocks(int T, int split) { return (int)row_blocks(T, split); }
 
 // Workgroups (of 4 waves) per CU that the row-copy kernels below run with,
-// measured with every input read from HBM (kernel time per launch; 8 is what
-// their registers allow, so 8 means no cap):
+// measured with every input read from HBM (time per launch over back-to-back
+// launches; 8 is what their registers allow, so 8 means no cap):
 //   bf16 cached pack: 7 against 8 -- 48.1-48.4 against 50.1-50.3 us on
 //   4096 x 7168 (8 buckets), 139.0-140.3 against 144.5-146.7 us on 16384 x 4096
 //   (16 buckets), 73.4-74.4 against 72.6-72.9 us on the 8192 x 7168 Zipf
