@@ -26,3 +26,26 @@ def bf16_ulp_distance(a_u16: np.ndarray, b_u16: np.ndarray) -> np.ndarray:
         mag = u & 0x7FFF
         return np.where(u & 0x8000, -mag, mag)
     return np.abs(ordered(a_u16) - ordered(b_u16))
+
+
+def load_golden(name: str) -> dict:
+    """A text fixture under tests/golden/: "key: values" lines, '#' comments,
+    matrix rows separated by '|'.  Integers stay integers; any value with a
+    '.' makes its array float."""
+    import os
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    out = {}
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, val = (s.strip() for s in line.split(":", 1))
+            rows = [r.split() for r in val.split("|")]
+            is_float = any("." in v for r in rows for v in r)
+            arr = np.array([[float(v) if is_float else int(v) for v in r] for r in rows])
+            out[key] = arr[0] if len(rows) == 1 else arr
+            if arr.size == 1 and len(rows) == 1:
+                out[key] = arr.reshape(-1)[0].item()
+    return out
