@@ -34,6 +34,7 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-ffp-contract=off",
     "-Wall",
+    "-Wextra",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

@@ -191,7 +191,7 @@ struct Exec {
     bool async = false;
     hipEvent_t start = nullptr;  // stamped at the op's kernel start
     hipEvent_t stop = nullptr;   // stamped at the op's kernel end
-    Launch launch() const { return Launch{run, start, stop}; }
+    Launch launch() const { return Launch{run, start, stop, 0u}; }
     // An op that launches no kernel still completes its timing events.
     hipError_t no_kernel() const {
         hipError_t e = hipSuccess;
@@ -307,7 +307,7 @@ static LayoutArgs handle_layout_args(const moedx_ctx* ctx, const moedx_handle* h
 static int finish_pending(moedx_ctx* ctx, const moedx_handle* h, hipStream_t run) {
     if (!h->prefixes_pending) return MOEDX_OK;
     HIP_OR_FAIL(launch_layout_finish(handle_layout_args(ctx, h, nullptr, false),
-                                     Launch{run, nullptr, nullptr}));
+                                     Launch{run, nullptr, nullptr, 0u}));
     (h->experts_given ? ctx->stats.scan_launches : ctx->stats.layout_launches) += 1;
     h->prefixes_pending = false;
     return MOEDX_OK;
@@ -362,7 +362,7 @@ static int settle_borrow(moedx_handle* h, hipStream_t run, bool elsewhere) {
     a.E = h->E;
     a.n_group_cnt = num_groups(h->T) * h->R;
     a.n_chan_part = (h->C + 1) * h->R;
-    HIP_OR_FAIL(launch_adopt(a, Launch{run, nullptr, nullptr}));
+    HIP_OR_FAIL(launch_adopt(a, Launch{run, nullptr, nullptr, 0u}));
     c->stats.scan_launches += 1;
     if (elsewhere) {
         if (!h->adopted) HIP_OR_FAIL(hipEventCreateWithFlags(&h->adopted, hipEventDisableTiming));
@@ -639,7 +639,7 @@ int moedx_get_dispatch_layout_static(const int64_t* topk_idx, int T, int K, int 
     int dev = 0;
     HIP_OR_FAIL(hipGetDevice(&dev));
     if (dev < 0 || dev >= kMaxDevices) return fail(MOEDX_EINVAL, "device %d >= %d", dev, kMaxDevices);
-    const Launch L{stream, nullptr, nullptr};
+    const Launch L{stream, nullptr, nullptr, 0u};
     unsigned char* base = nullptr;
     {
         std::lock_guard<std::mutex> lock(g_static_mu);

@@ -208,8 +208,8 @@ __global__ __launch_bounds__(kThreads) void ll_recv_kernel(
 // sums the token's slot rows in k order (fp32 fused multiply-adds from +0.0).
 __global__ __launch_bounds__(kThreads) void ll_combine_kernel(
     const u32x4* __restrict__ y, const int64_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_weights, const int32_t* __restrict__ slot_of, int T, int K,
-    int H8, int E, int cap, int slices, u32x4* __restrict__ out) {
+    const float* __restrict__ topk_weights, const int32_t* __restrict__ slot_of, int K, int H8,
+    int E, int cap, int slices, u32x4* __restrict__ out) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x / slices;
     const int slice = blockIdx.x - t * slices;
@@ -310,8 +310,8 @@ hipError_t launch_ll_combine(const void* y, const int64_t* topk_idx, const float
     const int H8 = H / 8;
     const int slices = ll_slices(T, H8, MOEDX_LL_COMBINE_TARGET_WG);
     return launch_kernel(ll_combine_kernel, dim3(T * slices), dim3(kThreads), L,
-                         static_cast<const u32x4*>(y), topk_idx, topk_weights, slot_of, T, K, H8,
-                         E, cap, slices, static_cast<u32x4*>(out));
+                         static_cast<const u32x4*>(y), topk_idx, topk_weights, slot_of, K, H8, E,
+                         cap, slices, static_cast<u32x4*>(out));
 }
 
 }  // namespace moedx
