@@ -88,7 +88,7 @@ TRAFFIC_SOURCES = {"layout": "layout.hip", "get_layout": "layout.hip", "pack": "
                    "ll_dispatch": "ll.hip", "ll_combine": "ll.hip", "launch_floor": "ll.hip",
                    "pack_ltd": "pack.hip"}
 # headers every kernel source includes: a change there changes the kernels too
-SHARED_HEADERS = ("launch.h", "rows.h", "fastdiv.h", "layout_core.h", "fp8_codec.h")
+SHARED_HEADERS = ("launch.h", "rows.h", "fastdiv.h", "layout_core.h", "fp8_codec.h", "xcd.h")
 
 
 def source_digest(src):
