@@ -830,6 +830,29 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
             C.moedx_handle_destroy(s["h"])
     del llsets, buf
     torch.cuda.synchronize()
+
+    # Two workloads' whole timed regions, as the sums of rows above (each part
+    # timed on its own rotation, as the headline step's dispatch and combine
+    # are): the skewed FP8 workload's step (layout + scan + FP8 pack on a fresh
+    # handle, then the bf16 combine) and the reuse workload's first call
+    # (exact-mode first dispatch, then the combine), beside reuse_rep.
+    def composite(name, parts, note):
+        if not all(p in rows for p in parts):
+            return
+        us = sum(rows[p]["us"] for p in parts)
+        nbytes = sum(rows[p]["bytes"] for p in parts)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        rows[name] = {"workload": rows[parts[0]]["workload"], "us": round(us, 2),
+                      "bytes": int(nbytes), "GBps": round(gbs, 1),
+                      "roofline_frac": round(gbs / HBM_PEAK_GBS, 4), "parts": list(parts),
+                      "note": note}
+
+    composite("step_fp8_skewed", ("first_dispatch_fp8", "combine_fp8_skewed"),
+              "sum of the two rows: the FP8 workload's timed region (first FP8 dispatch, then "
+              "the bf16 combine of rows shaped like the receive buffer)")
+    composite("first_call_reuse", ("first_dispatch_exact", "combine_reuse"),
+              "sum of the two rows: the reuse workload's first call (exact mode: layout, host "
+              "wait, pack; then the combine); reuse_rep is one repetition after it")
     return rows
 
 
