@@ -28,9 +28,11 @@ __host__ __device__ inline int num_groups(int T) { return (T + kGroup - 1) / kGr
 
 // ---- work order of the row kernels ------------------------------------------
 // The pack and combine kernels run one wave per (token, slice of its row), 4
-// waves per workgroup; wave index = token * waves_per_token + slice, in
-// workgroup order.  (Keeping each 64-token group on one XCD was measured
-// slower: it spreads the rows in flight over more of HBM.)
+// waves per workgroup; wave index = token * waves_per_token + slice.  The
+// packs take it in workgroup order; the combine takes its workgroups in short
+// runs per XCD (xcd.h).  Long runs (a 64-token group, or a contiguous range,
+// per XCD) were measured slower for both: they spread the rows in flight over
+// more of HBM.
 #ifndef MOEDX_ROW_WAVES_PER_BLOCK
 #define MOEDX_ROW_WAVES_PER_BLOCK 4
 #endif
