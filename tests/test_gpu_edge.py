@@ -88,6 +88,16 @@ def test_ragged_tiles(oracle, T):
     run_case(oracle, _rand(T, 64, 6, seed=T), 128, 64, 16, 7)
 
 
+# The combine takes its workgroups in runs of 16 per XCD, in spans of 128
+# workgroups (a last partial span keeps the plain order): grids just below, at
+# and past one and two spans, and spans whose last workgroup holds waves past
+# the last token (H = 512: one wave per token; H = 7168: 14).
+@pytest.mark.parametrize("T,H", [(508, 512), (512, 512), (516, 512), (1024, 512), (1030, 512),
+                                 (36, 7168), (37, 7168), (73, 7168)])
+def test_combine_workgroup_order_spans(oracle, T, H):
+    run_case(oracle, _rand(T, 64, 6, seed=T + H), H, 64, 8, 4, capacity=True)
+
+
 def test_more_channels_than_tokens(oracle):
     run_case(oracle, _rand(5, 16, 2, seed=3), 64, 16, 4, 24)
 
