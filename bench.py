@@ -698,6 +698,41 @@ def measure_rows(steps, warmup, cpu_budget_s, flush, log_fn):
                                {"bound_note": "latency (under 0.3 MB)", "per_launch_us": dist}, cpu)
     del lsets, buf
 
+    # -- the first FP8 dispatch on the prefill routing (a fresh capacity-mode
+    # handle each time: the layout's partials, then the FP8 pack that also
+    # finishes the handle)
+    log_fn(f"[bench] row first_dispatch_fp8_prefill: {w.name}")
+    inp, buf, idx, sets, N = normal_sets(w, True, [None] * input_copies(2 * T * H))
+    capp = T * min(K, R)
+    nbp = ctypes.c_size_t()
+    C.check(C.moedx_handle_workspace_bytes(buf.ctx, T, K, capp, ctypes.byref(nbp)))
+    for s in sets:
+        s["ws_first"] = torch.empty(nbp.value, dtype=torch.uint8, device=dev)
+
+    def first_fp8_prefill(s):
+        def f():
+            h = ctypes.c_void_p()
+            C.check(C.moedx_dispatch_prepare(buf.ctx, P(idx), T, K, None, None, None,
+                                             P(s["ws_first"]), nbp.value, capp, ctypes.byref(h),
+                                             exr))
+            C.check(C.moedx_dispatch(buf.ctx, h, P(s["x"]), T, H, C.MOEDX_QUANT_FP8_E4M3_1X128,
+                                     None, None, P(s["recv"]), P(s["scales"]), None, None, exr))
+            C.moedx_handle_destroy(h)
+        return f
+
+    ms = timed([first_fp8_prefill(s) for s in sets])
+    layp = 8 * T * K + T * R + 4 * (2 * R + E + 2 * R * w.channels)
+    rows["first_dispatch_fp8_prefill"] = entry(
+        w, "first_dispatch_fp8_prefill", ms,
+        layp + row_bytes("pack_fp8", T, H, K, E, N=N) + 4 * T * R + 4 * N,
+        {"recv_rows": N, "dtype": "bf16->e4m3",
+         "note": "prepare (the layout's partials) + the FP8 pack that also finishes the handle "
+                 "(prefixes, send_head, recv_src_idx) in the same launch, on a fresh "
+                 "capacity-mode handle"})
+    for s in sets:
+        C.moedx_handle_destroy(s["h"])
+    del sets, buf
+
     # -- the whole step on the tiny workload (launch-bound; its 0.4 MB stay in
     # the caches whatever the rotation)
     w = wl.TINY

@@ -389,6 +389,53 @@ static int handle_ready(const moedx_handle* hc, hipStream_t run) {
     return MOEDX_OK;
 }
 
+// A first pack that also finishes a partials-only capacity-mode handle
+// (launch_pack_bf16_first, launch_pack_fp8_first).  For a handle that borrowed
+// a layout's partials, the pack reads them from that ctx's scratch and writes
+// the handle's per-token arrays (ht); any other handle is made ready first.
+struct FirstPack {
+    LayoutArgs la;
+    HandleTokens ht;
+    moedx_ctx* borrowed_from;
+};
+
+static int first_pack_begin(moedx_ctx* ctx, const moedx_handle* h, const int64_t* topk_idx,
+                            hipStream_t run, FirstPack* fp) {
+    fp->la = handle_layout_args(ctx, h, topk_idx, false);
+    fp->ht = HandleTokens{};
+    fp->borrowed_from = h->borrow_ctx;
+    moedx_ctx* bc = fp->borrowed_from;
+    if (bc) {
+        fp->la.group_cnt = bc->lay_group_cnt;
+        fp->la.chan_part = bc->lay_chan_part;
+        fp->la.token_mask = bc->lay_mask;
+        fp->la.tile_expert = nullptr;
+        fp->la.experts_in = bc->lay_experts;
+        fp->ht = HandleTokens{h->token_mask, h->is_token_in_rank, h->slot_bucket,
+                              bc->lay_slot_bucket};
+        return MOEDX_OK;
+    }
+    return handle_ready(h, run);  // also refuses an orphaned borrower
+}
+
+// After the first pack is enqueued on `run`: the handle is finished and, for a
+// borrower, the ctx's next layout waits for this pack when it ran on another
+// stream than that layout (on one stream, the stream orders them).
+static int first_pack_end(const moedx_handle* h, const FirstPack& fp, hipStream_t run) {
+    h->prefixes_pending = false;
+    h->rows_written = true;
+    moedx_ctx* bc = fp.borrowed_from;
+    if (bc) {
+        if (run != bc->last.stream) {
+            HIP_OR_FAIL(hipEventRecord(bc->borrow_done, run));
+            bc->borrow_armed = true;
+        }
+        bc->pending = nullptr;
+        h->borrow_ctx = nullptr;
+    }
+    return MOEDX_OK;
+}
+
 extern "C" {
 
 const char* moedx_last_error(void) { return g_err; }
@@ -736,10 +783,10 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
     Exec ex;
     int rc = exec_begin(ctx, exec, &ex);
     hipError_t e = hipSuccess;
-    // Capacity mode, where a first bf16 dispatch can finish the prefixes in
-    // its own launch: the partials only, and the first dispatch (or combine)
-    // on the handle finishes them.  Elsewhere the layout kernel writes every
-    // prefix itself.
+    // Capacity mode, where a first dispatch (bf16, or quantising FP8) can
+    // finish the prefixes in its own launch: the partials only, and the first
+    // dispatch (or combine) on the handle finishes them.  Elsewhere the layout
+    // kernel writes every prefix itself.
     const bool partials = capacity_rows > 0 && T > 0 && pack_first_fits(T, h->R, h->E, h->C);
     // Given exactly the outputs of this ctx's last get_dispatch_layout, the
     // handle borrows the partials that call left in the ctx's scratch: nothing
@@ -911,38 +958,22 @@ int moedx_dispatch(moedx_ctx* ctx, const moedx_handle* h, const void* x, int T, 
     // The first dispatch on a handle also writes send_head and recv_src_idx.
     const HandleRows hr = h->rows_written ? HandleRows{nullptr, nullptr}
                                           : HandleRows{h->send_head, h->recv_src_idx};
-    if (T > 0 && quant == MOEDX_QUANT_NONE && h->prefixes_pending &&
-        pack_first_fits(T, h->R, h->E, h->C)) {
+    if (T > 0 && h->prefixes_pending && pack_first_fits(T, h->R, h->E, h->C)) {
         // One launch finishes the handle and packs the rows.
-        LayoutArgs la = handle_layout_args(ctx, h, topk_idx, false);
-        HandleTokens ht{};
-        moedx_ctx* bc = h->borrow_ctx;
-        if (bc) {  // partials borrowed from a layout: read from its ctx's scratch
-            la.group_cnt = bc->lay_group_cnt;
-            la.chan_part = bc->lay_chan_part;
-            la.token_mask = bc->lay_mask;
-            la.tile_expert = nullptr;
-            la.experts_in = bc->lay_experts;
-            ht = HandleTokens{h->token_mask, h->is_token_in_rank, h->slot_bucket,
-                              bc->lay_slot_bucket};
-        } else if (int rc = handle_ready(h, ex.run)) {  // also refuses an orphaned borrower
-            return rc;
+        FirstPack fp;
+        if (int rc = first_pack_begin(ctx, h, topk_idx, ex.run, &fp)) return rc;
+        if (quant == MOEDX_QUANT_NONE) {
+            HIP_OR_FAIL(launch_pack_bf16_first(fp.la, fp.ht, x, H, h->capacity, hr, recv_x,
+                                               topk_weights, recv_topk_idx, recv_topk_weights,
+                                               ex.launch()));
+            ctx->stats.pack_launches += 1;
+        } else {
+            HIP_OR_FAIL(launch_pack_fp8_first(fp.la, fp.ht, x, H, h->capacity, hr, recv_x,
+                                              recv_scales, MOEDX_FP8_SCALE_AMAX, 0.0f,
+                                              ex.launch()));
+            ctx->stats.pack_fp8_launches += 1;
         }
-        HIP_OR_FAIL(launch_pack_bf16_first(la, ht, x, H, h->capacity, hr, recv_x, topk_weights,
-                                           recv_topk_idx, recv_topk_weights, ex.launch()));
-        ctx->stats.pack_launches += 1;
-        h->prefixes_pending = false;
-        h->rows_written = true;
-        if (bc) {
-            // Read on another stream than the layout's: the ctx's next layout
-            // waits for this pack (on one stream, the stream orders them).
-            if (ex.run != bc->last.stream) {
-                HIP_OR_FAIL(hipEventRecord(bc->borrow_done, ex.run));
-                bc->borrow_armed = true;
-            }
-            bc->pending = nullptr;
-            h->borrow_ctx = nullptr;
-        }
+        if (int rc = first_pack_end(h, fp, ex.run)) return rc;
         return exec_end(ex);
     }
     if (int rc = handle_ready(h, ex.run)) return rc;
@@ -1004,6 +1035,17 @@ int moedx_dispatch_fp8(moedx_ctx* ctx, const moedx_handle* h, const void* x, int
                     h->R, h->T, h->capacity > 0 ? h->capacity : h->n_host};
     const HandleRows hr = h->rows_written ? HandleRows{nullptr, nullptr}
                                           : HandleRows{h->send_head, h->recv_src_idx};
+    if (T > 0 && !fp8->prequantized && h->prefixes_pending &&
+        pack_first_fits(T, h->R, h->E, h->C)) {
+        // One launch finishes the handle and quantises and packs the rows.
+        FirstPack fp;
+        if (int rc = first_pack_begin(ctx, h, nullptr, ex.run, &fp)) return rc;
+        HIP_OR_FAIL(launch_pack_fp8_first(fp.la, fp.ht, x, H, h->capacity, hr, recv_x, recv_scales,
+                                          mode, fp8->tensor_scale, ex.launch()));
+        ctx->stats.pack_fp8_launches += 1;
+        if (int rc = first_pack_end(h, fp, ex.run)) return rc;
+        return exec_end(ex);
+    }
     if (int rc = handle_ready(h, ex.run)) return rc;
     if (int rc = finish_pending(ctx, h, ex.run)) return rc;
     if (T == 0) {

@@ -198,10 +198,10 @@ struct HandleTokens {
     const int8_t* slot_bucket_src;
 };
 
-// First dispatch (bf16) on a handle prepared with launch_layout_partials (or
-// borrowing a layout's partials, ht), in one launch that also finishes the
-// handle's prefixes; for T <= 4096, R a multiple of 4 up to 16 and
-// (C + 1) * R <= 768 (pack_first_fits).  `la` carries every handle array
+// First dispatch (bf16; launch_pack_fp8_first for FP8) on a handle prepared
+// with launch_layout_partials (or borrowing a layout's partials, ht), in one
+// launch that also finishes the handle's prefixes; for T <= 4096, R a multiple
+// of 4 up to 16 and (C + 1) * R <= 768 (pack_first_fits).  `la` carries every handle array
 // (group_cnt, chan_part and token_mask being the partials read).
 bool pack_first_fits(int T, int R, int E, int C);
 hipError_t launch_pack_bf16_first(const LayoutArgs& la, const HandleTokens& ht, const void* x,
@@ -232,6 +232,13 @@ hipError_t launch_pack_bf16(const void* x, int T, int H, const RowMap& rm, const
                             void* recv_x, const int64_t* topk_idx, const float* topk_weights,
                             int K, int E, int P, BucketDiv bucket, int64_t* recv_topk_idx,
                             float* recv_topk_weights, const Launch& L);
+
+// The first FP8 dispatch on the same kind of handle as launch_pack_bf16_first
+// (pack_first_fits), in one launch that also finishes its prefixes; mode and
+// scales as launch_pack_fp8.
+hipError_t launch_pack_fp8_first(const LayoutArgs& la, const HandleTokens& ht, const void* x,
+                                 int H, int64_t rows, const HandleRows& hr, void* recv_x8,
+                                 void* recv_scales, int mode, float tensor_scale, const Launch& L);
 
 // mode: MOEDX_FP8_SCALE_* (AMAX 0, POW2 1, UE8M0 2, TENSOR 3); recv_scales fp32,
 // uint8 (UE8M0) or unused (TENSOR).

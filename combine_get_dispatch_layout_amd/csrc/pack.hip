@@ -229,6 +229,16 @@ __device__ __forceinline__ TokenRows token_rows_from_counts(const GroupCounts<RB
     return TokenRows{row, pos, mine, __ballot(row >= 0)};
 }
 
+// A handle that borrowed a layout's partials gets token t's mask,
+// is_token_in_rank row and slot buckets from its first pack (nothing otherwise).
+__device__ __forceinline__ void write_borrowed_token(const HandleTokens& ht, const TokenRows& d,
+                                                     int t, int R, int K, int lane) {
+    if (ht.token_mask == nullptr) return;
+    if (lane == 0) ht.token_mask[t] = d.mask;
+    if (lane < R) ht.is_token_in_rank[(int64_t)t * R + lane] = (uint8_t)((d.mask >> lane) & 1u);
+    if (lane < K) ht.slot_bucket[(int64_t)t * K + lane] = ht.slot_bucket_src[(int64_t)t * K + lane];
+}
+
 // The workgroup that finishes the handle runs the layout's straight-line
 // finishing step for one chunk of 64 groups and 16 tiles: its LDS holds the
 // group prefixes of up to 64 groups of 16 buckets.
@@ -266,13 +276,7 @@ __global__ __launch_bounds__(kRowThreads) void pack_bf16_first_kernel(
     u32x4 v[CPL];
     load_row_part<CPL>(x + (int64_t)t * H8, c_begin, c_end, lane, v);
     const TokenRows d = token_rows_from_counts<RB>(gcnt, la.R, rows, t, lane);
-    if (part == 0 && ht.token_mask != nullptr) {  // a borrowed layout: the token's handle rows
-        if (lane == 0) ht.token_mask[t] = d.mask;
-        if (lane < la.R)
-            ht.is_token_in_rank[(int64_t)t * la.R + lane] = (uint8_t)((d.mask >> lane) & 1u);
-        if (lane < la.K)
-            ht.slot_bucket[(int64_t)t * la.K + lane] = ht.slot_bucket_src[(int64_t)t * la.K + lane];
-    }
+    if (part == 0) write_borrowed_token(ht, d, t, la.R, la.K, lane);
     pack_bf16_store<CPL>(v, d, t, part, H8, c_begin, c_end, lane, la.R, hr, recv_x, la.topk_idx,
                          topk_weights, la.K, la.E, la.P, la.bucket, recv_topk_idx,
                          recv_topk_weights);
@@ -302,25 +306,18 @@ enum Fp8Mode { kAmax = 0, kPow2 = 1, kUe8m0 = 2, kTensor = 3 };
 // x / s with e4m3_code, the definition the scale and codes follow; the scale
 // s of a block depends on kMode (moedx.h).  tensor_s / tensor_rs: the caller's
 // scale and its correctly rounded reciprocal (kTensor only).
+// One wave's part of token t's FP8 row, chunks [c_begin, c_end) of its bf16
+// row in v (whole 1x128 blocks), quantised and stored to each of the token's
+// rows d, with the handle rows from the first part.
 template <int CPL, int kMode>
-__global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(
-    const u32x4* __restrict__ x, int T, int H8, RowSplit rs, RowMap rm, HandleRows hr,
-    u32x2* __restrict__ recv_x8, void* __restrict__ recv_scales, float tensor_s, float tensor_rs) {
-    const int lane = threadIdx.x & 63;
-    int t, part;
-    row_part(rs, &t, &part);
-    if (t >= T) return;
-    const u32x4* src = x + (int64_t)t * H8;
-    const int G = H8 >> 4;  // blocks per row; parts hold whole blocks (rs counts blocks)
-    const int c_begin = part * rs.per * 16;
-    const int c_end = min(part * rs.per + rs.per, G) * 16;
-    // One pass (CPL * 64 >= 16 * rs.per): the lookup's loads, then the row
-    // loads (chunks past c_end read 0).
-    const RowLoads lk = token_rows_load(rm, t, lane);
-    u32x4 v[CPL];
-    load_row_part<CPL>(src, c_begin, c_end, lane, v);
-    const TokenRows d = token_rows_from(rm, lk, t, lane);
-    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
+__device__ __forceinline__ void pack_fp8_part(const u32x4 (&v)[CPL], const TokenRows& d, int t,
+                                              int part, int H8, int c_begin, int c_end, int lane,
+                                              int R, const HandleRows& hr,
+                                              u32x2* __restrict__ recv_x8,
+                                              void* __restrict__ recv_scales, float tensor_s,
+                                              float tensor_rs) {
+    const int G = H8 >> 4;  // blocks per row
+    if (part == 0) write_handle_rows(hr, d, t, R, lane);
     {
         const int base = c_begin;
         u32x2 code[CPL];
@@ -441,6 +438,61 @@ __global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(
             }
         }
     }
+}
+
+template <int CPL, int kMode>
+__global__ __launch_bounds__(kRowThreads) void pack_fp8_kernel(
+    const u32x4* __restrict__ x, int T, int H8, RowSplit rs, RowMap rm, HandleRows hr,
+    u32x2* __restrict__ recv_x8, void* __restrict__ recv_scales, float tensor_s, float tensor_rs) {
+    const int lane = threadIdx.x & 63;
+    int t, part;
+    row_part(rs, &t, &part);
+    if (t >= T) return;
+    const u32x4* src = x + (int64_t)t * H8;
+    const int G = H8 >> 4;  // blocks per row; parts hold whole blocks (rs counts blocks)
+    const int c_begin = part * rs.per * 16;
+    const int c_end = min(part * rs.per + rs.per, G) * 16;
+    // One pass (CPL * 64 >= 16 * rs.per): the lookup's loads, then the row
+    // loads (chunks past c_end read 0).
+    const RowLoads lk = token_rows_load(rm, t, lane);
+    u32x4 v[CPL];
+    load_row_part<CPL>(src, c_begin, c_end, lane, v);
+    const TokenRows d = token_rows_from(rm, lk, t, lane);
+    pack_fp8_part<CPL, kMode>(v, d, t, part, H8, c_begin, c_end, lane, rm.R, hr, recv_x8,
+                              recv_scales, tensor_s, tensor_rs);
+}
+
+// The first FP8 dispatch on a capacity-mode handle prepared with the layout's
+// partials only (or borrowing them), in one launch: workgroup 0 finishes the
+// handle and every other wave finds its token's rows from the partials, as in
+// pack_bf16_first_kernel, then quantises and stores as pack_fp8_kernel.
+template <int CPL, int kMode, int RB>
+__global__ __launch_bounds__(kRowThreads) void pack_fp8_first_kernel(
+    LayoutArgs la, HandleTokens ht, int ntiles, const u32x4* __restrict__ x, int H8, RowSplit rs,
+    int64_t rows, HandleRows hr, u32x2* __restrict__ recv_x8, void* __restrict__ recv_scales,
+    float tensor_s, float tensor_rs) {
+    __shared__ FirstLds s;
+    if (blockIdx.x == 0) {
+        layout_finish_fast<kFirstChunks, kFirstTiles>(la, ntiles, s, (const TileToken*)nullptr);
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((blockIdx.x - 1) * kRowWavesPerBlock +
+                                                 (threadIdx.x >> 6));
+    const int t = (int)rs.div.div((uint32_t)w);
+    const int part = w - t * rs.split;
+    if (t >= la.T) return;
+    const int G = H8 >> 4;
+    const int c_begin = part * rs.per * 16;
+    const int c_end = min(part * rs.per + rs.per, G) * 16;
+    const GroupCounts<RB> gcnt =
+        load_group_counts<RB>(la.token_mask, la.group_cnt, la.T, la.R, t, lane);
+    u32x4 v[CPL];
+    load_row_part<CPL>(x + (int64_t)t * H8, c_begin, c_end, lane, v);
+    const TokenRows d = token_rows_from_counts<RB>(gcnt, la.R, rows, t, lane);
+    if (part == 0) write_borrowed_token(ht, d, t, la.R, la.K, lane);
+    pack_fp8_part<CPL, kMode>(v, d, t, part, H8, c_begin, c_end, lane, la.R, hr, recv_x8,
+                              recv_scales, tensor_s, tensor_rs);
 }
 
 // Pre-quantised rows: code rows (C16 16-byte chunks) and scale rows (SB bytes)
@@ -656,6 +708,40 @@ hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const 
         default: MOEDX_PACK8(kTensor);
     }
 #undef MOEDX_PACK8
+}
+
+hipError_t launch_pack_fp8_first(const LayoutArgs& la, const HandleTokens& ht, const void* x,
+                                 int H, int64_t rows, const HandleRows& hr, void* recv_x8,
+                                 void* recv_scales, int mode, float tensor_scale, const Launch& L) {
+    const int T = la.T;
+    const int H8 = H / 8;
+    const int split = pack_split(H8 / 16, kWaveBlocks);
+    const RowSplit rs = make_row_split(H8 / 16, split);  // in 1x128 blocks
+    const dim3 grid(1 + pack_blocks(T, split)), block(kRowThreads);
+    const u32x4* xs = static_cast<const u32x4*>(x);
+    u32x2* rx = static_cast<u32x2*>(recv_x8);
+    const float trs = mode == kTensor ? 1.0f / tensor_scale : 0.0f;
+    const int ntiles = num_tiles(T);
+    const bool two = pick_cpl(rs.per * 16) > 1;
+    Launch Lc = L;
+    Lc.lds_bytes = occupancy_lds(kFp8PackWorkgroupsPerCu, (unsigned int)sizeof(FirstLds));
+#define MOEDX_FIRST8(C, M, B)                                                                    \
+    return launch_kernel(pack_fp8_first_kernel<C, M, B>, grid, block, Lc, la, ht, ntiles, xs, H8, \
+                         rs, rows, hr, rx, recv_scales, tensor_scale, trs)
+#define MOEDX_FIRST8_MODE(C, B)              \
+    switch (mode) {                          \
+        case kAmax: MOEDX_FIRST8(C, kAmax, B);   \
+        case kPow2: MOEDX_FIRST8(C, kPow2, B);   \
+        case kUe8m0: MOEDX_FIRST8(C, kUe8m0, B); \
+        default: MOEDX_FIRST8(C, kTensor, B);    \
+    }
+    if (la.R <= 8) {
+        if (two) { MOEDX_FIRST8_MODE(2, 8) } else { MOEDX_FIRST8_MODE(1, 8) }
+    } else {
+        if (two) { MOEDX_FIRST8_MODE(2, 16) } else { MOEDX_FIRST8_MODE(1, 16) }
+    }
+#undef MOEDX_FIRST8_MODE
+#undef MOEDX_FIRST8
 }
 
 hipError_t launch_pack_bytes(const void* codes, const void* scales, int T, int H, int scale_bytes,

@@ -247,11 +247,12 @@ MOEDX_API int moedx_handle_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  * so it is not read.  Alignment: num_tokens_per_expert 4 bytes,
  * is_token_in_rank 4 bytes when R % 4 == 0.  All three NULL: the layout runs.
  * When they are exactly the outputs (same pointers, T and K) of this ctx's
- * last moedx_get_dispatch_layout, in capacity mode where a first bf16
- * dispatch finishes the handle in its own launch (below), not even the scan
- * runs: the handle borrows the partial counts, token masks and slot buckets
- * that get_dispatch_layout left in the ctx's scratch, and its first
- * moedx_dispatch (bf16) builds the handle from them.  Any other first use, a
+ * last moedx_get_dispatch_layout, in capacity mode where a first dispatch
+ * finishes the handle in its own launch (below), not even the scan runs: the
+ * handle borrows the partial counts, token masks and slot buckets that
+ * get_dispatch_layout left in the ctx's scratch, and its first moedx_dispatch
+ * (bf16 or FP8) or quantising moedx_dispatch_fp8 builds the handle from them.
+ * Any other first use, a
  * later prepare that borrows the same layout, or the ctx's next
  * moedx_get_dispatch_layout first copies them into the handle (one small
  * kernel, counted as a scan).  See moedx_create for ordering the next layout
@@ -269,8 +270,9 @@ MOEDX_API int moedx_handle_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  *     multiple of 4 up to 16 only the layout's per-token outputs and partial
  *     counts run here; the prefixes, totals and N (rank and channel prefix
  *     matrices, num_tokens_per_rank/expert, MOEDX_T_NUM_RECV) are written on
- *     the stream of the handle's first moedx_dispatch (by its pack kernel,
- *     for bf16), moedx_dispatch_fp8, moedx_combine or moedx_handle_finish:
+ *     the stream of the handle's first moedx_dispatch or moedx_dispatch_fp8
+ *     (by its pack kernel, in the same launch; for pre-quantised input, by
+ *     one small kernel before it), moedx_combine or moedx_handle_finish:
  *     read them after that call.  In exact mode the call blocks on the host
  *     even when exec->done is given.
  * *out receives a new handle (moedx_handle_destroy frees it). */

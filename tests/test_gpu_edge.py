@@ -235,9 +235,10 @@ def test_layout_finishing_step_limits(oracle, T, E, K, R, C):
     run_case(oracle, _rand(T, E, K, p_empty=0.02, seed=T + R + C), 8, E, R, C, capacity=(T % 2 == 0))
 
 
-# The first capacity-mode dispatch finishes the handle in its own launch when
-# T <= 4096 and R is a multiple of 4 up to 16 (it reads its receive rows from
-# the layout's partials); otherwise the layout writes every prefix at prepare.
+# The first capacity-mode dispatch (bf16 or FP8) finishes the handle in its own
+# launch when T <= 4096 and R is a multiple of 4 up to 16 (it reads its receive
+# rows from the layout's partials); otherwise the layout writes every prefix at
+# prepare.
 # Shapes on both sides: the 64-group limit, ragged groups, R = 4, 8, 12, 16
 # and R not a multiple of 4, and larger batches up to the layout's fast
 # finishing limits.
@@ -254,8 +255,10 @@ def test_layout_finishing_step_limits(oracle, T, E, K, R, C):
     (777, 36, 5, 6, 4),       # R = 6: prefixes at prepare
     (64, 16, 4, 8, 2),        # one group
 ], ids=lambda v: str(v))
-def test_first_capacity_dispatch_one_launch(oracle, T, E, K, R, C):
-    run_case(oracle, _rand(T, E, K, p_empty=0.05, seed=3 * T + R), 16, E, R, C, capacity=True)
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_first_capacity_dispatch_one_launch(oracle, T, E, K, R, C, fp8):
+    run_case(oracle, _rand(T, E, K, p_empty=0.05, seed=3 * T + R), 256 if fp8 else 16, E, R, C,
+             capacity=True, fp8=fp8)
 
 
 # A first dispatch given get_dispatch_layout's outputs (the normal-kernel

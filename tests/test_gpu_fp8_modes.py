@@ -58,6 +58,46 @@ def test_fp8_modes_skewed(oracle, name, tokens):
     _check(oracle, name, x2, ref.prefix, codes2, scales2)
 
 
+@pytest.mark.parametrize("borrow", [False, True], ids=["own_layout", "borrowed_layout"])
+@pytest.mark.parametrize("name", ["amax"] + sorted(MODES))
+def test_first_fp8_capacity_dispatch_one_launch(oracle, name, borrow):
+    """A first FP8 dispatch on a capacity-mode handle of at most 4096 tokens
+    (R a multiple of 4 up to 16) finishes the handle in its own launch, for
+    every scale mode: no finishing or scan kernel runs before the pack, whether
+    the dispatch prepared the handle (the layout's partials only) or the handle
+    borrowed the partials of the get_dispatch_layout just before it."""
+    w = wl.FP8_SKEWED
+    dev = device()
+    inp = wl.make_inputs(w, tokens=1000)
+    T, K, E, R, C = inp.x.shape[0], w.topk, w.experts, w.ranks, w.channels
+    print(f"[fp8 first one launch {name}] borrow={borrow}", flush=True)
+    ref = oracle_first_dispatch(oracle, inp, E, R, C, with_rows=False)
+    buf = make_buffer(E, R, C, T)
+    ti = inp.topk_idx.to(dev)
+    reuse = {}
+    if borrow:
+        ntr, _, nte, itr, _ = buf.get_dispatch_layout(ti, E)
+        reuse = dict(num_tokens_per_rank=ntr, is_token_in_rank=itr, num_tokens_per_expert=nte)
+    before = buf.stats()
+    kw = dict(fp8=True) if name == "amax" else MODES[name]
+    (codes, scales), rti, rtw, _, h, _ = buf.dispatch(inp.x.to(dev), topk_idx=ti,
+                                                       num_worst_tokens=T * min(K, R), **kw, **reuse)
+    torch.cuda.synchronize()
+    st = buf.stats()
+    assert st["layout_launches"] - before["layout_launches"] == (0 if borrow else 1), st
+    assert st["scan_launches"] == before["scan_launches"], st
+    assert st["pack_fp8_launches"] - before["pack_fp8_launches"] == 1, st
+    assert rti is None and rtw is None
+    N = ref.prefix.num_recv
+    check_handle(h, ref, N)
+    if name == "amax":
+        cref, sref = oracle.pack_fp8(bf16_bits(inp.x), ref.prefix)
+        assert_equal("codes", np_(codes)[:N], cref)
+        assert_equal("scales", np_(scales)[:N].view(np.uint32), sref.view(np.uint32))
+    else:
+        _check(oracle, name, inp.x, ref.prefix, codes, scales)
+
+
 def _edge_x(T, H, seed):
     rng = np.random.default_rng(seed)
     x = np.asarray(rng.integers(0, 1 << 16, (T, H)), np.uint16)
