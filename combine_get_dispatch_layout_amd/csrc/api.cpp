@@ -783,7 +783,7 @@ int moedx_dispatch_prepare(moedx_ctx* ctx, const int64_t* topk_idx, int T, int K
     Exec ex;
     int rc = exec_begin(ctx, exec, &ex);
     hipError_t e = hipSuccess;
-    // Capacity mode, where a first dispatch (bf16, or quantising FP8) can
+    // Capacity mode, where a first dispatch (bf16, FP8 or pre-quantised) can
     // finish the prefixes in its own launch: the partials only, and the first
     // dispatch (or combine) on the handle finishes them.  Elsewhere the layout
     // kernel writes every prefix itself.
@@ -1035,13 +1035,18 @@ int moedx_dispatch_fp8(moedx_ctx* ctx, const moedx_handle* h, const void* x, int
                     h->R, h->T, h->capacity > 0 ? h->capacity : h->n_host};
     const HandleRows hr = h->rows_written ? HandleRows{nullptr, nullptr}
                                           : HandleRows{h->send_head, h->recv_src_idx};
-    if (T > 0 && !fp8->prequantized && h->prefixes_pending &&
-        pack_first_fits(T, h->R, h->E, h->C)) {
-        // One launch finishes the handle and quantises and packs the rows.
+    const int sb = tensor ? 0 : (H / 128) * (mode == MOEDX_FP8_SCALE_UE8M0 ? 1 : 4);
+    if (T > 0 && h->prefixes_pending && pack_first_fits(T, h->R, h->E, h->C)) {
+        // One launch finishes the handle and quantises (or copies) and packs the rows.
         FirstPack fp;
         if (int rc = first_pack_begin(ctx, h, nullptr, ex.run, &fp)) return rc;
-        HIP_OR_FAIL(launch_pack_fp8_first(fp.la, fp.ht, x, H, h->capacity, hr, recv_x, recv_scales,
-                                          mode, fp8->tensor_scale, ex.launch()));
+        if (fp8->prequantized) {
+            HIP_OR_FAIL(launch_pack_bytes_first(fp.la, fp.ht, x, fp8->x_scales, H, sb, h->capacity,
+                                                hr, recv_x, recv_scales, ex.launch()));
+        } else {
+            HIP_OR_FAIL(launch_pack_fp8_first(fp.la, fp.ht, x, H, h->capacity, hr, recv_x,
+                                              recv_scales, mode, fp8->tensor_scale, ex.launch()));
+        }
         ctx->stats.pack_fp8_launches += 1;
         if (int rc = first_pack_end(h, fp, ex.run)) return rc;
         return exec_end(ex);
@@ -1051,7 +1056,6 @@ int moedx_dispatch_fp8(moedx_ctx* ctx, const moedx_handle* h, const void* x, int
     if (T == 0) {
         HIP_OR_FAIL(ex.no_kernel());
     } else if (fp8->prequantized) {
-        const int sb = tensor ? 0 : (H / 128) * (mode == MOEDX_FP8_SCALE_UE8M0 ? 1 : 4);
         HIP_OR_FAIL(launch_pack_bytes(x, fp8->x_scales, T, H, sb, rm, hr, recv_x, recv_scales,
                                       ex.launch()));
         ctx->stats.pack_fp8_launches += 1;

@@ -198,7 +198,8 @@ struct HandleTokens {
     const int8_t* slot_bucket_src;
 };
 
-// First dispatch (bf16; launch_pack_fp8_first for FP8) on a handle prepared
+// First dispatch (bf16; launch_pack_fp8_first and launch_pack_bytes_first for
+// FP8 and pre-quantised input) on a handle prepared
 // with launch_layout_partials (or borrowing a layout's partials, ht), in one
 // launch that also finishes the handle's prefixes; for T <= 4096, R a multiple
 // of 4 up to 16 and (C + 1) * R <= 768 (pack_first_fits).  `la` carries every handle array
@@ -245,6 +246,13 @@ hipError_t launch_pack_fp8_first(const LayoutArgs& la, const HandleTokens& ht, c
 hipError_t launch_pack_fp8(const void* x, int T, int H, const RowMap& rm, const HandleRows& hr,
                            void* recv_x8, void* recv_scales, int mode, float tensor_scale,
                            const Launch& L);
+
+// The first pre-quantised dispatch on the same kind of handle as
+// launch_pack_bf16_first, in one launch that also finishes its prefixes.
+hipError_t launch_pack_bytes_first(const LayoutArgs& la, const HandleTokens& ht, const void* codes,
+                                  const void* scales, int H, int scale_bytes, int64_t rows,
+                                  const HandleRows& hr, void* recv_codes, void* recv_scales,
+                                  const Launch& L);
 
 // Pre-quantised rows: codes uint8 [T, H] and scale rows of scale_bytes bytes
 // (scales may be NULL when scale_bytes == 0).

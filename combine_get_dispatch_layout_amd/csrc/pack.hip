@@ -497,25 +497,15 @@ __global__ __launch_bounds__(kRowThreads) void pack_fp8_first_kernel(
 
 // Pre-quantised rows: code rows (C16 16-byte chunks) and scale rows (SB bytes)
 // of token t go unchanged to every receive row of t.  One wave per (token,
-// part of the code row); part 0 also moves the scale row.
+// part of the code row); part 0 also moves the scale row.  pack_bytes_part is
+// what a wave does once it holds its part of the code row (v) and the token's
+// rows (d).
 template <int CPL>
-__global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(
-    const u32x4* __restrict__ codes, const uint8_t* __restrict__ scales, int T, int C16, int SB,
-    RowSplit rs, RowMap rm, HandleRows hr, u32x4* __restrict__ recv,
-    uint8_t* __restrict__ recv_scales, bool words) {
-    const int lane = threadIdx.x & 63;
-    int t, part;
-    row_part(rs, &t, &part);
-    if (t >= T) return;
-    const u32x4* src = codes + (int64_t)t * C16;
-    const int c_begin = part * rs.per;
-    const int c_end = min(c_begin + rs.per, C16);
-    // One pass (CPL * 64 >= rs.per): the lookup's loads, then the row loads.
-    const RowLoads lk = token_rows_load(rm, t, lane);
-    u32x4 v[CPL];
-    load_row_part<CPL>(src, c_begin, c_end, lane, v);
-    const TokenRows d = token_rows_from(rm, lk, t, lane);
-    if (part == 0) write_handle_rows(hr, d, t, rm.R, lane);
+__device__ __forceinline__ void pack_bytes_part(
+    const u32x4 (&v)[CPL], const TokenRows& d, int t, int part, int C16, int c_begin, int c_end,
+    int lane, int R, const HandleRows& hr, const uint8_t* __restrict__ scales, int SB,
+    u32x4* __restrict__ recv, uint8_t* __restrict__ recv_scales, bool words) {
+    if (part == 0) write_handle_rows(hr, d, t, R, lane);
     {
         const int base = c_begin;
         uint64_t m = d.dest;
@@ -560,6 +550,60 @@ __global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(
             }
         }
     }
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kRowThreads) void pack_bytes_kernel(
+    const u32x4* __restrict__ codes, const uint8_t* __restrict__ scales, int T, int C16, int SB,
+    RowSplit rs, RowMap rm, HandleRows hr, u32x4* __restrict__ recv,
+    uint8_t* __restrict__ recv_scales, bool words) {
+    const int lane = threadIdx.x & 63;
+    int t, part;
+    row_part(rs, &t, &part);
+    if (t >= T) return;
+    const u32x4* src = codes + (int64_t)t * C16;
+    const int c_begin = part * rs.per;
+    const int c_end = min(c_begin + rs.per, C16);
+    // One pass (CPL * 64 >= rs.per): the lookup's loads, then the row loads.
+    const RowLoads lk = token_rows_load(rm, t, lane);
+    u32x4 v[CPL];
+    load_row_part<CPL>(src, c_begin, c_end, lane, v);
+    const TokenRows d = token_rows_from(rm, lk, t, lane);
+    pack_bytes_part<CPL>(v, d, t, part, C16, c_begin, c_end, lane, rm.R, hr, scales, SB, recv,
+                         recv_scales, words);
+}
+
+// The first pre-quantised dispatch on a capacity-mode handle prepared with the
+// layout's partials only (or borrowing them), in one launch: workgroup 0
+// finishes the handle and every other wave finds its token's rows from the
+// partials, as in pack_bf16_first_kernel, then moves its part as
+// pack_bytes_kernel.
+template <int CPL, int RB>
+__global__ __launch_bounds__(kRowThreads) void pack_bytes_first_kernel(
+    LayoutArgs la, HandleTokens ht, int ntiles, const u32x4* __restrict__ codes,
+    const uint8_t* __restrict__ scales, int C16, int SB, RowSplit rs, int64_t rows, HandleRows hr,
+    u32x4* __restrict__ recv, uint8_t* __restrict__ recv_scales, bool words) {
+    __shared__ FirstLds s;
+    if (blockIdx.x == 0) {
+        layout_finish_fast<kFirstChunks, kFirstTiles>(la, ntiles, s, (const TileToken*)nullptr);
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((blockIdx.x - 1) * kRowWavesPerBlock +
+                                                 (threadIdx.x >> 6));
+    const int t = (int)rs.div.div((uint32_t)w);
+    const int part = w - t * rs.split;
+    if (t >= la.T) return;
+    const int c_begin = part * rs.per;
+    const int c_end = min(c_begin + rs.per, C16);
+    const GroupCounts<RB> gcnt =
+        load_group_counts<RB>(la.token_mask, la.group_cnt, la.T, la.R, t, lane);
+    u32x4 v[CPL];
+    load_row_part<CPL>(codes + (int64_t)t * C16, c_begin, c_end, lane, v);
+    const TokenRows d = token_rows_from_counts<RB>(gcnt, la.R, rows, t, lane);
+    if (part == 0) write_borrowed_token(ht, d, t, la.R, la.K, lane);
+    pack_bytes_part<CPL>(v, d, t, part, C16, c_begin, c_end, lane, la.R, hr, scales, SB, recv,
+                         recv_scales, words);
 }
 
 int pick_cpl(int chunks) {
@@ -742,6 +786,35 @@ hipError_t launch_pack_fp8_first(const LayoutArgs& la, const HandleTokens& ht, c
     }
 #undef MOEDX_FIRST8_MODE
 #undef MOEDX_FIRST8
+}
+
+hipError_t launch_pack_bytes_first(const LayoutArgs& la, const HandleTokens& ht, const void* codes,
+                                  const void* scales, int H, int scale_bytes, int64_t rows,
+                                  const HandleRows& hr, void* recv_codes, void* recv_scales,
+                                  const Launch& L) {
+    const int T = la.T;
+    const int C16 = H / 16;
+    const int split = pack_split(C16, kWaveChunks);
+    const RowSplit parts = make_row_split(C16, split);
+    const dim3 grid(1 + pack_blocks(T, split)), block(kRowThreads);
+    const u32x4* cs = static_cast<const u32x4*>(codes);
+    u32x4* rc = static_cast<u32x4*>(recv_codes);
+    const uint8_t* ss = static_cast<const uint8_t*>(scales);
+    uint8_t* rs = static_cast<uint8_t*>(recv_scales);
+    const bool words = (scale_bytes & 3) == 0 && (reinterpret_cast<uintptr_t>(ss) & 3u) == 0 &&
+                       (reinterpret_cast<uintptr_t>(rs) & 3u) == 0;
+    const int ntiles = num_tiles(T);
+    const bool two = pick_cpl(parts.per) > 1;
+#define MOEDX_FIRSTB(C, B)                                                                        \
+    return launch_kernel(pack_bytes_first_kernel<C, B>, grid, block, L, la, ht, ntiles, cs, ss, C16, \
+                         scale_bytes, parts, rows, hr, rc, rs, words)
+    if (la.R <= 8) {
+        if (two) MOEDX_FIRSTB(2, 8);
+        MOEDX_FIRSTB(1, 8);
+    }
+    if (two) MOEDX_FIRSTB(2, 16);
+    MOEDX_FIRSTB(1, 16);
+#undef MOEDX_FIRSTB
 }
 
 hipError_t launch_pack_bytes(const void* codes, const void* scales, int T, int H, int scale_bytes,

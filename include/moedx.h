@@ -251,7 +251,7 @@ MOEDX_API int moedx_handle_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  * finishes the handle in its own launch (below), not even the scan runs: the
  * handle borrows the partial counts, token masks and slot buckets that
  * get_dispatch_layout left in the ctx's scratch, and its first moedx_dispatch
- * (bf16 or FP8) or quantising moedx_dispatch_fp8 builds the handle from them.
+ * or moedx_dispatch_fp8 builds the handle from them.
  * Any other first use, a
  * later prepare that borrows the same layout, or the ctx's next
  * moedx_get_dispatch_layout first copies them into the handle (one small
@@ -271,8 +271,8 @@ MOEDX_API int moedx_handle_workspace_bytes(const moedx_ctx *ctx, int T, int K,
  *     counts run here; the prefixes, totals and N (rank and channel prefix
  *     matrices, num_tokens_per_rank/expert, MOEDX_T_NUM_RECV) are written on
  *     the stream of the handle's first moedx_dispatch or moedx_dispatch_fp8
- *     (by its pack kernel, in the same launch; for pre-quantised input, by
- *     one small kernel before it), moedx_combine or moedx_handle_finish:
+ *     (by its pack kernel, in the same launch), moedx_combine (one small
+ *     kernel before it) or moedx_handle_finish:
  *     read them after that call.  In exact mode the call blocks on the host
  *     even when exec->done is given.
  * *out receives a new handle (moedx_handle_destroy frees it). */

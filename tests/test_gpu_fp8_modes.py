@@ -98,6 +98,54 @@ def test_first_fp8_capacity_dispatch_one_launch(oracle, name, borrow):
         _check(oracle, name, inp.x, ref.prefix, codes, scales)
 
 
+@pytest.mark.parametrize("borrow", [False, True], ids=["own_layout", "borrowed_layout"])
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0", "none", "ue8m0_5_blocks"])
+def test_first_prequantized_capacity_dispatch_one_launch(oracle, fmt, borrow):
+    """A first pre-quantised dispatch on a capacity-mode handle of at most
+    4096 tokens copies the code and scale rows and finishes the handle in one
+    launch (scale rows as 4-byte words, or byte by byte for 5 UE8M0 blocks)."""
+    dev = device()
+    T, E, R, C, K = 1000, 64, 8, 6, 6
+    H = 640 if fmt == "ue8m0_5_blocks" else 1024
+    G = H // 128
+    rng = np.random.default_rng(47)
+    idx = wl.random_routing(rng, T, E, K, p_empty=0.05)
+    codes = rng.integers(0, 256, (T, H), dtype=np.uint8)
+    if fmt == "fp32":
+        sc, kw = rng.standard_normal((T, G)).astype(np.float32), {}
+    elif fmt == "none":
+        sc, kw = None, dict(fp8_quant_scale=0.5)
+    else:
+        sc, kw = rng.integers(0, 256, (T, G), dtype=np.uint8), dict(use_ue8m0=True)
+    inp = wl.Inputs(torch.zeros(T, H, dtype=torch.bfloat16), torch.from_numpy(idx),
+                    torch.full((T, K), 1.0 / K))
+    print(f"[prequant first one launch {fmt}] borrow={borrow}", flush=True)
+    ref = oracle_first_dispatch(oracle, inp, E, R, C, with_rows=False)
+    buf = make_buffer(E, R, C, T)
+    ti = inp.topk_idx.to(dev)
+    reuse = {}
+    if borrow:
+        ntr, _, nte, itr, _ = buf.get_dispatch_layout(ti, E)
+        reuse = dict(num_tokens_per_rank=ntr, is_token_in_rank=itr, num_tokens_per_expert=nte)
+    before = buf.stats()
+    pair = (torch.from_numpy(codes).to(dev), torch.from_numpy(sc).to(dev) if sc is not None else None)
+    (rc, rs), _, _, _, h, _ = buf.dispatch(pair, topk_idx=ti, num_worst_tokens=T * min(K, R),
+                                           **kw, **reuse)
+    torch.cuda.synchronize()
+    st = buf.stats()
+    assert st["layout_launches"] - before["layout_launches"] == (0 if borrow else 1), st
+    assert st["scan_launches"] == before["scan_launches"], st
+    assert st["pack_fp8_launches"] - before["pack_fp8_launches"] == 1, st
+    N = ref.prefix.num_recv
+    check_handle(h, ref, N)
+    assert_equal("codes", np_(rc)[:N], oracle.pack_rows_bytes(codes, ref.prefix))
+    if sc is None:
+        assert rs is None
+    else:
+        got = np_(rs)[:N].view(np.uint8).reshape(N, -1)
+        assert_equal("scales", got, oracle.pack_rows_bytes(sc, ref.prefix))
+
+
 def _edge_x(T, H, seed):
     rng = np.random.default_rng(seed)
     x = np.asarray(rng.integers(0, 1 << 16, (T, H)), np.uint16)
