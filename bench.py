@@ -102,6 +102,21 @@ def source_digest(src):
     return h.hexdigest()[:16]
 
 
+def input_digests(inp) -> dict:
+    """First 16 hex digits of the sha256 of each generated input tensor's bytes
+    (x as bf16, topk_idx as int64, topk_weights as fp32), so that a rerun can
+    check it measured the same inputs."""
+    import hashlib
+
+    import torch
+
+    def digest(t):
+        return hashlib.sha256(t.contiguous().view(-1).view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+
+    return {"x": digest(inp.x), "topk_idx": digest(inp.topk_idx),
+            "topk_weights": digest(inp.topk_weights)}
+
+
 def measured_traffic(op):
     """HBM bytes per launch of `op` from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size), or
@@ -1020,6 +1035,7 @@ def main():
     T, H, K, E, R, Ch = w.tokens, w.hidden, w.topk, w.experts, w.ranks, w.channels
     log(f"[bench] generating {w.name}")
     inp = wl.make_inputs(w)
+    inputs_sha256 = input_digests(inp)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cap = T * min(K, R)
@@ -1267,6 +1283,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: seeded x ~ N(0,1) bf16, group-limited top-8 routing, softmax gates",
+        "inputs_sha256": inputs_sha256,
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": E, "topk": K,
                    "ranks": R, "channels": Ch, "routing": w.routing, "recv_rows": N,
                    "mode": "capacity (no host sync)",

@@ -65,3 +65,12 @@ def test_all_cores_oracle_leg_equals_the_single_thread_step():
     assert np.array_equal(rx1, rx4)
     assert np.array_equal(out1, out4)
     assert bench.cpu_threads() >= 1
+
+
+def test_headline_input_digests_are_stable():
+    """The bench line records a digest of each generated input of the prefill
+    workload; the seeded generator gives the same bytes on every run."""
+    from combine_get_dispatch_layout_amd import workloads as wl
+    d = bench.input_digests(wl.make_inputs(wl.PREFILL))
+    assert d == {"x": "dc0bef52dad6fc0f", "topk_idx": "97eb46dbb565f6c3",
+                 "topk_weights": "ee85ac06ed5a21f0"}
