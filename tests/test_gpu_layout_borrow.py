@@ -1,6 +1,6 @@
 """A first dispatch prepared from exactly the outputs of the ctx's last
 get_dispatch_layout borrows the partials that call left in the ctx's scratch
-(no scan kernel), and its first bf16 pack builds the handle.  Every other way
+(no scan kernel), and its first pack builds the handle.  Every other way
 the borrowed data can be needed is checked against the oracle: a new layout on
 the ctx before the first dispatch, an FP8 first dispatch, an explicit finish, a
 second handle borrowing the same layout, a destroyed borrower, a first pack on
@@ -137,9 +137,10 @@ def test_destroyed_borrower_then_new_layout(oracle):
     _check_first_dispatch(buf, h, inp, ref, dev)
 
 
-def test_first_pack_on_another_stream_then_layout(oracle):
-    """The layout after a borrowing first pack on another stream waits for
-    that pack's reads of the scratch."""
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_first_pack_on_another_stream_then_layout(oracle, fp8):
+    """The layout after a borrowing first pack (bf16 or FP8) on another
+    stream waits for that pack's reads of the scratch."""
     dev, inp, ref = _setup(oracle)
     _, inp2, ref2 = _setup(oracle, seed=78)
     buf = make_buffer(W.experts, W.ranks, W.channels, T)
@@ -155,13 +156,18 @@ def test_first_pack_on_another_stream_then_layout(oracle):
             recv, _, _, _, h, _ = buf.dispatch(
                 x, topk_idx=idx, num_tokens_per_rank=ntr, is_token_in_rank=itr,
                 num_tokens_per_expert=nte, num_worst_tokens=T * min(W.topk, W.ranks),
-                previous_event=ev, no_sync=True)
+                previous_event=ev, no_sync=True, fp8=fp8)
         with torch.cuda.stream(s1):
             ntr2, _, nte2, itr2, _ = buf.get_dispatch_layout(idx2, W.experts, async_finish=True)
         torch.cuda.synchronize()
         N = ref.prefix.num_recv
         check_handle(h, ref, N)
-        assert_equal("recv_x", np_(recv)[:N], ref.recv_x)
+        if fp8:
+            cref, sref = oracle.pack_fp8(np_(inp.x), ref.prefix)
+            assert_equal("codes", np_(recv[0])[:N], cref)
+            assert_equal("scales", np_(recv[1])[:N].view(np.uint32), sref.view(np.uint32))
+        else:
+            assert_equal("recv_x", np_(recv)[:N], ref.recv_x)
         assert_equal("second layout", np_(itr2), ref2.layout.is_token_in_rank)
         assert_equal("second experts", np_(nte2), ref2.layout.num_tokens_per_expert)
 
